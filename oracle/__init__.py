@@ -1,0 +1,230 @@
+"""CPU oracle of the fused Mixture-of-Experts layer (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The GPU library never imports it, and
+the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, OpenMP over tokens, fp32, no
+BLAS, no fast-math, no FMA contraction). This module only builds it with gcc,
+loads it with ctypes and marshals numpy arrays. Each function states the
+passage it follows:
+
+* :func:`route` -- top-k gating, the first stage of the fused MoE pipeline
+  (AITER article, itsolotime.com/th/archives/32381, section 3).
+* :func:`sort` -- token sort into expert-contiguous, block-padded groups
+  (same article, section 3.1, ``_moe_sorting_impl`` and its sizing formulas).
+* :func:`moe` -- per-token loop over the selected experts in fp32, SwiGLU
+  expert FFN, weighted combine (same article, section 3; rocketrecap.com
+  entries/19116, 5:58 and glossary "SwiGLU").
+* :func:`e4m3_encode` / :func:`e4m3_decode` / :func:`quant_rows` -- OCP FP8
+  E4M3FN and the amax/448 scale rule used by the fp8 layers (quant types
+  per_Token and per_1x128 named in the AITER article, sections 1.1 and 3.2).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+             "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it and return its path."""
+    global _lib
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+        _lib = None
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        lib.oracle_f32_to_bf16.argtypes = [f32]
+        lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = f32
+        lib.oracle_e4m3_encode.argtypes = [f32]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_quant_group.argtypes = [P, i32, P, P]
+        lib.oracle_quant_group.restype = f32
+        lib.oracle_route.argtypes = [P, i32, i32, i32, i32, i32, P, P]
+        lib.oracle_route.restype = i32
+        lib.oracle_max_padded.argtypes = [i32, i32, i32, i32]
+        lib.oracle_max_padded.restype = i64
+        lib.oracle_max_blocks.argtypes = [i32, i32, i32, i32]
+        lib.oracle_max_blocks.restype = i64
+        lib.oracle_sort.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, P]
+        lib.oracle_sort.restype = i32
+        lib.oracle_moe.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P,
+                                   P, P, P, P, P, i32, P, P, i32]
+        lib.oracle_moe.restype = i32
+        lib.oracle_quant_rows.argtypes = [P, i32, i32, i32, P, P]
+        lib.oracle_quant_rows.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    lib = _load()
+    v = np.asarray(v, dtype=np.float32).ravel()
+    return np.array([lib.oracle_f32_to_bf16(float(x)) for x in v], dtype=np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([lib.oracle_e4m3_decode(int(c)) for c in codes], dtype=np.float32)
+
+
+def e4m3_encode(values) -> np.ndarray:
+    lib = _load()
+    values = np.asarray(values, dtype=np.float32).ravel()
+    return np.array([lib.oracle_e4m3_encode(float(v)) for v in values], dtype=np.uint8)
+
+
+def quant_group(values):
+    """One shared scale: returns (codes, scale, dequantised values)."""
+    lib = _load()
+    v = _c(values, np.float32).ravel()
+    q = np.empty(v.size, np.uint8)
+    deq = np.empty(v.size, np.float32)
+    s = lib.oracle_quant_group(_ptr(v), v.size, _ptr(q), _ptr(deq))
+    return q, np.float32(s), deq
+
+
+def quant_rows(x_bf16: np.ndarray, group: int):
+    """Dynamic e4m3 quantisation of a bf16 matrix, one scale per `group` columns.
+
+    Returns (codes uint8 [rows, cols], scales fp32 [rows, cols // group])."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols), np.uint8)
+    scales = np.empty((rows, cols // group), np.float32)
+    rc = lib.oracle_quant_rows(_ptr(x), rows, cols, group, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_quant_rows failed ({rc})")
+    return codes, scales
+
+
+def route(logits: np.ndarray, k: int, score: str = "softmax", renorm: bool = True):
+    """Top-k routing. Returns (topk_ids int32 [T,k], topk_w fp32 [T,k])."""
+    lib = _load()
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    rc = lib.oracle_route(_ptr(lg), T, E, k, {"softmax": 0, "sigmoid": 1}[score], int(renorm),
+                          _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError(f"oracle_route failed ({rc})")
+    return ids, w
+
+
+def max_padded(T, k, E, B) -> int:
+    return int(_load().oracle_max_padded(T, k, E, B))
+
+
+def max_blocks(T, k, E, B) -> int:
+    return int(_load().oracle_max_blocks(T, k, E, B))
+
+
+def sort(topk_ids: np.ndarray, topk_w: np.ndarray, E: int, B: int) -> dict:
+    """Token sort. Returns a dict of numpy arrays with the buffer names used by
+    the GPU library: sorted_ids, sorted_w, sorted_expert_ids, expert_counts,
+    expert_offsets, num_valid."""
+    lib = _load()
+    ids = _c(topk_ids, np.int32)
+    w = _c(topk_w, np.float32)
+    T, k = ids.shape
+    P, NB = max_padded(T, k, E, B), max_blocks(T, k, E, B)
+    out = dict(sorted_ids=np.empty(P, np.int32), sorted_w=np.empty(P, np.float32),
+               sorted_expert_ids=np.empty(NB, np.int32), expert_counts=np.empty(E, np.int32),
+               expert_offsets=np.empty(E + 1, np.int32), num_valid=np.empty(1, np.int32))
+    rc = lib.oracle_sort(_ptr(ids), _ptr(w), T, k, E, B, _ptr(out["sorted_ids"]),
+                         _ptr(out["sorted_w"]), _ptr(out["sorted_expert_ids"]),
+                         _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+                         _ptr(out["num_valid"]))
+    if rc != 0:
+        raise ValueError(f"oracle_sort failed ({rc})")
+    return out
+
+
+QUANT = {"bf16": 0, "fp8_token": 1, "fp8_block": 2}
+
+
+def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
+        w13_scale=None, w2_scale=None, quant: str = "bf16", tokens=None,
+        h_exact: bool = False, threads: int = 0):
+    """The MoE layer output for the rows listed in `tokens` (default: all).
+
+    w13 / w2 (and the scales) are sequences indexed by expert holding numpy
+    arrays (or None for experts no listed token selects): w13[e] [2f, d],
+    w2[e] [d, f]; bf16 as uint16 bits, or e4m3 codes as uint8.
+    Returns (y fp32 [n, d], out bf16 bits uint16 [n, d])."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    w = _c(topk_w, np.float32)
+    T, d = x.shape
+    k = ids.shape[1]
+    E = len(w13)
+    q = QUANT[quant]
+    f = next(a for a in w13 if a is not None).shape[0] // 2
+    tok = np.arange(T, dtype=np.int32) if tokens is None else _c(tokens, np.int32)
+    keep = []
+
+    def table(arrs, dtype):
+        t = (ctypes.c_void_p * E)()
+        for e, a in enumerate(arrs):
+            if a is None:
+                t[e] = None
+            else:
+                a = _c(a, dtype)
+                keep.append(a)
+                t[e] = a.ctypes.data
+        return t
+
+    wdt = np.uint16 if q == 0 else np.uint8
+    t13, t2 = table(w13, wdt), table(w2, wdt)
+    if q:
+        s13, s2 = table(w13_scale, np.float32), table(w2_scale, np.float32)
+    else:
+        s13 = s2 = None
+    y = np.empty((tok.size, d), np.float32)
+    out = np.empty((tok.size, d), np.uint16)
+    rc = lib.oracle_moe(T, d, f, E, k, q, int(h_exact), _ptr(x), _ptr(ids), _ptr(w), t13, s13,
+                        t2, s2, _ptr(tok), tok.size, _ptr(y), _ptr(out), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_moe failed ({rc})")
+    return y, out

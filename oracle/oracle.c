@@ -1,0 +1,418 @@
+/*
+ * oracle.c — plain CPU oracle of the fused Mixture-of-Experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this library. The GPU library never
+ * links, includes or calls it, and this file shares no code, header, table or
+ * helper with it.
+ *
+ * What it computes, and where the pages define it:
+ *  - oracle_route: top-k gating, the first stage of the fused MoE pipeline
+ *    (AITER article, itsolotime.com/th/archives/32381, section 3 "Fused MoE",
+ *    pipeline gating -> token re-sort -> expert GEMMs -> weighted combine).
+ *    The scoring (softmax or sigmoid, renormalised over the selected k) is the
+ *    plain reading of "top-k of softmax(router logits) renormalised".
+ *  - oracle_sort: the token sort of section 3.1 of the same article. Buffer
+ *    sizes follow its max_num_tokens_padded / max_num_m_blocks formulas.
+ *    Inside an expert, assignments keep ascending flat order (stable sort);
+ *    padding and tail slots hold the sentinel T*k with weight 0; blocks past
+ *    the last used one get expert id -1.
+ *  - oracle_moe: the MoE FFN written as a per-token loop over the selected
+ *    experts in fp32 (one accumulator per dot product, ascending index, no
+ *    contraction into FMA). SwiGLU is silu(x Wg) * (x Wu) followed by Wd
+ *    (rocketrecap.com/entries/19116 talk summary, glossary "SwiGLU"; MoE GEMMs
+ *    at 5:58). The intermediate h is rounded to bf16; fp8 layers then
+ *    re-quantise that bf16 h (per row, or per 1x128 block) before the down
+ *    projection, and quantise the input row the same way.
+ *  - oracle_e4m3_encode / _decode / oracle_quant_group: the OCP FP8 E4M3FN
+ *    format (bias 7, 3 mantissa bits, max 448, no infinities, S.1111.111 is
+ *    NaN) and the scale rule s = amax / 448 (s = 1 when amax = 0),
+ *    q = round-to-nearest-even, saturating encode of v / s.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no BLAS, no
+ * fast-math). Every exported function returns 0 on success and a negative
+ * value on a bad argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ */
+/* scalar formats                                                      */
+/* ------------------------------------------------------------------ */
+
+static float bf16_bits_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* IEEE round-to-nearest-even of an fp32 value to bfloat16 (1-8-7). */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) /* NaN stays a quiet NaN */
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+static float round_to_bf16(float f) { return bf16_bits_to_f32(oracle_f32_to_bf16(f)); }
+
+/* OCP E4M3FN decode: value = (-1)^s * 2^(e-7) * (1 + m/8) for e > 0,
+ * (-1)^s * 2^-6 * (m/8) for e = 0, NaN for e = 15, m = 7. */
+float oracle_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (float)(s ? -v : v);
+}
+
+/* OCP E4M3FN encode, round to nearest, ties to even, saturating at +-448. */
+uint8_t oracle_e4m3_encode(float v)
+{
+    if (isnan(v))
+        return 0x7f;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7e);
+    if (a == 0.0)
+        return sign;
+    /* spacing of representable values around a: 2^(binade-3), with the
+     * binade clamped at -6 (subnormals are spaced 2^-9). */
+    int ex;
+    frexp(a, &ex);
+    int binade = ex - 1;
+    if (binade < -6)
+        binade = -6;
+    double quantum = ldexp(1.0, binade - 3);
+    double r = nearbyint(a / quantum) * quantum; /* default mode: ties to even */
+    if (r == 0.0)
+        return sign;
+    frexp(r, &ex);
+    binade = ex - 1;
+    if (binade < -6) /* subnormal: r = m * 2^-9 */
+        return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9)));
+    int mant = (int)(r / ldexp(1.0, binade) * 8.0) - 8;
+    return (uint8_t)(sign | ((binade + 7) << 3) | mant);
+}
+
+/* Quantise n values that share one scale. s = amax / 448 in fp32 (s = 1 if
+ * amax is 0), q_i = encode(v_i / s). Writes the codes to q (if not NULL),
+ * the dequantised values fp32(decode(q_i)) * s to deq (if not NULL) and
+ * returns s. */
+float oracle_quant_group(const float *v, int n, uint8_t *q, float *deq)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax)
+            amax = a;
+    }
+    float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    for (int i = 0; i < n; ++i) {
+        uint8_t c = oracle_e4m3_encode(v[i] / s);
+        if (q)
+            q[i] = c;
+        if (deq)
+            deq[i] = oracle_e4m3_decode(c) * s;
+    }
+    return s;
+}
+
+/* ------------------------------------------------------------------ */
+/* routing                                                             */
+/* ------------------------------------------------------------------ */
+
+/* score: 0 = softmax over all E logits, 1 = sigmoid of each logit.
+ * renorm: 1 = divide the k selected scores by their sum.
+ * Selection is on the raw logit, ordered by (logit descending, expert
+ * ascending); topk_ids[t, j] lists the selected experts in that order. */
+int oracle_route(const float *logits, int T, int E, int k, int score, int renorm,
+                 int32_t *topk_ids, float *topk_w)
+{
+    if (!logits || !topk_ids || !topk_w || T < 0 || E < 1 || k < 1 || k > E)
+        return -1;
+    if (score != 0 && score != 1)
+        return -1;
+    char *taken = (char *)malloc((size_t)E);
+    float *p = (float *)malloc(sizeof(float) * (size_t)E);
+    if (!taken || !p) {
+        free(taken);
+        free(p);
+        return -2;
+    }
+    for (int t = 0; t < T; ++t) {
+        const float *l = logits + (size_t)t * E;
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || l[e] > l[best]))
+                    best = e;
+            taken[best] = 1;
+            topk_ids[(size_t)t * k + j] = best;
+        }
+        if (score == 0) {
+            float m = l[0];
+            for (int e = 1; e < E; ++e)
+                if (l[e] > m)
+                    m = l[e];
+            float den = 0.0f;
+            for (int e = 0; e < E; ++e)
+                den += expf(l[e] - m);
+            for (int e = 0; e < E; ++e)
+                p[e] = expf(l[e] - m) / den;
+        } else {
+            for (int e = 0; e < E; ++e)
+                p[e] = 1.0f / (1.0f + expf(-l[e]));
+        }
+        float sum = 0.0f;
+        for (int j = 0; j < k; ++j)
+            sum += p[topk_ids[(size_t)t * k + j]];
+        for (int j = 0; j < k; ++j) {
+            float pj = p[topk_ids[(size_t)t * k + j]];
+            topk_w[(size_t)t * k + j] = renorm ? pj / sum : pj;
+        }
+    }
+    free(taken);
+    free(p);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* token sort                                                          */
+/* ------------------------------------------------------------------ */
+
+int64_t oracle_max_padded(int T, int k, int E, int B)
+{
+    return (int64_t)T * k + (int64_t)E * B - k;
+}
+
+int64_t oracle_max_blocks(int T, int k, int E, int B)
+{
+    int64_t P = oracle_max_padded(T, k, E, B);
+    return (P + B - 1) / B;
+}
+
+/* Stable counting sort of the T*k assignments a = t*k + j by expert, each
+ * expert's segment padded up to a multiple of B. Outputs:
+ *   sorted_ids [P], sorted_w [P], sorted_expert_ids [NB],
+ *   expert_counts [E], expert_offsets [E+1] (padded), num_valid [1]. */
+int oracle_sort(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, int B,
+                int32_t *sorted_ids, float *sorted_w, int32_t *sorted_expert_ids,
+                int32_t *expert_counts, int32_t *expert_offsets, int32_t *num_valid)
+{
+    if (!topk_ids || !topk_w || !sorted_ids || !sorted_w || !sorted_expert_ids ||
+        !expert_counts || !expert_offsets || !num_valid)
+        return -1;
+    if (T < 0 || k < 1 || E < k || B < 1)
+        return -1;
+    const int64_t N = (int64_t)T * k;
+    const int64_t P = oracle_max_padded(T, k, E, B);
+    const int64_t NB = oracle_max_blocks(T, k, E, B);
+    for (int64_t a = 0; a < N; ++a)
+        if (topk_ids[a] < 0 || topk_ids[a] >= E)
+            return -1;
+
+    for (int e = 0; e < E; ++e)
+        expert_counts[e] = 0;
+    for (int64_t a = 0; a < N; ++a)
+        expert_counts[topk_ids[a]] += 1;
+
+    expert_offsets[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int32_t padded = (expert_counts[e] + B - 1) / B * B;
+        expert_offsets[e + 1] = expert_offsets[e] + padded;
+    }
+    *num_valid = expert_offsets[E];
+    if (*num_valid > P)
+        return -3; /* cannot happen when k <= E */
+
+    for (int64_t i = 0; i < P; ++i) {
+        sorted_ids[i] = (int32_t)N;
+        sorted_w[i] = 0.0f;
+    }
+    for (int64_t b = 0; b < NB; ++b)
+        sorted_expert_ids[b] = -1;
+
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    if (!cursor)
+        return -2;
+    for (int e = 0; e < E; ++e)
+        cursor[e] = expert_offsets[e];
+    for (int64_t a = 0; a < N; ++a) {
+        int e = topk_ids[a];
+        sorted_ids[cursor[e]] = (int32_t)a;
+        sorted_w[cursor[e]] = topk_w[a];
+        cursor[e] += 1;
+    }
+    free(cursor);
+
+    for (int e = 0; e < E; ++e)
+        for (int32_t b = expert_offsets[e] / B; b < expert_offsets[e + 1] / B; ++b)
+            sorted_expert_ids[b] = e;
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* the MoE FFN, one token at a time                                     */
+/* ------------------------------------------------------------------ */
+
+/* quant: 0 = bf16 operands; 1 = e4m3 weights with one fp32 scale per output
+ * channel and e4m3 activations with one scale per row; 2 = e4m3 weights with
+ * one scale per 128x128 block and activations with one scale per 1x128 block.
+ * Weights are given per expert (entries of unused experts may be NULL):
+ *   w13[e]: [2f, d] (rows 0..f-1 gate, f..2f-1 up), d contiguous,
+ *           scales [2f] (quant 1) or [2f/128, d/128] (quant 2);
+ *   w2[e]:  [d, f], f contiguous, scales [d] or [d/128, f/128].
+ * h_exact = 1 skips the rounding of h (pinning use only). */
+typedef struct {
+    int d, f, quant;
+    const void *w13, *w2;
+    const float *s13, *s2;
+} expert_view;
+
+static float weight13(const expert_view *v, int row, int col)
+{
+    size_t idx = (size_t)row * v->d + col;
+    if (v->quant == 0)
+        return bf16_bits_to_f32(((const uint16_t *)v->w13)[idx]);
+    float code = oracle_e4m3_decode(((const uint8_t *)v->w13)[idx]);
+    float s = (v->quant == 1) ? v->s13[row] : v->s13[(size_t)(row / 128) * (v->d / 128) + col / 128];
+    return code * s;
+}
+
+static float weight2(const expert_view *v, int row, int col)
+{
+    size_t idx = (size_t)row * v->f + col;
+    if (v->quant == 0)
+        return bf16_bits_to_f32(((const uint16_t *)v->w2)[idx]);
+    float code = oracle_e4m3_decode(((const uint8_t *)v->w2)[idx]);
+    float s = (v->quant == 1) ? v->s2[row] : v->s2[(size_t)(row / 128) * (v->f / 128) + col / 128];
+    return code * s;
+}
+
+/* Replace v[0..n) by its quantise-dequantise image: one group (quant 1) or
+ * groups of 128 (quant 2). */
+static void fake_quant(float *v, int n, int quant)
+{
+    int g = (quant == 1) ? n : 128;
+    for (int i = 0; i < n; i += g)
+        oracle_quant_group(v + i, g, NULL, v + i);
+}
+
+static float silu(float z) { return z / (1.0f + expf(-z)); }
+
+int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
+               const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+               const void *const *w13, const float *const *w13_scale,
+               const void *const *w2, const float *const *w2_scale,
+               const int32_t *tokens, int n_tokens, float *y, uint16_t *out, int nthreads)
+{
+    if (!x || !topk_ids || !topk_w || !w13 || !w2 || !tokens || !y || !out)
+        return -1;
+    if (T < 0 || d < 1 || f < 1 || E < 1 || k < 1 || k > E || n_tokens < 0)
+        return -1;
+    if (quant < 0 || quant > 2)
+        return -1;
+    if (quant != 0 && (!w13_scale || !w2_scale))
+        return -1;
+    if (quant == 2 && (d % 128 || f % 128))
+        return -1;
+    for (int i = 0; i < n_tokens; ++i) {
+        int t = tokens[i];
+        if (t < 0 || t >= T)
+            return -1;
+        for (int j = 0; j < k; ++j) {
+            int e = topk_ids[(size_t)t * k + j];
+            if (e < 0 || e >= E || !w13[e] || !w2[e] || (quant && (!w13_scale[e] || !w2_scale[e])))
+                return -1;
+        }
+    }
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#endif
+    for (int i = 0; i < n_tokens; ++i) {
+        const int t = tokens[i];
+        float *xt = (float *)malloc(sizeof(float) * (size_t)d);
+        float *h = (float *)malloc(sizeof(float) * (size_t)f);
+        float *yt = y + (size_t)i * d;
+        if (!xt || !h) {
+            free(xt);
+            free(h);
+            bad |= 1;
+            continue;
+        }
+        for (int c = 0; c < d; ++c)
+            xt[c] = bf16_bits_to_f32(x[(size_t)t * d + c]);
+        if (quant)
+            fake_quant(xt, d, quant);
+        for (int m = 0; m < d; ++m)
+            yt[m] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int e = topk_ids[(size_t)t * k + j];
+            const float w = topk_w[(size_t)t * k + j];
+            expert_view v = {d, f, quant, w13[e], w2[e],
+                             quant ? w13_scale[e] : NULL, quant ? w2_scale[e] : NULL};
+            for (int n = 0; n < f; ++n) {
+                float g = 0.0f, u = 0.0f;
+                for (int c = 0; c < d; ++c) {
+                    g += xt[c] * weight13(&v, n, c);
+                    u += xt[c] * weight13(&v, f + n, c);
+                }
+                float hn = silu(g) * u;
+                h[n] = h_exact ? hn : round_to_bf16(hn);
+            }
+            if (quant && !h_exact)
+                fake_quant(h, f, quant);
+            for (int m = 0; m < d; ++m) {
+                float z = 0.0f;
+                for (int n = 0; n < f; ++n)
+                    z += h[n] * weight2(&v, m, n);
+                yt[m] += w * z;
+            }
+        }
+        for (int m = 0; m < d; ++m)
+            out[(size_t)i * d + m] = oracle_f32_to_bf16(yt[m]);
+        free(xt);
+        free(h);
+    }
+    return bad ? -2 : 0;
+}
+
+/* Dynamic activation quantisation of a bf16 matrix [rows, cols]: one scale
+ * per row (group = cols) or per 1x128 block (group = 128). codes [rows, cols],
+ * scales [rows, cols / group]. */
+int oracle_quant_rows(const uint16_t *x, int rows, int cols, int group, uint8_t *codes, float *scales)
+{
+    if (!x || !codes || !scales || rows < 0 || cols < 1 || group < 1 || cols % group)
+        return -1;
+    float *buf = (float *)malloc(sizeof(float) * (size_t)cols);
+    if (!buf)
+        return -2;
+    for (int r = 0; r < rows; ++r) {
+        for (int c = 0; c < cols; ++c)
+            buf[c] = bf16_bits_to_f32(x[(size_t)r * cols + c]);
+        for (int c = 0; c < cols; c += group)
+            scales[(size_t)r * (cols / group) + c / group] =
+                oracle_quant_group(buf + c, group, codes + (size_t)r * cols + c, NULL);
+    }
+    free(buf);
+    return 0;
+}
