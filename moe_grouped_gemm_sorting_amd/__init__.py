@@ -1,0 +1,284 @@
+"""Python binding of libmoe, the gfx950 fused Mixture-of-Experts library.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/moe.h``. PyTorch supplies device
+memory (``torch.empty`` on the GPU) and the current stream. The functions
+carry the ABI's names; importing works without a GPU, and any call fails
+loudly if ``libmoe.so`` has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MoeError", "QUANT", "SCORE", "load_library", "library_path",
+    "moe_sort_max_padded", "moe_sort_max_blocks", "moe_topk", "moe_sort", "moe_quant_act",
+    "moe_gemm1_workspace_bytes", "moe_gemm1_swiglu", "moe_gemm2_workspace_bytes",
+    "moe_gemm2_combine", "fused_moe_workspace_bytes", "fused_moe", "moe_select_config",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmoe.so")
+_lib = None
+
+QUANT = {"bf16": 0, "fp8_token": 1, "fp8_block": 2}
+SCORE = {"softmax": 0, "sigmoid": 1}
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
+          4: "MOE_ERR_HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmoe.so (built by ``moe_grouped_gemm_sorting_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m moe_grouped_gemm_sorting_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "moe_sort_max_padded": (i64, [i32, i32, i32, i32]),
+        "moe_sort_max_blocks": (i64, [i32, i32, i32, i32]),
+        "moe_topk": (i32, [P, i32, i32, i32, i32, i32, P, P, P]),
+        "moe_sort": (i32, [P, P, i32, i32, i32, i32, P, P, P, P, P, P, P]),
+        "moe_quant_act": (i32, [P, i32, i32, i32, P, P, P]),
+        "moe_gemm1_workspace_bytes": (sz, [i32] * 7),
+        "moe_gemm1_swiglu": (i32, [i32] * 7 + [P] * 8 + [P, sz, P]),
+        "moe_gemm2_workspace_bytes": (sz, [i32] * 7),
+        "moe_gemm2_combine": (i32, [i32] * 8 + [P] * 9 + [P, sz, P]),
+        "fused_moe_workspace_bytes": (sz, [i32] * 8),
+        "fused_moe": (i32, [i32] * 8 + [P] * 8 + [i32, i32, i32, P, P, sz, P]),
+        "moe_select_config": (i32, [i32] * 7 + [P, P, P]),
+        "moe_status_string": (ctypes.c_char_p, [i32]),
+        "moe_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = load_library().moe_last_error().decode(errors="replace")
+        raise MoeError(rc, msg)
+
+
+def _need(t, name, dtypes, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+_W8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _wdtypes(quant):
+    return (torch.bfloat16,) if quant == "bf16" else _W8
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, need {nbytes}")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------- ABI
+def moe_sort_max_padded(T: int, k: int, E: int, B: int) -> int:
+    return int(load_library().moe_sort_max_padded(T, k, E, B))
+
+
+def moe_sort_max_blocks(T: int, k: int, E: int, B: int) -> int:
+    return int(load_library().moe_sort_max_blocks(T, k, E, B))
+
+
+def moe_topk(logits: torch.Tensor, k: int, score: str = "softmax", renorm: bool = True):
+    """Top-k routing of fp32 logits [T, E]; returns (topk_ids int32, topk_w fp32), [T, k]."""
+    lib = load_library()
+    _need(logits, "logits", (torch.float32,))
+    T, E = logits.shape
+    ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _check(lib.moe_topk(_ptr(logits), T, E, k, SCORE[score], int(renorm), _ptr(ids), _ptr(w),
+                        _stream(logits)))
+    return ids, w
+
+
+def moe_sort(topk_ids: torch.Tensor, topk_w: torch.Tensor, E: int, B: int) -> dict:
+    """Stable block-padded sort; returns sorted_ids, sorted_w, sorted_expert_ids,
+    expert_counts, expert_offsets, num_valid (GPU tensors)."""
+    lib = load_library()
+    _need(topk_ids, "topk_ids", (torch.int32,))
+    _need(topk_w, "topk_w", (torch.float32,), topk_ids.device)
+    T, k = topk_ids.shape
+    P, NB = moe_sort_max_padded(T, k, E, B), moe_sort_max_blocks(T, k, E, B)
+    if P < 0:
+        raise ValueError(f"bad sort shape T={T} k={k} E={E} B={B}")
+    dev = topk_ids.device
+    out = dict(sorted_ids=torch.empty(P, dtype=torch.int32, device=dev),
+               sorted_w=torch.empty(P, dtype=torch.float32, device=dev),
+               sorted_expert_ids=torch.empty(NB, dtype=torch.int32, device=dev),
+               expert_counts=torch.empty(E, dtype=torch.int32, device=dev),
+               expert_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               num_valid=torch.empty(1, dtype=torch.int32, device=dev))
+    _check(lib.moe_sort(_ptr(topk_ids), _ptr(topk_w), T, k, E, B, _ptr(out["sorted_ids"]),
+                        _ptr(out["sorted_w"]), _ptr(out["sorted_expert_ids"]),
+                        _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+                        _ptr(out["num_valid"]), _stream(topk_ids)))
+    return out
+
+
+def moe_quant_act(x: torch.Tensor, group: int):
+    """Dynamic e4m3 quantisation of bf16 x [rows, cols]; returns (codes uint8, scales fp32)."""
+    lib = load_library()
+    _need(x, "x", (torch.bfloat16,))
+    rows, cols = x.shape
+    codes = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, cols // group, dtype=torch.float32, device=x.device)
+    _check(lib.moe_quant_act(_ptr(x), rows, cols, group, _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def moe_gemm1_workspace_bytes(T, d, f, E, k, B, quant="bf16") -> int:
+    return int(load_library().moe_gemm1_workspace_bytes(T, d, f, E, k, B, QUANT[quant]))
+
+
+def moe_gemm1_swiglu(x, w13, sort: dict, k: int, B: int, quant: str = "bf16", w13_scale=None,
+                     workspace=None):
+    """Stage 1: grouped gate/up GEMM + SwiGLU. Returns (h, h_scale) in the
+    format of `quant` (bf16 [P, f]; or e4m3 codes [P, f] + scales)."""
+    lib = load_library()
+    _need(x, "x", (torch.bfloat16,))
+    E, f2, d = w13.shape
+    f = f2 // 2
+    _need(w13, "w13", _wdtypes(quant), x.device)
+    T = x.shape[0]
+    P = sort["sorted_ids"].numel()
+    dev = x.device
+    q = QUANT[quant]
+    if q == 0:
+        h = torch.empty(P, f, dtype=torch.bfloat16, device=dev)
+        h_scale = None
+    else:
+        _need(w13_scale, "w13_scale", (torch.float32,), dev)
+        h = torch.empty(P, f, dtype=torch.uint8, device=dev)
+        h_scale = torch.empty(P if q == 1 else P * (f // 128), dtype=torch.float32, device=dev)
+    nbytes = moe_gemm1_workspace_bytes(T, d, f, E, k, B, quant)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.moe_gemm1_swiglu(T, d, f, E, k, B, q, _ptr(x), _ptr(w13), _ptr(w13_scale),
+                                _ptr(sort["sorted_ids"]), _ptr(sort["sorted_expert_ids"]),
+                                _ptr(sort["num_valid"]), _ptr(h), _ptr(h_scale), _ptr(ws), nbytes,
+                                _stream(x)))
+    if h_scale is not None and q == 2:
+        h_scale = h_scale.view(P, f // 128)
+    return h, h_scale
+
+
+def moe_gemm2_workspace_bytes(T, d, f, E, k, B, quant="bf16") -> int:
+    return int(load_library().moe_gemm2_workspace_bytes(T, d, f, E, k, B, QUANT[quant]))
+
+
+def moe_gemm2_combine(h, h_scale, w2, sort: dict, T: int, k: int, B: int, quant: str = "bf16",
+                      w2_scale=None, ksplit: int = 0, out=None, workspace=None):
+    """Stage 2: grouped down GEMM + routing-weighted combine; returns out bf16 [T, d]."""
+    lib = load_library()
+    E, d, f = w2.shape
+    dev = w2.device
+    _need(w2, "w2", _wdtypes(quant))
+    q = QUANT[quant]
+    _need(h, "h", (torch.bfloat16,) if q == 0 else _W8, dev)
+    if q:
+        _need(w2_scale, "w2_scale", (torch.float32,), dev)
+        _need(h_scale, "h_scale", (torch.float32,), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    nbytes = moe_gemm2_workspace_bytes(T, d, f, E, k, B, quant)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.moe_gemm2_combine(T, d, f, E, k, B, q, ksplit, _ptr(h), _ptr(h_scale), _ptr(w2),
+                                 _ptr(w2_scale), _ptr(sort["sorted_ids"]), _ptr(sort["sorted_w"]),
+                                 _ptr(sort["sorted_expert_ids"]), _ptr(sort["num_valid"]),
+                                 _ptr(out), _ptr(ws), nbytes, _stream(w2)))
+    return out
+
+
+def fused_moe_workspace_bytes(T, d, f, E, k, quant="bf16", B=0, stage=0) -> int:
+    return int(load_library().fused_moe_workspace_bytes(T, d, f, E, k, QUANT[quant], B, stage))
+
+
+def fused_moe(x, w13, w2, k: int, logits=None, topk_ids=None, topk_w=None, quant: str = "bf16",
+              w13_scale=None, w2_scale=None, score: str = "softmax", renorm: bool = True,
+              B: int = 0, stage: int = 0, ksplit: int = 0, out=None, workspace=None):
+    """The whole layer; returns out bf16 [T, d]. Pass `logits` [T, E] fp32, or
+    precomputed `topk_ids` / `topk_w`."""
+    lib = load_library()
+    _need(x, "x", (torch.bfloat16,))
+    dev = x.device
+    T, d = x.shape
+    E, f2, _ = w13.shape
+    f = f2 // 2
+    q = QUANT[quant]
+    _need(w13, "w13", _wdtypes(quant), dev)
+    _need(w2, "w2", _wdtypes(quant), dev)
+    if logits is not None:
+        _need(logits, "logits", (torch.float32,), dev)
+    else:
+        _need(topk_ids, "topk_ids", (torch.int32,), dev)
+        _need(topk_w, "topk_w", (torch.float32,), dev)
+    if q:
+        _need(w13_scale, "w13_scale", (torch.float32,), dev)
+        _need(w2_scale, "w2_scale", (torch.float32,), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    nbytes = fused_moe_workspace_bytes(T, d, f, E, k, quant, B, stage)
+    if nbytes == 0:
+        _check(lib.fused_moe(T, d, f, E, k, q, SCORE[score], int(renorm), *([None] * 8), B, stage,
+                             ksplit, None, None, 0, None))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.fused_moe(T, d, f, E, k, q, SCORE[score], int(renorm), _ptr(logits), _ptr(topk_ids),
+                         _ptr(topk_w), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                         _ptr(w2_scale), B, stage, ksplit, _ptr(out), _ptr(ws), nbytes, _stream(x)))
+    return out
+
+
+def moe_select_config(T, d, f, E, k, quant="bf16", cu_count: int = 0):
+    """The library's (B, stage, ksplit) choice for a shape."""
+    lib = load_library()
+    B, stage, ks = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib.moe_select_config(T, d, f, E, k, QUANT[quant], cu_count, ctypes.byref(B),
+                                 ctypes.byref(stage), ctypes.byref(ks)))
+    return B.value, stage.value, ks.value

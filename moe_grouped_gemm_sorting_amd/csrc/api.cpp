@@ -1,0 +1,444 @@
+// api.cpp -- the C ABI of libmoe (declared in include/moe.h): argument
+// validation, workspace carving, the block-size / stage / K-split choice and
+// launch sequencing. No allocation, no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "moe.h"
+#include "launch.h"
+
+namespace moe {
+// implemented in gemm_stream.hip / gemm_tiled.hip / moe_1stage.hip
+bool stream_gemm1_supported(const GemmShape &sh);
+bool stream_gemm2_supported(const GemmShape &sh);
+hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s);
+hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream_t s);
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                          \
+    do {                                             \
+        hipError_t _e = (expr);                      \
+        if (_e != hipSuccess) return hip_fail(_e, what); \
+    } while (0)
+
+// Carves 256-byte aligned sub-buffers out of a workspace. With base == NULL
+// it only measures, so size queries and launches share one layout.
+struct Carver {
+    char *base;
+    size_t off = 0;
+    explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+    template <class T>
+    T *take(size_t count) {
+        size_t start = (off + 255) & ~size_t(255);
+        off = start + count * sizeof(T);
+        return base ? reinterpret_cast<T *>(base + start) : nullptr;
+    }
+    size_t bytes() const { return (off + 255) & ~size_t(255); }
+};
+
+int cu_count_cached() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cu <= 0)
+            cu = 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
+}
+
+bool valid_B(int B) { return B == 16 || B == 32 || B == 64 || B == 128; }
+
+int check_shape(int T, int d, int f, int E, int k, int B, int quant) {
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
+        return fail(MOE_ERR_INVALID_ARG, "bad shape T=%d E=%d k=%d (need T>=0, 1<=k<=E<=%d, k<=%d)",
+                    T, E, k, MOE_MAX_EXPERTS, MOE_MAX_TOPK);
+    if (d < 1 || f < 1) return fail(MOE_ERR_INVALID_ARG, "bad sizes d=%d f=%d", d, f);
+    if (d % 128 || f % 128)
+        return fail(MOE_ERR_UNSUPPORTED, "d=%d and f=%d must be multiples of 128", d, f);
+    if (quant < 0 || quant > 2) return fail(MOE_ERR_INVALID_ARG, "bad quant %d", quant);
+    if (!valid_B(B)) return fail(MOE_ERR_INVALID_ARG, "B=%d must be 16, 32, 64 or 128", B);
+    if ((int64_t)T * k > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "T*k=%lld above 2^24", (long long)T * k);
+    if ((int64_t)T * d >= (int64_t(1) << 31) || ((int64_t)T * k + (int64_t)E * B) * f >= (int64_t(1) << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "activation buffers above 2^31 elements");
+    return MOE_OK;
+}
+
+int64_t max_padded(int T, int k, int E, int B) { return (int64_t)T * k + (int64_t)E * B - k; }
+int64_t max_blocks(int T, int k, int E, int B) { return (max_padded(T, k, E, B) + B - 1) / B; }
+
+// ----------------------------------------------------------- config choice
+struct Config {
+    int B, stage, ksplit;
+};
+
+int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
+    // enough workgroups for ~4 per CU in the down projection
+    const int64_t rows = (int64_t)T * k;
+    const int64_t blocks = std::min<int64_t>(max_blocks(T, k, E, B), std::min<int64_t>(E, rows) + rows / B);
+    const int CT = (d % 256 == 0) ? 4 : 2;
+    const int64_t ntiles = d / (64 * CT);
+    const int64_t base = std::max<int64_t>(1, ntiles * blocks);
+    const int KS = quant == 0 ? 64 : 128;
+    int ks = (int)std::min<int64_t>((4 * (int64_t)cu + base - 1) / base, f / KS / 4);
+    return std::max(1, ks);
+}
+
+Config choose(int T, int d, int f, int E, int k, int quant, int cu) {
+    Config c;
+    c.B = 32;
+    c.stage = 2;
+    c.ksplit = auto_ksplit(T, d, f, E, k, c.B, quant, cu);
+    return c;
+}
+
+// -------------------------------------------------------------- stage 1/2
+struct Gemm1Ws {
+    uint8_t *qx = nullptr;
+    float *sx = nullptr;
+    uint16_t *hb = nullptr;
+    float *amax = nullptr;
+};
+
+Gemm1Ws carve_gemm1(Carver &c, int T, int d, int f, int E, int k, int B, int quant) {
+    Gemm1Ws w;
+    const size_t P = (size_t)max_padded(T, k, E, B);
+    if (quant != 0) {
+        w.qx = c.take<uint8_t>((size_t)T * d);
+        w.sx = c.take<float>(quant == 1 ? (size_t)T : (size_t)T * (d / 128));
+    }
+    if (quant == 1) {
+        w.hb = c.take<uint16_t>(P * f);
+        w.amax = c.take<float>(P);
+    }
+    return w;
+}
+
+int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x, const void *w13,
+              const float *w13_scale, const int32_t *sorted_ids, const int32_t *seid,
+              const int32_t *num_valid, void *h, float *h_scale, const Gemm1Ws &w, hipStream_t s) {
+    Gemm1Args g{};
+    g.sh = GemmShape{T, d, f, E, k, B, quant};
+    g.w13 = w13;
+    g.w13_scale = w13_scale;
+    g.sorted_ids = sorted_ids;
+    g.sorted_expert_ids = seid;
+    g.num_valid = num_valid;
+    const size_t P = (size_t)max_padded(T, k, E, B);
+    if (quant == 0) {
+        g.a = x;
+        g.h = h;
+    } else {
+        HIP_TRY(launch_quant_act(static_cast<const uint16_t *>(x), T, d, quant == 1 ? d : 128, w.qx,
+                                 w.sx, s),
+                "activation quantisation launch");
+        g.a = w.qx;
+        g.a_scale = w.sx;
+        if (quant == 1) {
+            HIP_TRY(launch_fill_f32(w.amax, P, 0.0f, s), "fill launch");
+            g.h = w.hb;
+            g.h_scale = w.amax;
+        } else {
+            g.h = h;
+            g.h_scale = h_scale;
+        }
+    }
+    if (!stream_gemm1_supported(g.sh))
+        return fail(MOE_ERR_UNSUPPORTED, "no GEMM1 kernel for B=%d", B);
+    HIP_TRY(launch_stream_gemm1(g, 2, s), "GEMM1 launch");
+    if (quant == 1)
+        HIP_TRY(launch_quant_h_rows(w.hb, w.amax, (int)P, f, num_valid, static_cast<uint8_t *>(h),
+                                    h_scale, s),
+                "h quantisation launch");
+    return MOE_OK;
+}
+
+float *carve_gemm2(Carver &c, int T, int d) { return c.take<float>((size_t)T * d); }
+
+int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, const void *h,
+              const float *h_scale, const void *w2, const float *w2_scale,
+              const int32_t *sorted_ids, const float *sorted_w, const int32_t *seid,
+              const int32_t *num_valid, void *out, float *acc, hipStream_t s) {
+    Gemm2Args g{};
+    g.sh = GemmShape{T, d, f, E, k, B, quant};
+    g.h = h;
+    g.h_scale = h_scale;
+    g.w2 = w2;
+    g.w2_scale = w2_scale;
+    g.sorted_ids = sorted_ids;
+    g.sorted_w = sorted_w;
+    g.sorted_expert_ids = seid;
+    g.num_valid = num_valid;
+    g.acc = acc;
+    if (ksplit <= 0) ksplit = auto_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
+    g.ksplit = ksplit;
+    if (!stream_gemm2_supported(g.sh))
+        return fail(MOE_ERR_UNSUPPORTED, "no GEMM2 kernel for B=%d", B);
+    HIP_TRY(launch_fill_f32(acc, (size_t)T * d, 0.0f, s), "fill launch");
+    HIP_TRY(launch_stream_gemm2(g, 4, ksplit, s), "GEMM2 launch");
+    HIP_TRY(launch_finalize(acc, static_cast<uint16_t *>(out), (size_t)T * d, s), "finalize launch");
+    return MOE_OK;
+}
+
+struct FusedWs {
+    int32_t *topk_ids = nullptr;
+    float *topk_w = nullptr;
+    int32_t *sorted_ids = nullptr, *seid = nullptr, *counts = nullptr, *offsets = nullptr,
+            *num_valid = nullptr;
+    float *sorted_w = nullptr;
+    void *h = nullptr;
+    float *h_scale = nullptr;
+    Gemm1Ws g1;
+    float *acc = nullptr;
+};
+
+FusedWs carve_fused(Carver &c, int T, int d, int f, int E, int k, int quant, int B, bool route) {
+    FusedWs w;
+    const size_t P = (size_t)max_padded(T, k, E, B), NB = (size_t)max_blocks(T, k, E, B);
+    if (route) {
+        w.topk_ids = c.take<int32_t>((size_t)T * k);
+        w.topk_w = c.take<float>((size_t)T * k);
+    }
+    w.sorted_ids = c.take<int32_t>(P);
+    w.sorted_w = c.take<float>(P);
+    w.seid = c.take<int32_t>(NB);
+    w.counts = c.take<int32_t>(E);
+    w.offsets = c.take<int32_t>(E + 1);
+    w.num_valid = c.take<int32_t>(1);
+    w.h = c.take<uint8_t>(P * f * (quant == 0 ? 2 : 1));
+    if (quant == 1) w.h_scale = c.take<float>(P);
+    if (quant == 2) w.h_scale = c.take<float>(P * (f / 128));
+    w.g1 = carve_gemm1(c, T, d, f, E, k, B, quant);
+    w.acc = carve_gemm2(c, T, d);
+    return w;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int64_t moe_sort_max_padded(int T, int k, int E, int B) {
+    if (T < 0 || k < 1 || k > E || B < 1) return -1;
+    return max_padded(T, k, E, B);
+}
+
+int64_t moe_sort_max_blocks(int T, int k, int E, int B) {
+    if (T < 0 || k < 1 || k > E || B < 1) return -1;
+    return max_blocks(T, k, E, B);
+}
+
+int moe_topk(const float *logits, int T, int E, int k, int score, int renorm, int32_t *topk_ids,
+             float *topk_w, void *stream) {
+    g_err[0] = 0;
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
+        return fail(MOE_ERR_INVALID_ARG, "bad routing shape T=%d E=%d k=%d", T, E, k);
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARG, "bad score %d", score);
+    if (T > 0 && (!logits || !topk_ids || !topk_w)) return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    HIP_TRY(launch_topk(logits, T, E, k, score, renorm, topk_ids, topk_w, (hipStream_t)stream),
+            "topk launch");
+    return MOE_OK;
+}
+
+int moe_sort(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, int B,
+             int32_t *sorted_ids, float *sorted_w, int32_t *sorted_expert_ids,
+             int32_t *expert_counts, int32_t *expert_offsets, int32_t *num_valid, void *stream) {
+    g_err[0] = 0;
+    if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || B < 1 || B > 1024)
+        return fail(MOE_ERR_INVALID_ARG, "bad sort shape T=%d k=%d E=%d B=%d", T, k, E, B);
+    if ((int64_t)T * k > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "T*k above 2^24");
+    if ((T > 0 && (!topk_ids || !topk_w)) || !sorted_ids || !sorted_w || !sorted_expert_ids ||
+        !expert_counts || !expert_offsets || !num_valid)
+        return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    HIP_TRY(launch_sort(topk_ids, topk_w, T, k, E, B, sorted_ids, sorted_w, sorted_expert_ids,
+                        expert_counts, expert_offsets, num_valid, (hipStream_t)stream),
+            "sort launch");
+    return MOE_OK;
+}
+
+int moe_quant_act(const void *x, int rows, int cols, int group, uint8_t *codes, float *scales,
+                  void *stream) {
+    g_err[0] = 0;
+    if (rows < 0 || cols < 1 || group < 1) return fail(MOE_ERR_INVALID_ARG, "bad quant shape");
+    if (cols % 128 || !(group == cols || group == 128))
+        return fail(MOE_ERR_UNSUPPORTED, "cols=%d group=%d: need cols %% 128 == 0 and group in {128, cols}",
+                    cols, group);
+    if (rows > 0 && (!x || !codes || !scales)) return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    HIP_TRY(launch_quant_act(static_cast<const uint16_t *>(x), rows, cols, group, codes, scales,
+                             (hipStream_t)stream),
+            "quant launch");
+    return MOE_OK;
+}
+
+size_t moe_gemm1_workspace_bytes(int T, int d, int f, int E, int k, int B, int quant) {
+    if (check_shape(T, d, f, E, k, B, quant) != MOE_OK) return 0;
+    Carver c(nullptr);
+    carve_gemm1(c, T, d, f, E, k, B, quant);
+    return c.bytes();
+}
+
+int moe_gemm1_swiglu(int T, int d, int f, int E, int k, int B, int quant, const void *x,
+                     const void *w13, const float *w13_scale, const int32_t *sorted_ids,
+                     const int32_t *sorted_expert_ids, const int32_t *num_valid, void *h,
+                     float *h_scale, void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    int rc = check_shape(T, d, f, E, k, B, quant);
+    if (rc) return rc;
+    if (!w13 || !sorted_ids || !sorted_expert_ids || !num_valid || !h || (T > 0 && !x))
+        return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    if (quant != 0 && (!w13_scale || !h_scale))
+        return fail(MOE_ERR_INVALID_ARG, "fp8 needs w13_scale and h_scale");
+    Carver c(nullptr);
+    carve_gemm1(c, T, d, f, E, k, B, quant);
+    if (ws_bytes < c.bytes() || (c.bytes() > 0 && !ws))
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, c.bytes());
+    if (T == 0) return MOE_OK;
+    Carver cw(ws);
+    Gemm1Ws w = carve_gemm1(cw, T, d, f, E, k, B, quant);
+    return run_gemm1(T, d, f, E, k, B, quant, x, w13, w13_scale, sorted_ids, sorted_expert_ids,
+                     num_valid, h, h_scale, w, (hipStream_t)stream);
+}
+
+size_t moe_gemm2_workspace_bytes(int T, int d, int f, int E, int k, int B, int quant) {
+    if (check_shape(T, d, f, E, k, B, quant) != MOE_OK) return 0;
+    Carver c(nullptr);
+    carve_gemm2(c, T, d);
+    return c.bytes();
+}
+
+int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int ksplit,
+                      const void *h, const float *h_scale, const void *w2, const float *w2_scale,
+                      const int32_t *sorted_ids, const float *sorted_w,
+                      const int32_t *sorted_expert_ids, const int32_t *num_valid, void *out,
+                      void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    int rc = check_shape(T, d, f, E, k, B, quant);
+    if (rc) return rc;
+    if (!h || !w2 || !sorted_ids || !sorted_w || !sorted_expert_ids || !num_valid ||
+        (T > 0 && !out))
+        return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    if (quant != 0 && (!w2_scale || !h_scale))
+        return fail(MOE_ERR_INVALID_ARG, "fp8 needs w2_scale and h_scale");
+    Carver c(nullptr);
+    carve_gemm2(c, T, d);
+    if (ws_bytes < c.bytes() || (c.bytes() > 0 && !ws))
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, c.bytes());
+    if (T == 0) return MOE_OK;
+    Carver cw(ws);
+    float *acc = carve_gemm2(cw, T, d);
+    return run_gemm2(T, d, f, E, k, B, quant, ksplit, h, h_scale, w2, w2_scale, sorted_ids,
+                     sorted_w, sorted_expert_ids, num_valid, out, acc, (hipStream_t)stream);
+}
+
+int moe_select_config(int T, int d, int f, int E, int k, int quant, int cu_count, int *B,
+                      int *stage, int *ksplit) {
+    g_err[0] = 0;
+    if (!B || !stage || !ksplit) return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    int rc = check_shape(T, d, f, E, k, 32, quant);
+    if (rc) return rc;
+    if (cu_count <= 0) cu_count = cu_count_cached();
+    Config c = choose(T, d, f, E, k, quant, cu_count);
+    *B = c.B;
+    *stage = c.stage;
+    *ksplit = c.ksplit;
+    return MOE_OK;
+}
+
+static int resolve(int T, int d, int f, int E, int k, int quant, int *B, int *stage) {
+    if (*B == 0 || *stage == 0) {
+        Config c = choose(T, d, f, E, k, quant, cu_count_cached());
+        if (*B == 0) *B = c.B;
+        if (*stage == 0) *stage = c.stage;
+    }
+    if (*stage != 1 && *stage != 2) return fail(MOE_ERR_INVALID_ARG, "bad stage %d", *stage);
+    if (*stage == 1) return fail(MOE_ERR_UNSUPPORTED, "the one-stage kernel is not built");
+    return check_shape(T, d, f, E, k, *B, quant);
+}
+
+size_t fused_moe_workspace_bytes(int T, int d, int f, int E, int k, int quant, int B, int stage) {
+    if (resolve(T, d, f, E, k, quant, &B, &stage) != MOE_OK) return 0;
+    Carver c(nullptr);
+    carve_fused(c, T, d, f, E, k, quant, B, true);
+    return c.bytes();
+}
+
+int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renorm,
+              const float *logits, const int32_t *topk_ids, const float *topk_w, const void *x,
+              const void *w13, const float *w13_scale, const void *w2, const float *w2_scale,
+              int B, int stage, int ksplit, void *out, void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    int rc = resolve(T, d, f, E, k, quant, &B, &stage);
+    if (rc) return rc;
+    if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARG, "bad score %d", score);
+    if (T > 0 && (!x || !out || (!logits && (!topk_ids || !topk_w))))
+        return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    if (!w13 || !w2) return fail(MOE_ERR_INVALID_ARG, "null weights");
+    if (quant != 0 && (!w13_scale || !w2_scale)) return fail(MOE_ERR_INVALID_ARG, "fp8 needs scales");
+    Carver c(nullptr);
+    carve_fused(c, T, d, f, E, k, quant, B, true);
+    if (ws_bytes < c.bytes() || !ws)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, c.bytes());
+    if (T == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    Carver cw(ws);
+    FusedWs w = carve_fused(cw, T, d, f, E, k, quant, B, true);
+    const int32_t *ids = topk_ids;
+    const float *wt = topk_w;
+    if (logits) {
+        HIP_TRY(launch_topk(logits, T, E, k, score, renorm, w.topk_ids, w.topk_w, s), "topk launch");
+        ids = w.topk_ids;
+        wt = w.topk_w;
+    }
+    HIP_TRY(launch_sort(ids, wt, T, k, E, B, w.sorted_ids, w.sorted_w, w.seid, w.counts, w.offsets,
+                        w.num_valid, s),
+            "sort launch");
+    rc = run_gemm1(T, d, f, E, k, B, quant, x, w13, w13_scale, w.sorted_ids, w.seid, w.num_valid,
+                   w.h, w.h_scale, w.g1, s);
+    if (rc) return rc;
+    return run_gemm2(T, d, f, E, k, B, quant, ksplit, w.h, w.h_scale, w2, w2_scale, w.sorted_ids,
+                     w.sorted_w, w.seid, w.num_valid, out, w.acc, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// common.h -- device helpers shared by the gfx950 kernels of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+    __bf16 b = (__bf16)v;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __builtin_bit_cast(float, b << 16);
+}
+
+// Two fp32 -> two OCP e4m3 codes (low 16 bits), round to nearest even,
+// saturating at +-448 (the clamp makes saturation independent of the
+// converter's overflow mode). Inputs are finite.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
+    a = fminf(fmaxf(a, -448.0f), 448.0f);
+    b = fminf(fmaxf(b, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Wave-wide reductions (64 lanes).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & (WAVE - 1);
+    return lane == 0 ? 0ull : (~0ull >> (WAVE - lane));
+}
+
+// Non-returning fp32 atomic add to global memory (global_atomic_add_f32).
+__device__ __forceinline__ void atomic_add_f32(float *p, float v) { unsafeAtomicAdd(p, v); }
+
+// Max of non-negative floats through their bit patterns (monotone for >= 0).
+__device__ __forceinline__ void atomic_max_nonneg(float *p, float v) {
+    atomicMax(reinterpret_cast<unsigned int *>(p), __float_as_uint(v));
+}
+
+}  // namespace moe

@@ -1,0 +1,407 @@
+// gemm_stream.hip -- weight-streaming grouped GEMMs for small sort blocks.
+//
+// Grouped GEMM over the sorted assignment list (grouped GEMMs in place of
+// masked dense GEMMs: rocketrecap.com/entries/19116, talk summary at 5:58;
+// the two stages of the AITER walk-through, itsolotime.com/th/archives/32381,
+// section 3.2). One workgroup = one sort block (B <= 32 rows, all of one
+// expert) x a slice of output columns; 4 waves split the columns.
+//
+// Both operands have the reduction dimension contiguous, so every lane loads
+// its MFMA fragments straight from global memory: lane l serves row/column
+// l % 16 and the 32-byte piece (l / 16) of each 128-byte K step, i.e. a wave
+// reads whole 128-byte lines of 16 rows. The same K permutation is used for
+// both operands, so the v_mfma_f32_16x16x32 sums are the plain dot products.
+// No LDS: weights are used by exactly one workgroup, which is the decode
+// (weight-streaming, HBM-bound) regime.
+//
+//   GEMM1: C[slot, n] over K = d, n in gate rows n0.. and up rows f + n0..,
+//          epilogue h = silu(gate) * up -> bf16 (quant 0/1) or e4m3 per
+//          1x128 block (quant 2); quant 1 also records the row amax.
+//   GEMM2: C[slot, n] over K = f (optionally K-split across blockIdx.y),
+//          epilogue acc[token, n] += sorted_w[slot] * C (fp32 atomics).
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+struct StreamParams {
+    const uint8_t *a;        // A base (bytes)
+    const float *a_scale;
+    const uint8_t *w;        // weights base (bytes) [E, N_total, K]
+    const float *w_scale;
+    const int32_t *sorted_ids;
+    const float *sorted_w;
+    const int32_t *seid;
+    void *out;               // GEMM1: h ; GEMM2: acc fp32 [T, d]
+    float *out_scale;        // GEMM1 quant 1: row amax [P]; quant 2: h_scale [P, f/128]
+    int T, d, f, k, B;
+    int kchunk;              // K elements per blockIdx.y
+};
+
+template <int QUANT>
+struct Elem {
+    static constexpr int bytes = QUANT == 0 ? 2 : 1;
+    static constexpr int kstep = 128 / bytes;  // K elements per 128-byte step
+};
+
+struct Frag {
+    u32x4 lo, hi;  // 32 contiguous bytes of one row's 128-byte K step
+};
+
+__device__ __forceinline__ Frag load_frag(const uint8_t *p) {
+    Frag f;
+    f.lo = *reinterpret_cast<const u32x4 *>(p);
+    f.hi = *reinterpret_cast<const u32x4 *>(p + 16);
+    return f;
+}
+
+// acc += A . B over one 128-byte K step.
+template <int QUANT>
+__device__ __forceinline__ f32x4 mma_step(const Frag &a, const Frag &b, f32x4 acc) {
+    if constexpr (QUANT == 0) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.lo),
+                                                       __builtin_bit_cast(bf16x8, b.lo), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.hi),
+                                                       __builtin_bit_cast(bf16x8, b.hi), acc, 0, 0, 0);
+    } else {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const long a0 = __builtin_bit_cast(long, u32x2{a.lo.x, a.lo.y});
+        const long a1 = __builtin_bit_cast(long, u32x2{a.lo.z, a.lo.w});
+        const long a2 = __builtin_bit_cast(long, u32x2{a.hi.x, a.hi.y});
+        const long a3 = __builtin_bit_cast(long, u32x2{a.hi.z, a.hi.w});
+        const long b0 = __builtin_bit_cast(long, u32x2{b.lo.x, b.lo.y});
+        const long b1 = __builtin_bit_cast(long, u32x2{b.lo.z, b.lo.w});
+        const long b2 = __builtin_bit_cast(long, u32x2{b.hi.x, b.hi.y});
+        const long b3 = __builtin_bit_cast(long, u32x2{b.hi.z, b.hi.w});
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2, b2, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a3, b3, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// RT: 16-row tiles per block (B = 16 * RT). CT: 16-column tiles per wave
+// (GEMM1: CT gate tiles + CT matching up tiles).
+template <int QUANT, int RT, int CT, bool GEMM1>
+__global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
+    constexpr int ES = Elem<QUANT>::bytes;
+    constexpr int KS = Elem<QUANT>::kstep;
+    constexpr int NT = GEMM1 ? 2 * CT : CT;
+
+    const int blk = blockIdx.z;
+    const int e = p.seid[blk];
+    if (e < 0) return;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int sentinel = p.T * p.k;
+    const int K = GEMM1 ? p.d : p.f;
+    const int Ntot = GEMM1 ? 2 * p.f : p.d;   // weight rows per expert
+    const int n0 = (blockIdx.x * 4 + wave) * CT * 16;
+    const int kbeg = blockIdx.y * p.kchunk;
+    const int kend = min(K, kbeg + p.kchunk);
+    const int slot0 = blk * p.B;
+
+    // rows of this lane's A fragments, and which 16-row tiles hold real rows
+    const uint8_t *arow[RT];
+    bool arow_ok[RT];
+    bool live[RT];
+    int a_of_lane[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int slot = slot0 + rt * 16 + lr;
+        const int a = p.sorted_ids[slot];
+        a_of_lane[rt] = a;
+        live[rt] = p.sorted_ids[slot0 + rt * 16] < sentinel;
+        if (GEMM1) {
+            arow_ok[rt] = a < sentinel;
+            const int t = arow_ok[rt] ? a / p.k : 0;
+            arow[rt] = p.a + ((size_t)t * K + lg * (32 / ES)) * ES;
+        } else {
+            arow_ok[rt] = true;
+            arow[rt] = p.a + ((size_t)slot * K + lg * (32 / ES)) * ES;
+        }
+    }
+    const uint8_t *wrow[NT];
+    const uint8_t *wexp = p.w + (size_t)e * Ntot * K * ES;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int n = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16 + lr;
+        wrow[nt] = wexp + ((size_t)n * K + lg * (32 / ES)) * ES;
+    }
+
+    f32x4 acc[RT][NT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // per-row scale rows for the 1x128 / 128x128 block-scaled product
+    int srow[RT][4];
+    if constexpr (QUANT == 2) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = lg * 4 + i;
+                if (GEMM1) {
+                    const int a = __shfl(a_of_lane[rt], r, 64);
+                    srow[rt][i] = a < sentinel ? a / p.k : -1;
+                } else {
+                    srow[rt][i] = slot0 + rt * 16 + r;
+                }
+            }
+    }
+
+    Frag fa[2][RT], fb[2][NT];
+    auto load = [&](int buf, int kk) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (live[rt]) {
+                fa[buf][rt] = load_frag(arow[rt] + (size_t)kk * ES);
+                if (!arow_ok[rt]) {
+                    fa[buf][rt].lo = u32x4{0, 0, 0, 0};
+                    fa[buf][rt].hi = u32x4{0, 0, 0, 0};
+                }
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) fb[buf][nt] = load_frag(wrow[nt] + (size_t)kk * ES);
+    };
+    auto compute = [&](int buf, int kk) {
+        if constexpr (QUANT == 2) {
+            const int kb = kk / 128;
+            float sw[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int nrow = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16;
+                sw[nt] = p.w_scale[((size_t)e * (Ntot / 128) + nrow / 128) * (K / 128) + kb];
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                if (!live[rt]) continue;
+                float sa[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sa[i] = srow[rt][i] >= 0 ? p.a_scale[(size_t)srow[rt][i] * (K / 128) + kb] : 0.f;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const f32x4 part = mma_step<QUANT>(fa[buf][rt], fb[buf][nt], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[rt][nt][i] += part[i] * (sa[i] * sw[nt]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                if (!live[rt]) continue;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[rt][nt] = mma_step<QUANT>(fa[buf][rt], fb[buf][nt], acc[rt][nt]);
+            }
+        }
+    };
+
+    int kk = kbeg;
+    if (kk < kend) {
+        load(0, kk);
+        while (true) {
+            const bool more1 = kk + KS < kend;
+            if (more1) load(1, kk + KS);
+            compute(0, kk);
+            if (!more1) break;
+            kk += KS;
+            const bool more2 = kk + KS < kend;
+            if (more2) load(0, kk + KS);
+            compute(1, kk);
+            if (!more2) break;
+            kk += KS;
+        }
+    }
+
+    // ------------------------------------------------------------ epilogue
+    if constexpr (GEMM1) {
+        const int f = p.f;
+        __shared__ float amax_lds[4][RT * 16];
+        float hv[RT][CT][4];
+        float rmax[RT][4];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = lg * 4 + i;
+                const int a = __shfl(a_of_lane[rt], r, 64);
+                const int t = a < sentinel ? a / p.k : 0;
+                const float sx = (QUANT == 1 && a < sentinel) ? p.a_scale[t] : 1.0f;
+                float m = 0.0f;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    float g = acc[rt][ct][i], u = acc[rt][CT + ct][i];
+                    if constexpr (QUANT == 1) {
+                        const int n = n0 + ct * 16 + lr;
+                        g = g * sx * p.w_scale[(size_t)e * Ntot + n];
+                        u = u * sx * p.w_scale[(size_t)e * Ntot + f + n];
+                    }
+                    const float h = bf16_bits_to_f32(f32_to_bf16_bits(silu(g) * u));
+                    hv[rt][ct][i] = h;
+                    m = fmaxf(m, fabsf(h));
+                }
+                if constexpr (QUANT != 0) {
+#pragma unroll
+                    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                }
+                rmax[rt][i] = m;
+            }
+        if constexpr (QUANT == 2) {
+            if (lr == 0)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) amax_lds[wave][rt * 16 + lg * 4 + i] = rmax[rt][i];
+            __syncthreads();
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int slot = slot0 + rt * 16 + lg * 4 + i;
+                float s = 1.0f;
+                if constexpr (QUANT == 2) {
+                    const int r = rt * 16 + lg * 4 + i;
+                    const float am = fmaxf(fmaxf(amax_lds[0][r], amax_lds[1][r]),
+                                           fmaxf(amax_lds[2][r], amax_lds[3][r]));
+                    s = am == 0.0f ? 1.0f : am / 448.0f;
+                    // one 128-column block per workgroup (4 waves x CT x 16 = 128)
+                    if (wave == 0 && lr == 0)
+                        p.out_scale[(size_t)slot * (f / 128) + (blockIdx.x * 4 * CT * 16) / 128] = s;
+                }
+                if constexpr (QUANT == 1) {
+                    if (lr == 0) atomic_max_nonneg(p.out_scale + slot, rmax[rt][i]);
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int n = n0 + ct * 16 + lr;
+                    if constexpr (QUANT == 2) {
+                        uint8_t *h = reinterpret_cast<uint8_t *>(p.out);
+                        h[(size_t)slot * f + n] = (uint8_t)f32x2_to_e4m3x2(hv[rt][ct][i] / s, 0.0f);
+                    } else {
+                        uint16_t *h = reinterpret_cast<uint16_t *>(p.out);
+                        h[(size_t)slot * f + n] = f32_to_bf16_bits(hv[rt][ct][i]);
+                    }
+                }
+            }
+    } else {
+        float *accg = reinterpret_cast<float *>(p.out);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (!live[rt]) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = lg * 4 + i;
+                const int slot = slot0 + rt * 16 + r;
+                const int a = __shfl(a_of_lane[rt], r, 64);
+                if (a >= sentinel) continue;
+                float wgt = p.sorted_w[slot];
+                if constexpr (QUANT == 1) wgt *= p.a_scale[slot];
+                float *dst = accg + (size_t)(a / p.k) * p.d;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int n = n0 + ct * 16 + lr;
+                    float y = acc[rt][ct][i];
+                    if constexpr (QUANT == 1) y *= p.w_scale[(size_t)e * Ntot + n];
+                    atomic_add_f32(dst + n, wgt * y);
+                }
+            }
+        }
+    }
+}
+
+template <int QUANT, int RT, int CT, bool GEMM1>
+hipError_t run(const StreamParams &p, dim3 grid, hipStream_t s) {
+    k_gemm_stream<QUANT, RT, CT, GEMM1><<<grid, 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+template <bool GEMM1, int QUANT>
+hipError_t dispatch_rt_ct(const StreamParams &p, int RT, int CT, dim3 grid, hipStream_t s) {
+    if (RT == 1) {
+        if (CT == 1) return run<QUANT, 1, 1, GEMM1>(p, grid, s);
+        if (CT == 2) return run<QUANT, 1, 2, GEMM1>(p, grid, s);
+        if (!GEMM1 && CT == 4) return run<QUANT, 1, 4, GEMM1>(p, grid, s);
+    } else if (RT == 2) {
+        if (CT == 1) return run<QUANT, 2, 1, GEMM1>(p, grid, s);
+        if (CT == 2) return run<QUANT, 2, 2, GEMM1>(p, grid, s);
+        if (!GEMM1 && CT == 4) return run<QUANT, 2, 4, GEMM1>(p, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool GEMM1>
+hipError_t dispatch(const StreamParams &p, int quant, int RT, int CT, dim3 grid, hipStream_t s) {
+    if (quant == 0) return dispatch_rt_ct<GEMM1, 0>(p, RT, CT, grid, s);
+    if (quant == 1) return dispatch_rt_ct<GEMM1, 1>(p, RT, CT, grid, s);
+    return dispatch_rt_ct<GEMM1, 2>(p, RT, CT, grid, s);
+}
+
+}  // namespace
+
+bool stream_gemm1_supported(const GemmShape &sh) {
+    return (sh.B == 16 || sh.B == 32) && sh.f % 128 == 0 && sh.d % 128 == 0;
+}
+
+bool stream_gemm2_supported(const GemmShape &sh) {
+    return (sh.B == 16 || sh.B == 32) && sh.f % 128 == 0 && sh.d % 128 == 0;
+}
+
+hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
+    const GemmShape &sh = g.sh;
+    StreamParams p{};
+    p.a = static_cast<const uint8_t *>(g.a);
+    p.a_scale = g.a_scale;
+    p.w = static_cast<const uint8_t *>(g.w13);
+    p.w_scale = g.w13_scale;
+    p.sorted_ids = g.sorted_ids;
+    p.seid = g.sorted_expert_ids;
+    p.out = g.h;
+    p.out_scale = g.h_scale;
+    p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
+    p.kchunk = sh.d;
+    if (sh.quant == 2) CT = 2;  // one 128-column quant block per workgroup
+    const int RT = sh.B / 16;
+    const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
+    const int NB = (P + sh.B - 1) / sh.B;
+    const dim3 grid(sh.f / (64 * CT), 1, NB);
+    return dispatch<true>(p, sh.quant, RT, CT, grid, s);
+}
+
+hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream_t s) {
+    const GemmShape &sh = g.sh;
+    StreamParams p{};
+    p.a = static_cast<const uint8_t *>(g.h);
+    p.a_scale = g.h_scale;
+    p.w = static_cast<const uint8_t *>(g.w2);
+    p.w_scale = g.w2_scale;
+    p.sorted_ids = g.sorted_ids;
+    p.sorted_w = g.sorted_w;
+    p.seid = g.sorted_expert_ids;
+    p.out = g.acc;
+    p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
+    const int KS = sh.quant == 0 ? 64 : 128;
+    const int steps = sh.f / KS;
+    if (ksplit < 1) ksplit = 1;
+    if (ksplit > steps) ksplit = steps;
+    const int steps_per = (steps + ksplit - 1) / ksplit;
+    p.kchunk = steps_per * KS;
+    ksplit = (steps + steps_per - 1) / steps_per;
+    const int RT = sh.B / 16;
+    const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
+    const int NB = (P + sh.B - 1) / sh.B;
+    while (CT > 1 && sh.d % (64 * CT) != 0) CT >>= 1;
+    const dim3 grid(sh.d / (64 * CT), ksplit, NB);
+    return dispatch<false>(p, sh.quant, RT, CT, grid, s);
+}
+
+}  // namespace moe

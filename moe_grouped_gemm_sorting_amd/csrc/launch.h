@@ -1,0 +1,65 @@
+// launch.h -- host-side launchers of libmoe's kernels (internal to the library).
+// Every launcher only enqueues work on `s` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_topk(const float *logits, int T, int E, int k, int score, int renorm,
+                       int32_t *ids, float *w, hipStream_t s);
+
+hipError_t launch_sort(const int32_t *ids, const float *w, int T, int k, int E, int B,
+                       int32_t *sorted_ids, float *sorted_w, int32_t *sorted_expert_ids,
+                       int32_t *counts, int32_t *offsets, int32_t *num_valid, hipStream_t s);
+
+// codes [rows, cols], scales [rows, cols / group]
+hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, uint8_t *codes,
+                            float *scales, hipStream_t s);
+
+// h rows: bf16 [rows, cols] with row amax [rows] -> e4m3 codes + scale [rows]
+hipError_t launch_quant_h_rows(const uint16_t *h, const float *amax, int rows, int cols,
+                               const int32_t *num_valid, uint8_t *codes, float *scales,
+                               hipStream_t s);
+
+hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
+
+// acc fp32 [n] -> bf16 [n]
+hipError_t launch_finalize(const float *acc, uint16_t *out, size_t n, hipStream_t s);
+
+struct GemmShape {
+    int T, d, f, E, k, B, quant;
+};
+
+struct Gemm1Args {
+    GemmShape sh;
+    const void *a;          // x bf16 [T, d] (quant 0) or e4m3 codes [T, d]
+    const float *a_scale;   // fp8: [T] or [T, d/128]
+    const void *w13;
+    const float *w13_scale;
+    const int32_t *sorted_ids, *sorted_expert_ids, *num_valid;
+    void *h;                // quant 0/1: bf16 [P, f]; quant 2: e4m3 [P, f]
+    float *h_scale;         // quant 1: row amax [P] (zeroed by the caller); quant 2: [P, f/128]
+};
+
+struct Gemm2Args {
+    GemmShape sh;
+    int ksplit;
+    const void *h;
+    const float *h_scale;
+    const void *w2;
+    const float *w2_scale;
+    const int32_t *sorted_ids;
+    const float *sorted_w;
+    const int32_t *sorted_expert_ids, *num_valid;
+    float *acc;             // fp32 [T, d], zeroed by the caller
+};
+
+hipError_t launch_gemm1(const Gemm1Args &a, hipStream_t s);
+hipError_t launch_gemm2(const Gemm2Args &a, hipStream_t s);
+bool gemm1_supported(const GemmShape &sh);
+bool gemm2_supported(const GemmShape &sh);
+
+}  // namespace moe

@@ -1,0 +1,153 @@
+// quant.hip -- dynamic e4m3 quantisation of activations and of the
+// intermediate h, plus the accumulator fill and the final fp32 -> bf16 pass.
+//
+// Quantisation rule (the per_Token and per_1x128 quant types of the AITER
+// walk-through, itsolotime.com/th/archives/32381, sections 1.1 and 3.2):
+// s = amax / 448 over the group (s = 1 when amax = 0), q = e4m3(v / s) with
+// round-to-nearest-even and saturation. Both divisions are IEEE
+// correctly rounded.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// One workgroup of 256 threads per row. Thread t owns the 8-element chunks
+// t, t + 256, ... (16-byte loads). GROUP_ROW: one scale for the whole row;
+// otherwise one scale per 128 columns (16 consecutive chunks = 16 lanes).
+template <bool GROUP_ROW>
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t *__restrict__ x,
+                                                    const float *__restrict__ row_amax,
+                                                    const int32_t *__restrict__ num_valid,
+                                                    int cols, uint8_t *__restrict__ codes,
+                                                    float *__restrict__ scales) {
+    const int r = blockIdx.x;
+    if (num_valid && r >= *num_valid) return;
+    const int tid = threadIdx.x;
+    const int nchunk = cols / 8;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)r * cols);
+    uint2 *dst = reinterpret_cast<uint2 *>(codes + (size_t)r * cols);
+    __shared__ float red[4];
+
+    float s_row = 1.0f;
+    if (GROUP_ROW) {
+        float amax;
+        if (row_amax) {
+            amax = row_amax[r];
+        } else {
+            float m = 0.0f;
+            for (int c = tid; c < nchunk; c += 256) {
+                const uint4 q = src[c];
+                const uint32_t wds[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    m = fmaxf(m, fabsf(bf16_bits_to_f32(wds[i] & 0xffffu)));
+                    m = fmaxf(m, fabsf(bf16_bits_to_f32(wds[i] >> 16)));
+                }
+            }
+            m = wave_max(m);
+            if ((tid & 63) == 0) red[tid >> 6] = m;
+            __syncthreads();
+            amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        }
+        s_row = amax == 0.0f ? 1.0f : amax / 448.0f;
+        if (tid == 0) scales[r] = s_row;
+    }
+    // chunk loop; for the 1x128 grouping all 16 lanes of a group are in the
+    // same iteration because 256 is a multiple of 16.
+    for (int c0 = 0; c0 < nchunk; c0 += 256) {
+        const int c = c0 + tid;
+        const bool live = c < nchunk;
+        float v[8];
+        if (live) {
+            const uint4 q = src[c];
+            const uint32_t wds[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = bf16_bits_to_f32(wds[i] & 0xffffu);
+                v[2 * i + 1] = bf16_bits_to_f32(wds[i] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+        }
+        float s = s_row;
+        if (!GROUP_ROW) {
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            s = m == 0.0f ? 1.0f : m / 448.0f;
+            if (live && (c & 15) == 0) scales[(size_t)r * (cols / 128) + c / 16] = s;
+        }
+        if (live) {
+            uint32_t lo = f32x2_to_e4m3x2(v[0] / s, v[1] / s) |
+                          (f32x2_to_e4m3x2(v[2] / s, v[3] / s) << 16);
+            uint32_t hi = f32x2_to_e4m3x2(v[4] / s, v[5] / s) |
+                          (f32x2_to_e4m3x2(v[6] / s, v[7] / s) << 16);
+            dst[c] = make_uint2(lo, hi);
+        }
+    }
+}
+
+hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, uint8_t *codes,
+                            float *scales, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    if (group == cols)
+        k_quant_rows<true><<<rows, 256, 0, s>>>(x, nullptr, nullptr, cols, codes, scales);
+    else
+        k_quant_rows<false><<<rows, 256, 0, s>>>(x, nullptr, nullptr, cols, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_h_rows(const uint16_t *h, const float *amax, int rows, int cols,
+                               const int32_t *num_valid, uint8_t *codes, float *scales,
+                               hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    k_quant_rows<true><<<rows, 256, 0, s>>>(h, amax, num_valid, cols, codes, scales);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_fill(float *__restrict__ p, size_t n, float v) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t n4 = n / 4;
+    float4 *p4 = reinterpret_cast<float4 *>(p);
+    for (; i < n4; i += stride) p4[i] = make_float4(v, v, v, v);
+    for (size_t j = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; j < n; j += stride) p[j] = v;
+}
+
+hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n / 4 + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks == 0) blocks = 1;
+    k_fill<<<(unsigned)blocks, 256, 0, s>>>(p, n, v);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_finalize(const float *__restrict__ acc,
+                                                  uint16_t *__restrict__ out, size_t n) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    const size_t n4 = n / 4;
+    const float4 *a4 = reinterpret_cast<const float4 *>(acc);
+    uint2 *o4 = reinterpret_cast<uint2 *>(out);
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        const float4 v = a4[i];
+        o4[i] = make_uint2(f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
+                           f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
+    }
+    for (size_t j = n4 * 4 + (size_t)blockIdx.x * 256 + threadIdx.x; j < n; j += stride)
+        out[j] = f32_to_bf16_bits(acc[j]);
+}
+
+hipError_t launch_finalize(const float *acc, uint16_t *out, size_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n / 4 + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks == 0) blocks = 1;
+    k_finalize<<<(unsigned)blocks, 256, 0, s>>>(acc, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

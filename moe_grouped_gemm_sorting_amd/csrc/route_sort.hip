@@ -1,0 +1,238 @@
+// route_sort.hip -- top-k routing and the stable block-padded token sort.
+//
+// Routing is the gating stage of the fused MoE pipeline and the sort is its
+// token re-sort stage (AITER walk-through, itsolotime.com/th/archives/32381,
+// section 3 and section 3.1). The sort is an exact counting sort; every rank
+// comes from ordered wave ballots and per-wave prefix counts, never from the
+// order in which atomics land, so the result is bit-exact and repeatable.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- routing
+// One wave per token; lane l holds the logits of experts l, l + 64, ...
+// k rounds of a (logit descending, expert ascending) wave argmax pick the
+// experts; lane j keeps selection j.
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E,
+                                              int k, int score, int renorm,
+                                              int32_t *__restrict__ ids,
+                                              float *__restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float *row = logits + (size_t)t * E;
+    float v[PER_LANE];
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? row[e] : -INFINITY;
+    }
+    uint32_t taken = 0;
+    float my_val = 0.0f;
+    int my_id = 0;
+    float top = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == j) {
+            my_val = bv;
+            my_id = bi;
+        }
+        if (j == 0) top = bv;
+    }
+    float p;
+    if (score == 0) {
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i)
+            if (lane + 64 * i < E) part += expf(v[i] - top);
+        const float den = wave_sum(part);
+        p = expf(my_val - top) / den;
+    } else {
+        p = 1.0f / (1.0f + expf(-my_val));
+    }
+    // sum of the selected scores in selection order, as one sequential chain
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) sum += __shfl(p, j, 64);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = my_id;
+        w[(size_t)t * k + lane] = renorm ? p / sum : p;
+    }
+}
+
+hipError_t launch_topk(const float *logits, int T, int E, int k, int score, int renorm,
+                       int32_t *ids, float *w, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid((T + 3) / 4), block(256);
+    if (E <= 64)
+        k_topk<1><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+    else if (E <= 128)
+        k_topk<2><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+    else if (E <= 256)
+        k_topk<4><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+    else if (E <= 512)
+        k_topk<8><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+    else
+        k_topk<16><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------- sort
+// One workgroup of SORT_WAVES waves. The N = T*k assignments are cut into
+// SORT_WAVES contiguous segments, one per wave, so that "earlier wave" means
+// "smaller assignment index".
+//   1. count: cnt[w][e] = assignments of expert e in wave w's segment
+//      (LDS atomics; counts are order-free);
+//   2. scan: cnt[w][e] becomes the exclusive prefix over waves, the padded
+//      expert sizes are scanned into off[];
+//   3. scatter: each wave walks its segment 64 assignments at a time; the
+//      rank of an assignment among equal experts in the chunk comes from a
+//      peer mask built from log2(E) bit-plane ballots;
+//   4. padding slots, the tail and the per-block expert ids are filled.
+constexpr int SORT_WAVES = 8;
+constexpr int SORT_THREADS = SORT_WAVES * 64;
+
+__global__ __launch_bounds__(SORT_THREADS) void k_sort(
+    const int32_t *__restrict__ ids, const float *__restrict__ wts, int N, int E, int B, int P,
+    int NB, int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w,
+    int32_t *__restrict__ seid, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ num_valid) {
+    extern __shared__ int lds[];
+    int *cnt = lds;                     // [SORT_WAVES][E]
+    int *tot = cnt + SORT_WAVES * E;    // [E]
+    int *off = tot + E;                 // [E + 1]
+    __shared__ int wave_sum_lds[SORT_WAVES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < SORT_WAVES * E; i += SORT_THREADS) cnt[i] = 0;
+    __syncthreads();
+
+    const int seg = (((N + SORT_WAVES - 1) / SORT_WAVES) + 63) / 64 * 64;
+    const int beg = min(N, wave * seg), end = min(N, beg + seg);
+    for (int a = beg + lane; a < end; a += 64) {
+        const int e = ids[a];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave * E + e], 1);
+    }
+    __syncthreads();
+
+    int carry = 0;
+    for (int base = 0; base < E; base += SORT_THREADS) {
+        const int e = base + tid;
+        int pad = 0;
+        if (e < E) {
+            int t = 0;
+            for (int w = 0; w < SORT_WAVES; ++w) {
+                const int c = cnt[w * E + e];
+                cnt[w * E + e] = t;
+                t += c;
+            }
+            tot[e] = t;
+            counts[e] = t;
+            pad = (t + B - 1) / B * B;
+        }
+        int incl = pad;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int up = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += up;
+        }
+        if (lane == 63) wave_sum_lds[wave] = incl;
+        __syncthreads();
+        int before = 0, all = 0;
+        for (int w = 0; w < SORT_WAVES; ++w) {
+            const int ws = wave_sum_lds[w];
+            before += (w < wave) ? ws : 0;
+            all += ws;
+        }
+        if (e < E) off[e] = carry + before + incl - pad;
+        carry += all;
+        __syncthreads();
+    }
+    if (tid == 0) off[E] = carry;
+    __syncthreads();
+    const int nv = off[E];
+    for (int e = tid; e <= E; e += SORT_THREADS) offsets[e] = off[e];
+    if (tid == 0) *num_valid = nv;
+
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const uint64_t lt = lanemask_lt();
+    for (int a0 = beg; a0 < end; a0 += 64) {
+        const int a = a0 + lane;
+        int e = a < end ? ids[a] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        int basecnt = 0, rank = 0;
+        if (valid) {
+            rank = __popcll(peers & lt);
+            basecnt = cnt[wave * E + e];
+            const int pos = off[e] + basecnt + rank;
+            sorted_ids[pos] = a;
+            sorted_w[pos] = wts[a];
+        }
+        if (valid && rank == 0) cnt[wave * E + e] = basecnt + __popcll(peers);
+    }
+
+    for (int e = tid; e < E; e += SORT_THREADS)
+        for (int i = off[e] + tot[e]; i < off[e + 1]; ++i) {
+            sorted_ids[i] = N;
+            sorted_w[i] = 0.0f;
+        }
+    for (int i = nv + tid; i < P; i += SORT_THREADS) {
+        sorted_ids[i] = N;
+        sorted_w[i] = 0.0f;
+    }
+    for (int b = tid; b < NB; b += SORT_THREADS) {
+        const long slot = (long)b * B;
+        int owner = -1;
+        if (slot < nv) {
+            int lo = 0, hi = E - 1;  // last e with off[e] <= slot
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= slot) lo = mid; else hi = mid - 1;
+            }
+            owner = lo;
+        }
+        seid[b] = owner;
+    }
+}
+
+hipError_t launch_sort(const int32_t *ids, const float *w, int T, int k, int E, int B,
+                       int32_t *sorted_ids, float *sorted_w, int32_t *sorted_expert_ids,
+                       int32_t *counts, int32_t *offsets, int32_t *num_valid, hipStream_t s) {
+    const int N = T * k;
+    const int P = N + E * B - k;
+    const int NB = (P + B - 1) / B;
+    const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + E + E + 1);
+    k_sort<<<1, SORT_THREADS, lds, s>>>(ids, w, N, E, B, P, NB, sorted_ids, sorted_w,
+                                        sorted_expert_ids, counts, offsets, num_valid);
+    return hipGetLastError();
+}
+
+}  // namespace moe

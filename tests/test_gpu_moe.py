@@ -1,0 +1,112 @@
+"""GPU parity of the grouped GEMMs and the fused layer against the CPU oracle.
+
+Small shapes compare every output; the five full-size workloads run exactly
+as the benchmark launches them and compare sampled token rows (the oracle
+computes any row on its own). Bar: relative error floored at the output RMS
+<= 2e-2 (bf16) or 6e-2 (fp8)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_sorting_amd as moe
+import workloads
+from gpu_helpers import DEV, TOL, bits, bf16_to_f64, log, oracle_layer, rel_err
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    workloads.get("tiny"),
+    workloads.Workload("ragged_bf16", T=37, d=256, f=384, E=5, k=2, seed=21),
+    workloads.Workload("wide_bf16", T=200, d=512, f=256, E=8, k=2, seed=22),
+    workloads.Workload("skew_sigmoid", T=64, d=384, f=256, E=16, k=4, score="sigmoid",
+                       logits="zipf", seed=23),
+    workloads.Workload("tok_fp8", T=45, d=256, f=512, E=4, k=2, quant="fp8_token", seed=24),
+    workloads.Workload("blk_fp8", T=33, d=384, f=256, E=12, k=3, quant="fp8_block",
+                       score="sigmoid", logits="zipf", seed=25),
+    workloads.Workload("one_expert", T=20, d=128, f=128, E=1, k=1, seed=26),
+    workloads.Workload("single_token", T=1, d=256, f=256, E=8, k=2, seed=27),
+]
+
+
+def _run_two_stage(wl, x, ids, w, ws, B, ksplit):
+    s = moe.moe_sort(ids, w, wl.E, B)
+    h, hs = moe.moe_gemm1_swiglu(x, ws["w13"], s, wl.k, B, wl.quant, ws["w13_scale"])
+    return moe.moe_gemm2_combine(h, hs, ws["w2"], s, wl.T, wl.k, B, wl.quant, ws["w2_scale"],
+                                 ksplit=ksplit)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_two_stage_small_all_outputs(wl):
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    ref, rid, rw = oracle_layer(wl, x, logits, ws)
+    ids = torch.from_numpy(rid).to(DEV)
+    w = torch.from_numpy(rw).to(DEV)
+    for B in (16, 32):
+        for ksplit in (1, 3):
+            log(f"two-stage {wl.name} B={B} ksplit={ksplit}")
+            out = _run_two_stage(wl, x, ids, w, ws, B, ksplit)
+            torch.cuda.synchronize()
+            err, norm = rel_err(bf16_to_f64(bits(out)), ref)
+            log(f"  err={err:.3e} norm={norm:.3e}")
+            assert err <= TOL[wl.quant], (wl.name, B, ksplit, err)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_fused_small_all_outputs(wl):
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    ref, _, _ = oracle_layer(wl, x, logits, ws)
+    out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, quant=wl.quant,
+                        w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"], score=wl.score)
+    torch.cuda.synchronize()
+    err, norm = rel_err(bf16_to_f64(bits(out)), ref)
+    log(f"fused {wl.name}: err={err:.3e} norm={norm:.3e}")
+    assert err <= TOL[wl.quant]
+
+
+def test_fused_with_given_routing_and_idle_experts():
+    """Precomputed routing (logits = NULL) that leaves experts idle and piles
+    every token on two experts, so some experts get many blocks."""
+    wl = workloads.Workload("piled", T=150, d=256, f=256, E=8, k=2, seed=28)
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    rid = np.tile(np.array([[6, 1]], np.int32), (wl.T, 1))
+    rid[::7] = [[1, 3]]
+    rw = np.random.default_rng(0).dirichlet([1, 1], wl.T).astype(np.float32)
+    ref, _, _ = oracle_layer(wl, x, logits, ws, ids=rid, w=rw)
+    for B in (16, 32):
+        out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, topk_ids=torch.from_numpy(rid).to(DEV),
+                            topk_w=torch.from_numpy(rw).to(DEV), B=B, stage=2)
+        torch.cuda.synchronize()
+        err, _ = rel_err(bf16_to_f64(bits(out)), ref)
+        assert err <= TOL["bf16"], (B, err)
+
+
+FULL_SAMPLES = {"tiny": None, "mixtral_decode": None, "mixtral_prefill": 24, "mixtral_fp8": 24,
+                "deepseek_fp8": 6}
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_fused_full_size_sampled(name):
+    wl = workloads.get(name)
+    log(f"full-size parity: {name} (generating inputs)")
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, quant=wl.quant,
+                        w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"], score=wl.score)
+    torch.cuda.synchronize()
+    n = FULL_SAMPLES[name]
+    if n is None:
+        tokens = np.arange(wl.T)
+    else:
+        rng = np.random.default_rng(7)
+        tokens = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, n, replace=False)]))
+    log(f"  oracle on {tokens.size} tokens")
+    ref, _, _ = oracle_layer(wl, x, logits, ws, tokens=tokens)
+    got = bf16_to_f64(bits(out))[tokens]
+    err, norm = rel_err(got, ref)
+    log(f"  err={err:.3e} norm={norm:.3e}")
+    assert err <= TOL[wl.quant]
+    # tokens outside the sample still got finite values
+    assert torch.isfinite(out.float()).all()

@@ -1,0 +1,126 @@
+"""GPU parity of routing, sorting and activation quantisation: bit-exact
+against the CPU oracle (weights of the routing within 2e-6 relative)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_sorting_amd as moe
+import oracle
+import workloads
+from gpu_helpers import DEV, bits, log
+
+pytestmark = pytest.mark.gpu
+
+SORT_KEYS = ["sorted_ids", "sorted_w", "sorted_expert_ids", "expert_counts", "expert_offsets",
+             "num_valid"]
+
+
+def _gpu_sort(ids_np, w_np, E, B):
+    ids = torch.from_numpy(ids_np).to(DEV)
+    w = torch.from_numpy(w_np).to(DEV)
+    s = moe.moe_sort(ids, w, E, B)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in s.items()}
+
+
+def _assert_sort_equal(ids, w, E, B):
+    ref = oracle.sort(ids, w, E, B)
+    got = _gpu_sort(ids, w, E, B)
+    for key in SORT_KEYS:
+        assert np.array_equal(got[key], ref[key]), f"{key} differs (E={E} B={B} T={ids.shape[0]})"
+    again = _gpu_sort(ids, w, E, B)
+    for key in SORT_KEYS:
+        assert np.array_equal(again[key], got[key]), f"{key} not repeatable"
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_topk_and_sort_on_workload_routings(name):
+    wl = workloads.get(name)
+    log(f"routing+sort parity: {name}")
+    _, logits = wl.activations(DEV)
+    ids, w = moe.moe_topk(logits, wl.k, wl.score)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(logits.cpu().numpy(), wl.k, wl.score)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=0)
+    for B in (16, 32, 64, 128):
+        _assert_sort_equal(rid, rw, wl.E, B)
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (3, 2, 2), (100, 64, 6), (77, 65, 3), (9, 300, 16),
+                                   (1000, 1024, 8), (513, 129, 4), (5, 16, 16)])
+def test_topk_fuzz(score, T, E, k):
+    g = torch.Generator(device=DEV).manual_seed(T * 7 + E)
+    logits = torch.randn(T, E, generator=g, device=DEV) * 3
+    # plant exact ties: duplicate a column
+    if E >= 4:
+        logits[:, 3] = logits[:, 1]
+    ids, w = moe.moe_topk(logits, k, score)
+    torch.cuda.synchronize()
+    rid, rw = oracle.route(logits.cpu().numpy(), k, score)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=0)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_sort_fuzz(seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.choice([1, 2, 3, 8, 33, 64, 65, 256, 1000]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.choice([0, 1, 5, 64, 1000, 4096, 9000]))
+    B = int(rng.choice([1, 16, 32, 64, 128]))
+    log(f"sort fuzz seed={seed} T={T} E={E} k={k} B={B}")
+    p = 1.0 / np.arange(1, E + 1) ** (1.2 if seed % 2 else 0.0)
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]) \
+        if T else np.zeros((0, k), np.int64)
+    ids = ids.astype(np.int32).reshape(T, k)
+    w = rng.random((T, k)).astype(np.float32)
+    _assert_sort_equal(ids, w, E, B)
+
+
+def test_sort_edge_cases():
+    # everything on one expert, experts without tokens, E = 1, k = E
+    ids = np.tile(np.array([[5, 2]], np.int32), (300, 1))
+    _assert_sort_equal(ids, np.ones((300, 2), np.float32), 8, 16)
+    _assert_sort_equal(np.zeros((7, 1), np.int32), np.ones((7, 1), np.float32), 1, 32)
+    ids = np.tile(np.arange(4, dtype=np.int32)[::-1], (10, 1)).copy()
+    _assert_sort_equal(ids, np.random.default_rng(0).random((10, 4)).astype(np.float32), 4, 1)
+    # the largest tested sort: T*k = 65536 assignments over 1024 experts
+    rng = np.random.default_rng(1)
+    ids = np.stack([rng.choice(1024, 8, replace=False) for _ in range(8192)]).astype(np.int32)
+    _assert_sort_equal(ids, rng.random((8192, 8)).astype(np.float32), 1024, 128)
+
+
+@pytest.mark.parametrize("rows,cols,group", [(1, 128, 128), (3, 256, 256), (17, 4096, 4096),
+                                             (128, 7168, 128), (5, 384, 128), (64, 2048, 2048)])
+def test_quant_act_bit_exact(rows, cols, group):
+    g = torch.Generator(device=DEV).manual_seed(rows * cols)
+    x = (torch.randn(rows, cols, generator=g, device=DEV) * 4).to(torch.bfloat16)
+    x[0, :5] = 0
+    if rows > 2:
+        x[2] = 0  # an all-zero row takes scale 1
+    codes, scales = moe.moe_quant_act(x, group)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant_rows(bits(x), group)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_e4m3_rounding_of_every_bf16_value():
+    """Every bf16 value with |v| <= 448 through the GPU quantiser with scale 1
+    (a row whose amax is 448): the codes equal the oracle's e4m3 encoding,
+    including the round-half-even ties that bf16 values can hit exactly."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_bits_to_f32(allbits)
+    keep = np.isfinite(vals) & (np.abs(vals) <= 448.0)
+    v = vals[keep]
+    n = -(-(v.size + 1) // 128) * 128
+    row = np.zeros(n, np.float32)
+    row[:v.size] = v
+    row[v.size] = 448.0
+    x = torch.from_numpy(row).to(torch.bfloat16).view(1, n).to(DEV)
+    codes, scales = moe.moe_quant_act(x, n)
+    torch.cuda.synchronize()
+    assert float(scales[0, 0]) == 1.0
+    assert np.array_equal(codes.cpu().numpy()[0, :v.size], oracle.e4m3_encode(v))

@@ -1,0 +1,108 @@
+"""Host-side checks of libmoe that need no GPU: the library loads, exports
+every entry point include/moe.h declares, and validates arguments on the host
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_grouped_gemm_sorting_amd as moe
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.library_path()):
+        pytest.skip("libmoe.so not built")
+    return moe.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ["moe_topk", "moe_sort", "moe_gemm1_swiglu", "moe_gemm2_combine", "fused_moe",
+                     "moe_quant_act", "moe_sort_max_padded", "moe_sort_max_blocks",
+                     "moe_last_error", "moe_status_string"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_sizes_follow_the_padding_formula(lib):
+    for T, k, E, B in [(16, 2, 4, 32), (32, 2, 8, 32), (4096, 2, 8, 128), (128, 8, 256, 16),
+                       (0, 1, 1, 16), (1, 1, 1, 1)]:
+        assert moe.moe_sort_max_padded(T, k, E, B) == oracle.max_padded(T, k, E, B)
+        assert moe.moe_sort_max_blocks(T, k, E, B) == oracle.max_blocks(T, k, E, B)
+    assert lib.moe_sort_max_padded(-1, 1, 1, 1) == -1
+    assert lib.moe_sort_max_padded(1, 3, 2, 1) == -1   # k > E
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+def test_validation_before_any_device_call(lib):
+    S = None
+    # routing: k > E, bad score, null pointers
+    assert lib.moe_topk(None, 4, 4, 5, 0, 1, None, None, S) == 1
+    assert lib.moe_topk(None, 4, 4, 2, 7, 1, None, None, S) == 1
+    assert lib.moe_topk(None, 4, 4, 2, 0, 1, None, None, S) == 1 and "null" in _err(lib)
+    assert lib.moe_topk(None, 4, 2000, 2, 0, 1, None, None, S) == 1
+    # sort: bad B, null pointers
+    assert lib.moe_sort(None, None, 4, 2, 4, 0, None, None, None, None, None, None, S) == 1
+    assert lib.moe_sort(None, None, 4, 2, 4, 16, None, None, None, None, None, None, S) == 1
+    # quant: unsupported group
+    assert lib.moe_quant_act(None, 2, 256, 64, None, None, S) == 2
+    assert lib.moe_quant_act(None, 2, 200, 200, None, None, S) == 2
+    # gemm1: d not a multiple of 128, bad B, bad quant, null pointers, small workspace
+    args = [None] * 8 + [None, 0, S]
+    assert lib.moe_gemm1_swiglu(4, 100, 256, 4, 2, 16, 0, *args) == 2
+    assert lib.moe_gemm1_swiglu(4, 128, 256, 4, 2, 48, 0, *args) == 1
+    assert lib.moe_gemm1_swiglu(4, 128, 256, 4, 2, 16, 5, *args) == 1
+    assert lib.moe_gemm1_swiglu(4, 128, 256, 4, 2, 16, 0, *args) == 1
+    fake = ctypes.c_void_p(16)
+    assert lib.moe_gemm1_swiglu(4, 128, 256, 4, 2, 16, 1, fake, fake, None, fake, fake, fake, fake,
+                                fake, None, 0, S) == 1          # fp8 without scales
+    n = lib.moe_gemm1_workspace_bytes(4, 128, 256, 4, 2, 16, 1)
+    assert n > 0
+    assert lib.moe_gemm1_swiglu(4, 128, 256, 4, 2, 16, 1, fake, fake, fake, fake, fake, fake, fake,
+                                fake, fake, n - 1, S) == 3
+    # gemm2 / fused
+    assert lib.moe_gemm2_combine(4, 128, 256, 4, 2, 16, 0, 0, *([None] * 9), None, 0, S) == 1
+    assert lib.fused_moe(4, 128, 256, 4, 2, 0, 0, 1, *([None] * 8), 16, 2, 0, None, None, 0, S) == 1
+    n = lib.fused_moe_workspace_bytes(4, 128, 256, 4, 2, 0, 16, 2)
+    assert lib.fused_moe(4, 128, 256, 4, 2, 0, 0, 1, fake, None, None, fake, fake, None, fake, None,
+                         16, 2, 0, fake, fake, n - 1, S) == 3
+    assert lib.fused_moe_workspace_bytes(4, 128, 256, 4, 2, 0, 16, 3) == 0
+    assert lib.moe_status_string(3) == b"workspace too small"
+
+
+def test_workspace_queries_grow_with_the_problem(lib):
+    a = lib.fused_moe_workspace_bytes(32, 4096, 14336, 8, 2, 0, 32, 2)
+    b = lib.fused_moe_workspace_bytes(4096, 4096, 14336, 8, 2, 0, 32, 2)
+    assert 0 < a < b
+    assert lib.moe_gemm2_workspace_bytes(32, 4096, 14336, 8, 2, 32, 0) >= 32 * 4096 * 4
+    assert lib.moe_gemm1_workspace_bytes(32, 4096, 14336, 8, 2, 32, 0) == 0
+
+
+def test_select_config_is_host_only_and_valid(lib):
+    for shape in [(16, 128, 256, 4, 2, "bf16"), (32, 4096, 14336, 8, 2, "bf16"),
+                  (4096, 4096, 14336, 8, 2, "bf16"), (512, 4096, 14336, 8, 2, "fp8_token"),
+                  (128, 7168, 2048, 256, 8, "fp8_block"), (1, 4096, 14336, 8, 2, "bf16")]:
+        B, stage, ks = moe.moe_select_config(*shape, cu_count=256)
+        assert B in (16, 32, 64, 128) and stage in (1, 2) and ks >= 1
+    with pytest.raises(moe.MoeError):
+        moe.moe_select_config(4, 100, 256, 4, 2, "bf16", cu_count=256)
