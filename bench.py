@@ -1,0 +1,244 @@
+"""Benchmark of the fused MoE layer on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of fused_moe (routing, sort, activation quantisation for
+fp8, grouped GEMM1 + SwiGLU, grouped GEMM2 + weighted combine) over one batch
+of synthetic, seeded inputs already resident in HBM. The default workload is
+the Mixtral-8x7B-shaped decode layer (T=32, d=4096, f=14336, E=8, top-2,
+bf16). One JSON line goes to stdout. Besides the standard fields it reports:
+
+  roofline      the dominant kernel (GEMM1 + SwiGLU) against its roofline:
+                algorithmic bytes (or FLOPs) per launch over its mean duration,
+                timed with HIP events on the stream it runs on;
+  layer         the whole layer against the HBM and MFMA rooflines;
+  stages        mean per-stage times of the same path;
+  cpu_baseline  the CPU oracle on the host cores, on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_token": 5000.0, "fp8_block": 5000.0}
+METRIC = "fused-MoE tokens/s + % HBM BW (decode) / % MFMA peak (prefill), Mixtral"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["moe_grouped_gemm_sorting_amd/csrc/gemm_stream.hip",
+                  "moe_grouped_gemm_sorting_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_decode")
+    ap.add_argument("--B", type=int, default=0)
+    ap.add_argument("--stage", type=int, default=0)
+    ap.add_argument("--ksplit", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="tokens the CPU oracle runs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this layer is built and measured on a single MI355X "
+              "(no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_grouped_gemm_sorting_amd as moe
+    import workloads
+
+    wl = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {wl.name}: T={wl.T} d={wl.d} f={wl.f} E={wl.E} k={wl.k} quant={wl.quant} "
+        f"on {torch.cuda.get_device_name(0)}")
+    x, logits = wl.activations(dev)
+    ws = wl.weights(dev)
+    torch.cuda.synchronize()
+
+    B, stage, ksplit = moe.moe_select_config(wl.T, wl.d, wl.f, wl.E, wl.k, wl.quant)
+    B = args.B or B
+    stage = args.stage or stage
+    ksplit = args.ksplit or ksplit
+    nbytes = moe.fused_moe_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, wl.quant, B, stage)
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty(wl.T, wl.d, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, quant=wl.quant,
+                      w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"], score=wl.score,
+                      B=B, stage=stage, ksplit=ksplit, out=out, workspace=workspace)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- timed region: K whole-layer steps --------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    tokens_per_s = wl.T / (ms / 1e3)
+    log(f"[bench] fused_moe: {ms * 1e3:.1f} us/step, {tokens_per_s:,.0f} tokens/s")
+
+    # ---- per-stage timing with HIP events on the library's stream ---------------
+    stream = torch.cuda.current_stream()
+    ids, w = moe.moe_topk(logits, wl.k, wl.score)
+    srt = moe.moe_sort(ids, w, wl.E, B)
+    h, hs = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, B, wl.quant, ws["w13_scale"])
+    g2ws = torch.empty(moe.moe_gemm2_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, B, wl.quant),
+                       dtype=torch.uint8, device=dev)
+    g1ws = torch.empty(max(1, moe.moe_gemm1_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, B,
+                                                            wl.quant)), dtype=torch.uint8,
+                       device=dev)
+    stage_fns = {
+        "topk": lambda: moe.moe_topk(logits, wl.k, wl.score),
+        "sort": lambda: moe.moe_sort(ids, w, wl.E, B),
+        "gemm1_swiglu": lambda: moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, B, wl.quant,
+                                                     ws["w13_scale"], workspace=g1ws),
+        "gemm2_combine": lambda: moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B,
+                                                       wl.quant, ws["w2_scale"], ksplit=ksplit,
+                                                       out=out, workspace=g2ws),
+    }
+    stages = {}
+    for name, fn in stage_fns.items():
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        stages[name] = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3  # us
+    log("[bench] stages (us): " + ", ".join(f"{k}={v:.1f}" for k, v in stages.items()))
+
+    # ---- algorithmic work ----------------------------------------------------
+    counts = srt["expert_counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+    eb = 2 if wl.quant == "bf16" else 1
+    w13_bytes = touched * 2 * wl.f * wl.d * eb
+    if wl.quant == "fp8_token":
+        w13_bytes += touched * 2 * wl.f * 4
+    elif wl.quant == "fp8_block":
+        w13_bytes += touched * (2 * wl.f // 128) * (wl.d // 128) * 4
+    g1_bytes = w13_bytes + wl.T * wl.d * 2
+    g1_flops = 4 * wl.d * wl.f * wl.T * wl.k
+    layer_bytes = touched * wl.weight_bytes_per_expert() + wl.T * wl.d * 2 * 2 + wl.T * wl.E * 4
+    layer_flops = wl.flops()
+    g1_us = stages["gemm1_swiglu"]
+    hbm_bound = (layer_bytes / HBM_PEAK_GBS) > (layer_flops / (MFMA_PEAK_TFLOPS[wl.quant] * 1e3))
+    if hbm_bound:
+        achieved = g1_bytes / (g1_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = g1_flops / (g1_us * 1e-6) / 1e12
+        peak = MFMA_PEAK_TFLOPS[wl.quant]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    roof["kernel"] = "GEMM1 + SwiGLU (moe_gemm1_swiglu)"
+    roof["kernel_us"] = round(g1_us, 2)
+    roof["algorithmic_per_launch"] = {"bytes": g1_bytes, "flops": g1_flops,
+                                      "touched_experts": touched}
+    roof["traffic"] = None
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(wl.name)
+        if rec and rec.get("source_hash") == kernel_source_hash():
+            roof["traffic"] = rec["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    layer = {
+        "bytes": layer_bytes, "flops": layer_flops,
+        "hbm_GBs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "TFLOPs": round(layer_flops / (ms * 1e-3) / 1e12, 2),
+        "mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[wl.quant], 4),
+    }
+
+    # ---- CPU oracle on the host cores (bounded sample) -----------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+        n = min(args.cpu_sample, wl.T)
+        tokens = np.arange(n, dtype=np.int32)
+        rid, rw = oracle.route(logits.cpu().numpy(), wl.k, wl.score)
+        need = sorted(set(rid[tokens].ravel().tolist()))
+        b16 = lambda t: t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)  # noqa
+        w13 = [None] * wl.E
+        w2 = [None] * wl.E
+        s13 = [None] * wl.E if wl.quant != "bf16" else None
+        s2 = [None] * wl.E if wl.quant != "bf16" else None
+        for e in need:
+            if wl.quant == "bf16":
+                w13[e], w2[e] = b16(ws["w13"][e]), b16(ws["w2"][e])
+            else:
+                w13[e], w2[e] = ws["w13"][e].cpu().numpy(), ws["w2"][e].cpu().numpy()
+                s13[e], s2[e] = ws["w13_scale"][e].cpu().numpy(), ws["w2_scale"][e].cpu().numpy()
+        xb = b16(x)
+        t0 = time.perf_counter()
+        oracle.moe(xb, rid, rw, w13, w2, s13, s2, quant=wl.quant, tokens=tokens, threads=threads)
+        sec = time.perf_counter() - t0
+        cpu = {"value": round(n / sec, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n} of {wl.T} tokens of {wl.name} (route + per-token fp32 expert loop), "
+                         f"{sec:.1f} s"}
+        log(f"[bench] CPU oracle: {n} tokens in {sec:.1f} s on {threads} threads")
+
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.quant == "bf16" else "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "k": wl.k,
+                   "quant": wl.quant, "score": wl.score, "B": B, "stage": stage,
+                   "ksplit": ksplit, "parallelism": "single GPU"},
+        "roofline": roof, "layer": layer, "stages_us": {k: round(v, 2) for k, v in stages.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

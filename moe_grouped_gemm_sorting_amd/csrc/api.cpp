@@ -13,6 +13,13 @@
 #include "moe.h"
 #include "launch.h"
 
+#ifndef MOE_G1_CT
+#define MOE_G1_CT 1
+#endif
+#ifndef MOE_G2_CT
+#define MOE_G2_CT 4
+#endif
+
 namespace moe {
 // implemented in gemm_stream.hip / gemm_tiled.hip / moe_1stage.hip
 bool stream_gemm1_supported(const GemmShape &sh);
@@ -100,14 +107,15 @@ struct Config {
 };
 
 int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
-    // enough workgroups for ~4 per CU in the down projection
+    // about two workgroups per CU in the down projection (measured best on
+    // the Mixtral decode shape: 4 splits of K = 14336)
     const int64_t rows = (int64_t)T * k;
     const int64_t blocks = std::min<int64_t>(max_blocks(T, k, E, B), std::min<int64_t>(E, rows) + rows / B);
     const int CT = (d % 256 == 0) ? 4 : 2;
     const int64_t ntiles = d / (64 * CT);
     const int64_t base = std::max<int64_t>(1, ntiles * blocks);
     const int KS = quant == 0 ? 64 : 128;
-    int ks = (int)std::min<int64_t>((4 * (int64_t)cu + base - 1) / base, f / KS / 4);
+    int ks = (int)std::min<int64_t>((2 * (int64_t)cu + base - 1) / base, f / KS / 4);
     return std::max(1, ks);
 }
 
@@ -143,8 +151,11 @@ Gemm1Ws carve_gemm1(Carver &c, int T, int d, int f, int E, int k, int B, int qua
 
 int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x, const void *w13,
               const float *w13_scale, const int32_t *sorted_ids, const int32_t *seid,
-              const int32_t *num_valid, void *h, float *h_scale, const Gemm1Ws &w, hipStream_t s) {
+              const int32_t *num_valid, void *h, float *h_scale, const Gemm1Ws &w, hipStream_t s,
+              float *zero = nullptr, size_t zero_n = 0) {
     Gemm1Args g{};
+    g.zero = zero;
+    g.zero_n = zero_n;
     g.sh = GemmShape{T, d, f, E, k, B, quant};
     g.w13 = w13;
     g.w13_scale = w13_scale;
@@ -172,7 +183,7 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     }
     if (!stream_gemm1_supported(g.sh))
         return fail(MOE_ERR_UNSUPPORTED, "no GEMM1 kernel for B=%d", B);
-    HIP_TRY(launch_stream_gemm1(g, 2, s), "GEMM1 launch");
+    HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
     if (quant == 1)
         HIP_TRY(launch_quant_h_rows(w.hb, w.amax, (int)P, f, num_valid, static_cast<uint8_t *>(h),
                                     h_scale, s),
@@ -185,7 +196,8 @@ float *carve_gemm2(Carver &c, int T, int d) { return c.take<float>((size_t)T * d
 int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, const void *h,
               const float *h_scale, const void *w2, const float *w2_scale,
               const int32_t *sorted_ids, const float *sorted_w, const int32_t *seid,
-              const int32_t *num_valid, void *out, float *acc, hipStream_t s) {
+              const int32_t *num_valid, void *out, float *acc, hipStream_t s,
+              bool acc_zeroed = false) {
     Gemm2Args g{};
     g.sh = GemmShape{T, d, f, E, k, B, quant};
     g.h = h;
@@ -201,8 +213,8 @@ int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, c
     g.ksplit = ksplit;
     if (!stream_gemm2_supported(g.sh))
         return fail(MOE_ERR_UNSUPPORTED, "no GEMM2 kernel for B=%d", B);
-    HIP_TRY(launch_fill_f32(acc, (size_t)T * d, 0.0f, s), "fill launch");
-    HIP_TRY(launch_stream_gemm2(g, 4, ksplit, s), "GEMM2 launch");
+    if (!acc_zeroed) HIP_TRY(launch_fill_f32(acc, (size_t)T * d, 0.0f, s), "fill launch");
+    HIP_TRY(launch_stream_gemm2(g, MOE_G2_CT, ksplit, s), "GEMM2 launch");
     HIP_TRY(launch_finalize(acc, static_cast<uint16_t *>(out), (size_t)T * d, s), "finalize launch");
     return MOE_OK;
 }
@@ -424,21 +436,22 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     hipStream_t s = (hipStream_t)stream;
     Carver cw(ws);
     FusedWs w = carve_fused(cw, T, d, f, E, k, quant, B, true);
-    const int32_t *ids = topk_ids;
-    const float *wt = topk_w;
     if (logits) {
-        HIP_TRY(launch_topk(logits, T, E, k, score, renorm, w.topk_ids, w.topk_w, s), "topk launch");
-        ids = w.topk_ids;
-        wt = w.topk_w;
+        HIP_TRY(launch_route_sort(logits, T, k, E, B, score, renorm, w.topk_ids, w.topk_w,
+                                  w.sorted_ids, w.sorted_w, w.seid, w.counts, w.offsets,
+                                  w.num_valid, s),
+                "route+sort launch");
+    } else {
+        HIP_TRY(launch_sort(topk_ids, topk_w, T, k, E, B, w.sorted_ids, w.sorted_w, w.seid,
+                            w.counts, w.offsets, w.num_valid, s),
+                "sort launch");
     }
-    HIP_TRY(launch_sort(ids, wt, T, k, E, B, w.sorted_ids, w.sorted_w, w.seid, w.counts, w.offsets,
-                        w.num_valid, s),
-            "sort launch");
+    // GEMM1 also clears GEMM2's accumulator (same stream, so it is done first)
     rc = run_gemm1(T, d, f, E, k, B, quant, x, w13, w13_scale, w.sorted_ids, w.seid, w.num_valid,
-                   w.h, w.h_scale, w.g1, s);
+                   w.h, w.h_scale, w.g1, s, w.acc, (size_t)T * d);
     if (rc) return rc;
     return run_gemm2(T, d, f, E, k, B, quant, ksplit, w.h, w.h_scale, w2, w2_scale, w.sorted_ids,
-                     w.sorted_w, w.seid, w.num_valid, out, w.acc, s);
+                     w.sorted_w, w.seid, w.num_valid, out, w.acc, s, true);
 }
 
 }  // extern "C"

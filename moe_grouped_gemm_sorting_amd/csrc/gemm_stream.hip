@@ -38,6 +38,8 @@ struct StreamParams {
     float *out_scale;        // GEMM1 quant 1: row amax [P]; quant 2: h_scale [P, f/128]
     int T, d, f, k, B;
     int kchunk;              // K elements per blockIdx.y
+    float *zero;             // optional fp32 buffer cleared by the grid on the way
+    size_t zero_n;           // its length (a multiple of 4)
 };
 
 template <int QUANT>
@@ -50,11 +52,28 @@ struct Frag {
     u32x4 lo, hi;  // 32 contiguous bytes of one row's 128-byte K step
 };
 
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 0
+#endif
+
 __device__ __forceinline__ Frag load_frag(const uint8_t *p) {
     Frag f;
     f.lo = *reinterpret_cast<const u32x4 *>(p);
     f.hi = *reinterpret_cast<const u32x4 *>(p + 16);
     return f;
+}
+
+// Weights are read once per call: nontemporal loads keep them from evicting
+// reused data (activations, h) from the caches.
+__device__ __forceinline__ Frag load_frag_stream(const uint8_t *p) {
+#if MOE_STREAM_NT
+    Frag f;
+    f.lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    f.hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 16));
+    return f;
+#else
+    return load_frag(p);
+#endif
 }
 
 // acc += A . B over one 128-byte K step.
@@ -91,6 +110,14 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
     constexpr int KS = Elem<QUANT>::kstep;
     constexpr int NT = GEMM1 ? 2 * CT : CT;
 
+    if (p.zero) {
+        // clear the next stage's accumulator, 16 bytes per thread per pass
+        const size_t nwg = (size_t)gridDim.x * gridDim.y * gridDim.z;
+        const size_t wg = blockIdx.x + (size_t)gridDim.x * (blockIdx.y + (size_t)gridDim.y * blockIdx.z);
+        float4 *z = reinterpret_cast<float4 *>(p.zero);
+        for (size_t i = wg * 256 + threadIdx.x; i < p.zero_n / 4; i += nwg * 256)
+            z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     const int blk = blockIdx.z;
     const int e = p.seid[blk];
     if (e < 0) return;
@@ -169,7 +196,7 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
             }
         }
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) fb[buf][nt] = load_frag(wrow[nt] + (size_t)kk * ES);
+        for (int nt = 0; nt < NT; ++nt) fb[buf][nt] = load_frag_stream(wrow[nt] + (size_t)kk * ES);
     };
     auto compute = [&](int buf, int kk) {
         if constexpr (QUANT == 2) {
@@ -369,6 +396,8 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
     p.out_scale = g.h_scale;
     p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
     p.kchunk = sh.d;
+    p.zero = g.zero;
+    p.zero_n = g.zero_n;
     if (sh.quant == 2) CT = 2;  // one 128-column quant block per workgroup
     const int RT = sh.B / 16;
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;

@@ -15,6 +15,12 @@ hipError_t launch_sort(const int32_t *ids, const float *w, int T, int k, int E, 
                        int32_t *sorted_ids, float *sorted_w, int32_t *sorted_expert_ids,
                        int32_t *counts, int32_t *offsets, int32_t *num_valid, hipStream_t s);
 
+// routing + sort in one launch (ids / w are written as scratch)
+hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, int score,
+                             int renorm, int32_t *ids, float *w, int32_t *sorted_ids,
+                             float *sorted_w, int32_t *sorted_expert_ids, int32_t *counts,
+                             int32_t *offsets, int32_t *num_valid, hipStream_t s);
+
 // codes [rows, cols], scales [rows, cols / group]
 hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, uint8_t *codes,
                             float *scales, hipStream_t s);
@@ -42,6 +48,8 @@ struct Gemm1Args {
     const int32_t *sorted_ids, *sorted_expert_ids, *num_valid;
     void *h;                // quant 0/1: bf16 [P, f]; quant 2: e4m3 [P, f]
     float *h_scale;         // quant 1: row amax [P] (zeroed by the caller); quant 2: [P, f/128]
+    float *zero;            // optional: fp32 buffer [zero_n] the kernel clears on the way
+    size_t zero_n;
 };
 
 struct Gemm2Args {

@@ -17,13 +17,10 @@ namespace moe {
 // k rounds of a (logit descending, expert ascending) wave argmax pick the
 // experts; lane j keeps selection j.
 template <int PER_LANE>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E,
-                                              int k, int score, int renorm,
-                                              int32_t *__restrict__ ids,
-                                              float *__restrict__ w) {
+__device__ __forceinline__ void topk_wave(const float *__restrict__ logits, int t, int E, int k,
+                                          int score, int renorm, int32_t *__restrict__ ids,
+                                          float *__restrict__ w) {
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
     const float *row = logits + (size_t)t * E;
     float v[PER_LANE];
 #pragma unroll
@@ -82,6 +79,55 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     }
 }
 
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E,
+                                              int k, int score, int renorm,
+                                              int32_t *__restrict__ ids,
+                                              float *__restrict__ w) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    topk_wave<PER_LANE>(logits, t, E, k, score, renorm, ids, w);
+}
+
+// One thread per token, for E <= 64: the same selection and scores, with
+// every sum taken in ascending expert / selection order.
+__device__ __forceinline__ void topk_thread(const float *__restrict__ logits, int t, int E, int k,
+                                            int score, int renorm, int32_t *__restrict__ ids,
+                                            float *__restrict__ w) {
+    const float *row = logits + (size_t)t * E;
+    uint64_t taken = 0;
+    float top = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        float bv = 0.0f;
+        for (int e = 0; e < E; ++e) {
+            const float v = row[e];
+            if (!((taken >> e) & 1ull) && (best < 0 || v > bv)) {
+                best = e;
+                bv = v;
+            }
+        }
+        taken |= 1ull << best;
+        if (j == 0) top = bv;
+        ids[(size_t)t * k + j] = best;
+        w[(size_t)t * k + j] = bv;  // raw logit for now
+    }
+    float den = 1.0f;
+    if (score == 0) {
+        den = 0.0f;
+        for (int e = 0; e < E; ++e) den += expf(row[e] - top);
+    }
+    float sum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        const float l = w[(size_t)t * k + j];
+        const float p = score == 0 ? expf(l - top) / den : 1.0f / (1.0f + expf(-l));
+        w[(size_t)t * k + j] = p;
+        sum += p;
+    }
+    if (renorm)
+        for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = w[(size_t)t * k + j] / sum;
+}
+
 hipError_t launch_topk(const float *logits, int T, int E, int k, int score, int renorm,
                        int32_t *ids, float *w, hipStream_t s) {
     if (T == 0) return hipSuccess;
@@ -114,7 +160,7 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int score, int 
 constexpr int SORT_WAVES = 8;
 constexpr int SORT_THREADS = SORT_WAVES * 64;
 
-__global__ __launch_bounds__(SORT_THREADS) void k_sort(
+__device__ __forceinline__ void sort_block(
     const int32_t *__restrict__ ids, const float *__restrict__ wts, int N, int E, int B, int P,
     int NB, int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w,
     int32_t *__restrict__ seid, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -221,6 +267,55 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(
         }
         seid[b] = owner;
     }
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void k_sort(
+    const int32_t *__restrict__ ids, const float *__restrict__ wts, int N, int E, int B, int P,
+    int NB, int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w,
+    int32_t *__restrict__ seid, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ num_valid) {
+    sort_block(ids, wts, N, E, B, P, NB, sorted_ids, sorted_w, seid, counts, offsets, num_valid);
+}
+
+// Routing and sort in one launch (one workgroup): top-k of every token into
+// ids / w, a workgroup barrier (which also orders the global writes for the
+// workgroup), then the sort.
+template <int PER_LANE>
+__global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
+    const float *__restrict__ logits, int T, int k, int E, int B, int score, int renorm,
+    int32_t *__restrict__ ids, float *__restrict__ wts, int P, int NB,
+    int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w, int32_t *__restrict__ seid,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ num_valid) {
+    if (PER_LANE == 0) {
+        for (int t = threadIdx.x; t < T; t += SORT_THREADS)
+            topk_thread(logits, t, E, k, score, renorm, ids, wts);
+    } else {
+        for (int t = threadIdx.x >> 6; t < T; t += SORT_WAVES)
+            topk_wave<PER_LANE == 0 ? 1 : PER_LANE>(logits, t, E, k, score, renorm, ids, wts);
+    }
+    __syncthreads();
+    sort_block(ids, wts, T * k, E, B, P, NB, sorted_ids, sorted_w, seid, counts, offsets,
+               num_valid);
+}
+
+hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, int score,
+                             int renorm, int32_t *ids, float *w, int32_t *sorted_ids,
+                             float *sorted_w, int32_t *sorted_expert_ids, int32_t *counts,
+                             int32_t *offsets, int32_t *num_valid, hipStream_t s) {
+    const int P = T * k + E * B - k;
+    const int NB = (P + B - 1) / B;
+    const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + E + E + 1);
+#define MOE_ROUTE_SORT(PL)                                                                    \
+    k_route_sort<PL><<<1, SORT_THREADS, lds, s>>>(logits, T, k, E, B, score, renorm, ids, w, P, \
+                                                   NB, sorted_ids, sorted_w, sorted_expert_ids, \
+                                                   counts, offsets, num_valid)
+    if (E <= 64) MOE_ROUTE_SORT(0);
+    else if (E <= 128) MOE_ROUTE_SORT(2);
+    else if (E <= 256) MOE_ROUTE_SORT(4);
+    else if (E <= 512) MOE_ROUTE_SORT(8);
+    else MOE_ROUTE_SORT(16);
+#undef MOE_ROUTE_SORT
+    return hipGetLastError();
 }
 
 hipError_t launch_sort(const int32_t *ids, const float *w, int T, int k, int E, int B,
