@@ -26,6 +26,9 @@ bool stream_gemm1_supported(const GemmShape &sh);
 bool stream_gemm2_supported(const GemmShape &sh);
 hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s);
 hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream_t s);
+bool tiled_gemm_supported(const GemmShape &sh);
+hipError_t launch_tiled_gemm1(const Gemm1Args &g, hipStream_t s);
+hipError_t launch_tiled_gemm2(const Gemm2Args &g, int ksplit, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -106,22 +109,39 @@ struct Config {
     int B, stage, ksplit;
 };
 
+bool use_tiled(int B) { return B >= 64; }
+
 int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
     // about two workgroups per CU in the down projection (measured best on
     // the Mixtral decode shape: 4 splits of K = 14336)
     const int64_t rows = (int64_t)T * k;
     const int64_t blocks = std::min<int64_t>(max_blocks(T, k, E, B), std::min<int64_t>(E, rows) + rows / B);
-    const int CT = (d % 256 == 0) ? 4 : 2;
-    const int64_t ntiles = d / (64 * CT);
+    int64_t ntiles;
+    if (use_tiled(B)) {
+        ntiles = d / 256;
+    } else {
+        const int CT = (d % 256 == 0) ? 4 : 2;
+        ntiles = d / (64 * CT);
+    }
     const int64_t base = std::max<int64_t>(1, ntiles * blocks);
     const int KS = quant == 0 ? 64 : 128;
     int ks = (int)std::min<int64_t>((2 * (int64_t)cu + base - 1) / base, f / KS / 4);
     return std::max(1, ks);
 }
 
+// Block size: at least the average rows per expert, so that most experts'
+// weights are streamed once; 64/128-row blocks go to the LDS-tiled kernels.
+int choose_B(int T, int E, int k, int quant) {
+    const double rows = (double)T * k / E;
+    if (quant != 2 && rows >= 96) return 128;
+    if (quant != 2 && rows >= 48) return 64;
+    if (rows <= 4) return 16;
+    return 32;
+}
+
 Config choose(int T, int d, int f, int E, int k, int quant, int cu) {
     Config c;
-    c.B = 32;
+    c.B = choose_B(T, E, k, quant);
     c.stage = 2;
     c.ksplit = auto_ksplit(T, d, f, E, k, c.B, quant, cu);
     return c;
@@ -181,9 +201,15 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
             g.h_scale = h_scale;
         }
     }
-    if (!stream_gemm1_supported(g.sh))
-        return fail(MOE_ERR_UNSUPPORTED, "no GEMM1 kernel for B=%d", B);
-    HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
+    if (use_tiled(B)) {
+        if (!tiled_gemm_supported(g.sh))
+            return fail(MOE_ERR_UNSUPPORTED, "no tiled GEMM1 kernel for B=%d quant=%d d=%d", B, quant, d);
+        HIP_TRY(launch_tiled_gemm1(g, s), "GEMM1 launch");
+    } else {
+        if (!stream_gemm1_supported(g.sh))
+            return fail(MOE_ERR_UNSUPPORTED, "no GEMM1 kernel for B=%d", B);
+        HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
+    }
     if (quant == 1)
         HIP_TRY(launch_quant_h_rows(w.hb, w.amax, (int)P, f, num_valid, static_cast<uint8_t *>(h),
                                     h_scale, s),
@@ -211,10 +237,14 @@ int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, c
     g.acc = acc;
     if (ksplit <= 0) ksplit = auto_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
     g.ksplit = ksplit;
-    if (!stream_gemm2_supported(g.sh))
-        return fail(MOE_ERR_UNSUPPORTED, "no GEMM2 kernel for B=%d", B);
+    const bool tiled = use_tiled(B);
+    if (tiled ? !tiled_gemm_supported(g.sh) : !stream_gemm2_supported(g.sh))
+        return fail(MOE_ERR_UNSUPPORTED, "no GEMM2 kernel for B=%d quant=%d d=%d", B, quant, d);
     if (!acc_zeroed) HIP_TRY(launch_fill_f32(acc, (size_t)T * d, 0.0f, s), "fill launch");
-    HIP_TRY(launch_stream_gemm2(g, MOE_G2_CT, ksplit, s), "GEMM2 launch");
+    if (tiled)
+        HIP_TRY(launch_tiled_gemm2(g, ksplit, s), "GEMM2 launch");
+    else
+        HIP_TRY(launch_stream_gemm2(g, MOE_G2_CT, ksplit, s), "GEMM2 launch");
     HIP_TRY(launch_finalize(acc, static_cast<uint16_t *>(out), (size_t)T * d, s), "finalize launch");
     return MOE_OK;
 }

@@ -1,0 +1,374 @@
+// gemm_tiled.hip -- LDS-tiled grouped GEMMs for large sort blocks (B = 64, 128).
+//
+// The compute-bound regime of the grouped GEMMs (many rows per expert, e.g.
+// prefill): grouped GEMMs in place of masked dense GEMMs (rocketrecap.com/
+// entries/19116, talk summary at 5:58), run as the two stages of the AITER
+// walk-through (itsolotime.com/th/archives/32381, section 3.2).
+//
+// Workgroup tile: one sort block (BM = B rows of one expert) x 256 weight
+// rows (GEMM1: 128 gate rows + the 128 matching up rows, so SwiGLU fuses into
+// the epilogue; GEMM2: 256 output columns), K in steps of 128 bytes per row.
+// 4 waves in a 2 x 2 arrangement, each owning (BM/2) x 128 of the tile with
+// v_mfma_f32_32x32x16 (bf16, or e4m3 twice per 16-byte fragment).
+//
+// Operands are staged through LDS, double-buffered, one barrier per K step.
+// Each 128-byte row segment is stored as 8 chunks of 16 bytes whose position
+// is XOR-swizzled by (row >> 1) & 7, so that a fragment read (32 rows, one
+// chunk column) spreads over all banks.
+//
+// Tile order: tiles are enumerated block-group-major (GM sort blocks x all
+// column tiles), and workgroup i, which the hardware places on XCD i % 8,
+// takes logical tile (i % 8) * ceil(tiles / 8) + i / 8. Neighbouring tiles,
+// which share activation rows and weight rows, therefore run on the same XCD
+// and share its L2. The tile count comes from num_valid on the device, so
+// no XCD is left with the padding blocks.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int TILE_N = 256;     // weight rows per workgroup
+constexpr int ROWB = 128;       // bytes per row per K step
+constexpr int GROUP_M = 4;      // sort blocks per tile group
+
+struct TiledParams {
+    const uint8_t *a;
+    const float *a_scale;
+    const uint8_t *w;
+    const float *w_scale;
+    const int32_t *sorted_ids;
+    const float *sorted_w;
+    const int32_t *seid;
+    const int32_t *num_valid;
+    void *out;
+    float *out_scale;
+    int T, d, f, k, B;
+    int kchunk;
+    float *zero;
+    size_t zero_n;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+template <int QUANT>
+__device__ __forceinline__ f32x16 mma32(const u32x4 &a, const u32x4 &b, f32x16 acc) {
+    if constexpr (QUANT == 0) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    } else {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const long a0 = __builtin_bit_cast(long, u32x2{a.x, a.y});
+        const long a1 = __builtin_bit_cast(long, u32x2{a.z, a.w});
+        const long b0 = __builtin_bit_cast(long, u32x2{b.x, b.y});
+        const long b1 = __builtin_bit_cast(long, u32x2{b.z, b.w});
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a0, b0, acc, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a1, b1, acc, 0, 0, 0);
+    }
+}
+
+// BM: rows per sort block (64 or 128). QUANT 0 (bf16) or 1 (e4m3, per-row
+// activation scale and per-channel weight scale applied in the epilogue).
+template <int QUANT, bool GEMM1, int BM>
+__global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
+    constexpr int ES = QUANT == 0 ? 2 : 1;
+    constexpr int KS = ROWB / ES;               // K elements per step
+    constexpr int A_CHUNKS = BM * 8 / 256;      // 16-byte chunks per thread per step
+    constexpr int B_CHUNKS = TILE_N * 8 / 256;
+    constexpr int RT = BM / 64;                 // 32-row tiles per wave
+    constexpr int CT = 4;                       // 32-column tiles per wave
+    constexpr int BUF = (BM + TILE_N) * ROWB;   // bytes per LDS buffer
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    if (p.zero) {
+        const size_t nwg = (size_t)gridDim.x * gridDim.y;
+        const size_t wg = blockIdx.x + (size_t)gridDim.x * blockIdx.y;
+        float4 *z = reinterpret_cast<float4 *>(p.zero);
+        for (size_t i = wg * 256 + tid; i < p.zero_n / 4; i += nwg * 256)
+            z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // ---- which tile -------------------------------------------------------
+    const int ntiles = GEMM1 ? p.f / 128 : p.d / TILE_N;
+    const int nblocks = *p.num_valid / BM;
+    const int total = nblocks * ntiles;
+    const int per_xcd = (total + 7) / 8;
+    const int j = blockIdx.x >> 3;
+    if (j >= per_xcd) return;
+    const int logical = (blockIdx.x & 7) * per_xcd + j;
+    if (logical >= total) return;
+    const int group = logical / (GROUP_M * ntiles);
+    const int gm = min(GROUP_M, nblocks - group * GROUP_M);
+    const int r = logical - group * GROUP_M * ntiles;
+    const int nt = r / gm;
+    const int blk = group * GROUP_M + r % gm;
+    const int e = p.seid[blk];
+    if (e < 0) return;
+
+    const int sentinel = p.T * p.k;
+    const int K = GEMM1 ? p.d : p.f;
+    const int Ntot = GEMM1 ? 2 * p.f : p.d;
+    const int slot0 = blk * BM;
+    const int kbeg = blockIdx.y * p.kchunk;
+    const int kend = min(K, kbeg + p.kchunk);
+
+    // ---- global -> LDS staging assignment ---------------------------------
+    // thread t moves chunk (t & 7) of rows (t >> 3) + 32 i.
+    const int cchunk = tid & 7, crow = tid >> 3;
+    const uint8_t *asrc[A_CHUNKS];
+    bool aok[A_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+        const int row = crow + 32 * i;
+        const int slot = slot0 + row;
+        if (GEMM1) {
+            const int a = p.sorted_ids[slot];
+            aok[i] = a < sentinel;
+            const int t = aok[i] ? a / p.k : 0;
+            asrc[i] = p.a + ((size_t)t * K) * ES + cchunk * 16;
+        } else {
+            aok[i] = true;
+            asrc[i] = p.a + ((size_t)slot * K) * ES + cchunk * 16;
+        }
+    }
+    const uint8_t *bsrc[B_CHUNKS];
+    const uint8_t *wexp = p.w + (size_t)e * Ntot * K * ES;
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) {
+        const int row = crow + 32 * i;   // 0..255
+        int n;
+        if (GEMM1)
+            n = (row < 128 ? 0 : p.f - 128) + nt * 128 + row;
+        else
+            n = nt * TILE_N + row;
+        bsrc[i] = wexp + ((size_t)n * K) * ES + cchunk * 16;
+    }
+    u32x4 sa[A_CHUNKS], sb[B_CHUNKS];
+    auto gload = [&](int kk) {
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            sa[i] = *reinterpret_cast<const u32x4 *>(asrc[i] + (size_t)kk * ES);
+            if (!aok[i]) sa[i] = u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < B_CHUNKS; ++i)
+            sb[i] = *reinterpret_cast<const u32x4 *>(bsrc[i] + (size_t)kk * ES);
+    };
+    auto lstore = [&](int buf) {
+        uint8_t *base = lds + buf * BUF;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            const int row = crow + 32 * i;
+            *reinterpret_cast<u32x4 *>(base + row * ROWB + swz(row, cchunk) * 16) = sa[i];
+        }
+#pragma unroll
+        for (int i = 0; i < B_CHUNKS; ++i) {
+            const int row = crow + 32 * i;
+            *reinterpret_cast<u32x4 *>(base + (BM + row) * ROWB + swz(row, cchunk) * 16) = sb[i];
+        }
+    };
+
+    // ---- compute assignment -------------------------------------------------
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 31, lh = lane >> 5;
+    int arow[RT], brow[CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) arow[rt] = wm * (BM / 2) + rt * 32 + lr;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        if (GEMM1)
+            brow[ct] = (ct < 2 ? 0 : 128) + wn * 64 + (ct & 1) * 32 + lr;
+        else
+            brow[ct] = wn * 128 + ct * 32 + lr;
+    }
+    f32x16 acc[RT][CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0.0f;
+
+    auto compute = [&](int buf) {
+        const uint8_t *base = lds + buf * BUF;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int chunk = 2 * s + lh;
+            u32x4 fa[RT], fb[CT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                fa[rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB +
+                                                          swz(arow[rt], chunk) * 16);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                fb[ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
+                                                          swz(brow[ct], chunk) * 16);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32<QUANT>(fa[rt], fb[ct], acc[rt][ct]);
+        }
+    };
+
+    // ---- main loop: prefetch step k+1 into registers while computing step k --
+    if (kbeg < kend) {
+        gload(kbeg);
+        lstore(0);
+        __syncthreads();
+        int buf = 0;
+        for (int kk = kbeg; kk < kend; kk += KS) {
+            const bool more = kk + KS < kend;
+            if (more) gload(kk + KS);
+            compute(buf);
+            if (more) lstore(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+
+    // ---- epilogue -----------------------------------------------------------
+    // 32x32 accumulator layout: lane holds column (lane & 31) and rows
+    // 8 * (v / 4) + 4 * (lane >> 5) + (v & 3), v = 0..15.
+    if constexpr (GEMM1) {
+        const int f = p.f;
+        uint16_t *h = reinterpret_cast<uint16_t *>(p.out);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = wm * (BM / 2) + rt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                const int slot = slot0 + row;
+                float sx = 1.0f;
+                if constexpr (QUANT == 1) {
+                    const int a = p.sorted_ids[slot];
+                    sx = a < sentinel ? p.a_scale[a / p.k] : 0.0f;
+                }
+                float m = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int n = nt * 128 + wn * 64 + c * 32 + lr;
+                    float g = acc[rt][c][v], u = acc[rt][c + 2][v];
+                    if constexpr (QUANT == 1) {
+                        g = g * sx * p.w_scale[(size_t)e * Ntot + n];
+                        u = u * sx * p.w_scale[(size_t)e * Ntot + f + n];
+                    }
+                    const uint16_t hb = f32_to_bf16_bits(silu(g) * u);
+                    h[(size_t)slot * f + n] = hb;
+                    m = fmaxf(m, fabsf(bf16_bits_to_f32(hb)));
+                }
+                if constexpr (QUANT == 1) {
+#pragma unroll
+                    for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                    if (lr == 0) atomic_max_nonneg(p.out_scale + slot, m);
+                }
+            }
+        }
+    } else {
+        float *accg = reinterpret_cast<float *>(p.out);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = wm * (BM / 2) + rt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                const int slot = slot0 + row;
+                const int a = p.sorted_ids[slot];
+                if (a >= sentinel) continue;
+                float wgt = p.sorted_w[slot];
+                if constexpr (QUANT == 1) wgt *= p.a_scale[slot];
+                float *dst = accg + (size_t)(a / p.k) * p.d;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int n = nt * TILE_N + wn * 128 + ct * 32 + lr;
+                    float y = acc[rt][ct][v];
+                    if constexpr (QUANT == 1) y *= p.w_scale[(size_t)e * Ntot + n];
+                    atomic_add_f32(dst + n, wgt * y);
+                }
+            }
+        }
+    }
+}
+
+template <int QUANT, bool GEMM1>
+hipError_t dispatch_bm(const TiledParams &p, int BM, dim3 grid, hipStream_t s) {
+    if (BM == 64)
+        k_gemm_tiled<QUANT, GEMM1, 64><<<grid, 256, 0, s>>>(p);
+    else if (BM == 128)
+        k_gemm_tiled<QUANT, GEMM1, 128><<<grid, 256, 0, s>>>(p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <bool GEMM1>
+hipError_t dispatch(const TiledParams &p, int quant, int BM, dim3 grid, hipStream_t s) {
+    if (quant == 0) return dispatch_bm<0, GEMM1>(p, BM, grid, s);
+    if (quant == 1) return dispatch_bm<1, GEMM1>(p, BM, grid, s);
+    return hipErrorInvalidValue;
+}
+
+unsigned grid_tiles(int NB, int ntiles) {
+    const unsigned total = (unsigned)NB * (unsigned)ntiles;
+    return (total + 7) / 8 * 8;
+}
+
+}  // namespace
+
+bool tiled_gemm_supported(const GemmShape &sh) {
+    return (sh.B == 64 || sh.B == 128) && (sh.quant == 0 || sh.quant == 1) && sh.f % 128 == 0 &&
+           sh.d % 256 == 0;
+}
+
+hipError_t launch_tiled_gemm1(const Gemm1Args &g, hipStream_t s) {
+    const GemmShape &sh = g.sh;
+    TiledParams p{};
+    p.a = static_cast<const uint8_t *>(g.a);
+    p.a_scale = g.a_scale;
+    p.w = static_cast<const uint8_t *>(g.w13);
+    p.w_scale = g.w13_scale;
+    p.sorted_ids = g.sorted_ids;
+    p.seid = g.sorted_expert_ids;
+    p.num_valid = g.num_valid;
+    p.out = g.h;
+    p.out_scale = g.h_scale;
+    p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
+    p.kchunk = sh.d;
+    p.zero = g.zero;
+    p.zero_n = g.zero_n;
+    const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
+    const int NB = (P + sh.B - 1) / sh.B;
+    const dim3 grid(grid_tiles(NB, sh.f / 128), 1);
+    return dispatch<true>(p, sh.quant, sh.B, grid, s);
+}
+
+hipError_t launch_tiled_gemm2(const Gemm2Args &g, int ksplit, hipStream_t s) {
+    const GemmShape &sh = g.sh;
+    TiledParams p{};
+    p.a = static_cast<const uint8_t *>(g.h);
+    p.a_scale = g.h_scale;
+    p.w = static_cast<const uint8_t *>(g.w2);
+    p.w_scale = g.w2_scale;
+    p.sorted_ids = g.sorted_ids;
+    p.sorted_w = g.sorted_w;
+    p.seid = g.sorted_expert_ids;
+    p.num_valid = g.num_valid;
+    p.out = g.acc;
+    p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
+    const int KS = sh.quant == 0 ? 64 : 128;
+    const int steps = sh.f / KS;
+    if (ksplit < 1) ksplit = 1;
+    if (ksplit > steps) ksplit = steps;
+    const int steps_per = (steps + ksplit - 1) / ksplit;
+    p.kchunk = steps_per * KS;
+    ksplit = (steps + steps_per - 1) / steps_per;
+    const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
+    const int NB = (P + sh.B - 1) / sh.B;
+    const dim3 grid(grid_tiles(NB, sh.d / TILE_N), ksplit);
+    return dispatch<false>(p, sh.quant, sh.B, grid, s);
+}
+
+}  // namespace moe

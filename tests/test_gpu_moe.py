@@ -25,7 +25,13 @@ SMALL = [
                        score="sigmoid", logits="zipf", seed=25),
     workloads.Workload("one_expert", T=20, d=128, f=128, E=1, k=1, seed=26),
     workloads.Workload("single_token", T=1, d=256, f=256, E=8, k=2, seed=27),
+    workloads.Workload("tiled_bf16", T=300, d=512, f=384, E=4, k=2, seed=29),
+    workloads.Workload("tiled_fp8", T=260, d=768, f=256, E=3, k=2, quant="fp8_token", seed=30),
 ]
+
+
+def _tiled_ok(wl):
+    return wl.quant != "fp8_block" and wl.d % 256 == 0
 
 
 def _run_two_stage(wl, x, ids, w, ws, B, ksplit):
@@ -42,7 +48,11 @@ def test_two_stage_small_all_outputs(wl):
     ref, rid, rw = oracle_layer(wl, x, logits, ws)
     ids = torch.from_numpy(rid).to(DEV)
     w = torch.from_numpy(rw).to(DEV)
-    for B in (16, 32):
+    for B in (16, 32, 64, 128):
+        if B >= 64 and not _tiled_ok(wl):
+            with pytest.raises(moe.MoeError):
+                _run_two_stage(wl, x, ids, w, ws, B, 1)
+            continue
         for ksplit in (1, 3):
             log(f"two-stage {wl.name} B={B} ksplit={ksplit}")
             out = _run_two_stage(wl, x, ids, w, ws, B, ksplit)
@@ -75,7 +85,7 @@ def test_fused_with_given_routing_and_idle_experts():
     rid[::7] = [[1, 3]]
     rw = np.random.default_rng(0).dirichlet([1, 1], wl.T).astype(np.float32)
     ref, _, _ = oracle_layer(wl, x, logits, ws, ids=rid, w=rw)
-    for B in (16, 32):
+    for B in (16, 32, 64, 128):
         out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, topk_ids=torch.from_numpy(rid).to(DEV),
                             topk_w=torch.from_numpy(rw).to(DEV), B=B, stage=2)
         torch.cuda.synchronize()
