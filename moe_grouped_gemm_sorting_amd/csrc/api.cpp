@@ -98,6 +98,8 @@ int check_shape(int T, int d, int f, int E, int k, int B, int quant) {
     if ((int64_t)T * k > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "T*k=%lld above 2^24", (long long)T * k);
     if ((int64_t)T * d >= (int64_t(1) << 31) || ((int64_t)T * k + (int64_t)E * B) * f >= (int64_t(1) << 31))
         return fail(MOE_ERR_UNSUPPORTED, "activation buffers above 2^31 elements");
+    if ((int64_t)2 * f * d * 2 >= (int64_t(1) << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "one expert's weights above 4 GiB");
     return MOE_OK;
 }
 

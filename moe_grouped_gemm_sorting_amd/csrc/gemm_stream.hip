@@ -76,6 +76,16 @@ __device__ __forceinline__ Frag load_frag_stream(const uint8_t *p) {
 #endif
 }
 
+// Padding rows (sentinel slots) enter the MFMA as zeros. The mask is applied
+// where the fragment is consumed: masking right after the load would make
+// the wave wait for that load before issuing the next ones.
+__device__ __forceinline__ Frag masked(const Frag &f, bool ok) {
+    Frag r;
+    r.lo = ok ? f.lo : u32x4{0, 0, 0, 0};
+    r.hi = ok ? f.hi : u32x4{0, 0, 0, 0};
+    return r;
+}
+
 // acc += A . B over one 128-byte K step.
 template <int QUANT>
 __device__ __forceinline__ f32x4 mma_step(const Frag &a, const Frag &b, f32x4 acc) {
@@ -100,6 +110,85 @@ __device__ __forceinline__ f32x4 mma_step(const Frag &a, const Frag &b, f32x4 ac
         acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a3, b3, acc, 0, 0, 0);
     }
     return acc;
+}
+
+#ifndef MOE_STREAM_DEPTH
+#define MOE_STREAM_DEPTH 2
+#endif
+
+template <int QUANT, int RT, int NT>
+struct StepBuf {
+    Frag a[RT], b[NT];
+    float sa[RT][4], sw[NT];
+};
+
+// The K loop of one wave: a ring of DEPTH fragment buffers, fully unrolled so
+// every buffer index is a compile-time constant; the loads of step k + DEPTH-1
+// are issued before the MFMAs of step k. Only the first RTL row tiles hold
+// real rows. Block scales (QUANT 2) travel with their fragments.
+template <int QUANT, int RT, int RTL, int NT>
+__device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t *const (&arow)[RT],
+                                             const bool (&arow_ok)[RT],
+                                             const uint8_t *const (&wrow)[NT],
+                                             const float *const (&sap)[RT][4],
+                                             const float *const (&swp)[NT], int kbeg, int kend) {
+    constexpr int ES = Elem<QUANT>::bytes;
+    constexpr int KS = Elem<QUANT>::kstep;
+    constexpr int DEPTH = MOE_STREAM_DEPTH;
+    StepBuf<QUANT, RT, NT> bf[DEPTH];
+    auto load = [&](StepBuf<QUANT, RT, NT> &b, int kk) {
+#pragma unroll
+        for (int rt = 0; rt < RTL; ++rt) b.a[rt] = load_frag(arow[rt] + (size_t)kk * ES);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) b.b[nt] = load_frag_stream(wrow[nt] + (size_t)kk * ES);
+        if constexpr (QUANT == 2) {
+            const int kb = kk / 128;
+#pragma unroll
+            for (int rt = 0; rt < RTL; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) b.sa[rt][i] = sap[rt][i][kb];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) b.sw[nt] = swp[nt][kb];
+        }
+    };
+    auto compute = [&](const StepBuf<QUANT, RT, NT> &b) {
+#pragma unroll
+        for (int rt = 0; rt < RTL; ++rt) {
+            const Frag a = masked(b.a[rt], arow_ok[rt]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if constexpr (QUANT == 2) {
+                    const f32x4 part = mma_step<QUANT>(a, b.b[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[rt][nt][i] += part[i] * (b.sa[rt][i] * b.sw[nt]);
+                } else {
+                    acc[rt][nt] = mma_step<QUANT>(a, b.b[nt], acc[rt][nt]);
+                }
+            }
+        }
+    };
+    // Straight-line steady state (every load unconditional, so the wait
+    // counts stay exact): prefetches past the last step are clamped to it and
+    // hit the cache.
+    const int nsteps = (kend - kbeg) / KS;
+    if (nsteps <= 0) return;
+    auto kof = [&](int i) { return kbeg + min(i, nsteps - 1) * KS; };
+#pragma unroll
+    for (int s = 0; s < DEPTH - 1; ++s) load(bf[s], kof(s));
+    int i = 0;
+    for (; i + DEPTH <= nsteps; i += DEPTH) {
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) {
+            load(bf[(s + DEPTH - 1) % DEPTH], kof(i + s + DEPTH - 1));
+            // keep the prefetch above the MFMAs (the scheduler would
+            // otherwise sink the loads below them)
+            __builtin_amdgcn_sched_barrier(0);
+            compute(bf[s]);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < DEPTH - 1; ++s)
+        if (i + s < nsteps) compute(bf[s]);
 }
 
 // RT: 16-row tiles per block (B = 16 * RT). CT: 16-column tiles per wave
@@ -183,71 +272,26 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
             }
     }
 
-    Frag fa[2][RT], fb[2][NT];
-    auto load = [&](int buf, int kk) {
+    // scale rows of the block-scaled product (sentinel rows read token 0's
+    // scales; their A fragment is zero, so the product stays zero)
+    const float *sap[RT][4];
+    const float *swp[NT];
+    if constexpr (QUANT == 2) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            if (live[rt]) {
-                fa[buf][rt] = load_frag(arow[rt] + (size_t)kk * ES);
-                if (!arow_ok[rt]) {
-                    fa[buf][rt].lo = u32x4{0, 0, 0, 0};
-                    fa[buf][rt].hi = u32x4{0, 0, 0, 0};
-                }
-            }
-        }
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) fb[buf][nt] = load_frag_stream(wrow[nt] + (size_t)kk * ES);
-    };
-    auto compute = [&](int buf, int kk) {
-        if constexpr (QUANT == 2) {
-            const int kb = kk / 128;
-            float sw[NT];
+            for (int i = 0; i < 4; ++i)
+                sap[rt][i] = p.a_scale + (size_t)max(srow[rt][i], 0) * (K / 128);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int nrow = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16;
-                sw[nt] = p.w_scale[((size_t)e * (Ntot / 128) + nrow / 128) * (K / 128) + kb];
-            }
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                if (!live[rt]) continue;
-                float sa[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sa[i] = srow[rt][i] >= 0 ? p.a_scale[(size_t)srow[rt][i] * (K / 128) + kb] : 0.f;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const f32x4 part = mma_step<QUANT>(fa[buf][rt], fb[buf][nt], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[rt][nt][i] += part[i] * (sa[i] * sw[nt]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                if (!live[rt]) continue;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    acc[rt][nt] = mma_step<QUANT>(fa[buf][rt], fb[buf][nt], acc[rt][nt]);
-            }
-        }
-    };
-
-    int kk = kbeg;
-    if (kk < kend) {
-        load(0, kk);
-        while (true) {
-            const bool more1 = kk + KS < kend;
-            if (more1) load(1, kk + KS);
-            compute(0, kk);
-            if (!more1) break;
-            kk += KS;
-            const bool more2 = kk + KS < kend;
-            if (more2) load(0, kk + KS);
-            compute(1, kk);
-            if (!more2) break;
-            kk += KS;
+        for (int nt = 0; nt < NT; ++nt) {
+            const int nrow = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16;
+            swp[nt] = p.w_scale + ((size_t)e * (Ntot / 128) + nrow / 128) * (K / 128);
         }
     }
+    if (RT == 2 && live[RT - 1])
+        stream_kloop<QUANT, RT, RT, NT>(acc, arow, arow_ok, wrow, sap, swp, kbeg, kend);
+    else
+        stream_kloop<QUANT, RT, 1, NT>(acc, arow, arow_ok, wrow, sap, swp, kbeg, kend);
 
     // ------------------------------------------------------------ epilogue
     if constexpr (GEMM1) {

@@ -13,7 +13,7 @@
 //
 // Operands are staged through LDS, double-buffered, one barrier per K step.
 // Each 128-byte row segment is stored as 8 chunks of 16 bytes whose position
-// is XOR-swizzled by (row >> 1) & 7, so that a fragment read (32 rows, one
+// is XOR-swizzled per row (see swz), so that a fragment read (32 rows, one
 // chunk column) spreads over all banks.
 //
 // Tile order: tiles are enumerated block-group-major (GM sort blocks x all
@@ -33,7 +33,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int TILE_N = 256;     // weight rows per workgroup
 constexpr int ROWB = 128;       // bytes per row per K step
-constexpr int GROUP_M = 4;      // sort blocks per tile group
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 8
+#endif
+constexpr int GROUP_M = MOE_GROUP_M;  // sort blocks per tile group
+#ifndef MOE_TILED_NSTAGE
+#define MOE_TILED_NSTAGE 2
+#endif
+constexpr int NSTAGE = MOE_TILED_NSTAGE;  // K steps of global loads in flight
 
 struct TiledParams {
     const uint8_t *a;
@@ -52,7 +59,20 @@ struct TiledParams {
     size_t zero_n;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// Chunk position of (row, chunk) inside the row's 128 bytes. A fragment read
+// takes one chunk column of consecutive rows: any 8 consecutive rows land on 8
+// different positions (32-bank LDS, 8 lanes per cycle) and any 16 on 16
+// different (row parity, position) pairs (64 banks, 16 lanes per cycle).
+#ifndef MOE_SWIZZLE
+#define MOE_SWIZZLE 1
+#endif
+__device__ __forceinline__ int swz(int row, int chunk) {
+#if MOE_SWIZZLE == 1
+    return chunk ^ (row & 7) ^ ((row >> 3) & 1);
+#else
+    return chunk ^ ((row >> 1) & 7);
+#endif
+}
 
 template <int QUANT>
 __device__ __forceinline__ f32x16 mma32(const u32x4 &a, const u32x4 &b, f32x16 acc) {
@@ -72,14 +92,20 @@ __device__ __forceinline__ f32x16 mma32(const u32x4 &a, const u32x4 &b, f32x16 a
 
 // BM: rows per sort block (64 or 128). QUANT 0 (bf16) or 1 (e4m3, per-row
 // activation scale and per-channel weight scale applied in the epilogue).
-template <int QUANT, bool GEMM1, int BM>
-__global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
+// WAVES: 4 (2 x 2 waves, each (BM/2) x 128) or 8 (2 x 4 waves, each
+// (BM/2) x 64, two waves per SIMD so that one wave's MFMAs cover the other's
+// LDS and barrier waits).
+template <int QUANT, bool GEMM1, int BM, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
+    constexpr int NTHR = 64 * WAVES;
     constexpr int ES = QUANT == 0 ? 2 : 1;
     constexpr int KS = ROWB / ES;               // K elements per step
-    constexpr int A_CHUNKS = BM * 8 / 256;      // 16-byte chunks per thread per step
-    constexpr int B_CHUNKS = TILE_N * 8 / 256;
+    constexpr int A_CHUNKS = BM * 8 / NTHR;     // 16-byte chunks per thread per step
+    constexpr int B_CHUNKS = TILE_N * 8 / NTHR;
+    constexpr int RPASS = NTHR / 8;             // rows covered by one pass of the threads
+    constexpr int WN = WAVES / 2;               // waves along the weight rows
     constexpr int RT = BM / 64;                 // 32-row tiles per wave
-    constexpr int CT = 4;                       // 32-column tiles per wave
+    constexpr int CT = TILE_N / WN / 32;        // 32-column tiles per wave
     constexpr int BUF = (BM + TILE_N) * ROWB;   // bytes per LDS buffer
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
 
@@ -89,7 +115,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
         const size_t nwg = (size_t)gridDim.x * gridDim.y;
         const size_t wg = blockIdx.x + (size_t)gridDim.x * blockIdx.y;
         float4 *z = reinterpret_cast<float4 *>(p.zero);
-        for (size_t i = wg * 256 + tid; i < p.zero_n / 4; i += nwg * 256)
+        for (size_t i = wg * NTHR + tid; i < p.zero_n / 4; i += nwg * NTHR)
             z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
@@ -118,58 +144,65 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
     const int kend = min(K, kbeg + p.kchunk);
 
     // ---- global -> LDS staging assignment ---------------------------------
-    // thread t moves chunk (t & 7) of rows (t >> 3) + 32 i.
+    // thread t moves chunk (t & 7) of rows (t >> 3) + RPASS i.
     const int cchunk = tid & 7, crow = tid >> 3;
-    const uint8_t *asrc[A_CHUNKS];
+    // 32-bit byte offsets from wave-uniform bases keep the address registers
+    // few (the host guarantees every operand matrix is below 4 GiB).
+    uint32_t aoff[A_CHUNKS];
     bool aok[A_CHUNKS];
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) {
-        const int row = crow + 32 * i;
+        const int row = crow + RPASS * i;
         const int slot = slot0 + row;
         if (GEMM1) {
             const int a = p.sorted_ids[slot];
             aok[i] = a < sentinel;
             const int t = aok[i] ? a / p.k : 0;
-            asrc[i] = p.a + ((size_t)t * K) * ES + cchunk * 16;
+            aoff[i] = (uint32_t)t * (uint32_t)(K * ES) + cchunk * 16;
         } else {
             aok[i] = true;
-            asrc[i] = p.a + ((size_t)slot * K) * ES + cchunk * 16;
+            aoff[i] = (uint32_t)slot * (uint32_t)(K * ES) + cchunk * 16;
         }
     }
-    const uint8_t *bsrc[B_CHUNKS];
+    uint32_t boff[B_CHUNKS];
     const uint8_t *wexp = p.w + (size_t)e * Ntot * K * ES;
 #pragma unroll
     for (int i = 0; i < B_CHUNKS; ++i) {
-        const int row = crow + 32 * i;   // 0..255
+        const int row = crow + RPASS * i;   // 0..255
         int n;
         if (GEMM1)
             n = (row < 128 ? 0 : p.f - 128) + nt * 128 + row;
         else
             n = nt * TILE_N + row;
-        bsrc[i] = wexp + ((size_t)n * K) * ES + cchunk * 16;
+        boff[i] = (uint32_t)n * (uint32_t)(K * ES) + cchunk * 16;
     }
-    u32x4 sa[A_CHUNKS], sb[B_CHUNKS];
-    auto gload = [&](int kk) {
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            sa[i] = *reinterpret_cast<const u32x4 *>(asrc[i] + (size_t)kk * ES);
-            if (!aok[i]) sa[i] = u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i)
-            sb[i] = *reinterpret_cast<const u32x4 *>(bsrc[i] + (size_t)kk * ES);
+    struct Stage {
+        u32x4 a[A_CHUNKS], b[B_CHUNKS];
     };
-    auto lstore = [&](int buf) {
+    // kk is clamped by the caller; the loads are unconditional so that the
+    // wait counts in the unrolled loop stay exact.
+    auto gload = [&](Stage &st, int kk) {
+        const uint8_t *ab = p.a + (size_t)kk * ES;
+        const uint8_t *bb = wexp + (size_t)kk * ES;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) st.a[i] = *reinterpret_cast<const u32x4 *>(ab + aoff[i]);
+#pragma unroll
+        for (int i = 0; i < B_CHUNKS; ++i) st.b[i] = *reinterpret_cast<const u32x4 *>(bb + boff[i]);
+    };
+    auto lstore = [&](const Stage &st, int buf) {
         uint8_t *base = lds + buf * BUF;
 #pragma unroll
         for (int i = 0; i < A_CHUNKS; ++i) {
-            const int row = crow + 32 * i;
-            *reinterpret_cast<u32x4 *>(base + row * ROWB + swz(row, cchunk) * 16) = sa[i];
+            // padding rows are zeroed here, where the data has arrived anyway
+            // (masking right after the load would stall the prefetch)
+            const int row = crow + RPASS * i;
+            *reinterpret_cast<u32x4 *>(base + row * ROWB + swz(row, cchunk) * 16) =
+                aok[i] ? st.a[i] : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < B_CHUNKS; ++i) {
-            const int row = crow + 32 * i;
-            *reinterpret_cast<u32x4 *>(base + (BM + row) * ROWB + swz(row, cchunk) * 16) = sb[i];
+            const int row = crow + RPASS * i;
+            *reinterpret_cast<u32x4 *>(base + (BM + row) * ROWB + swz(row, cchunk) * 16) = st.b[i];
         }
     };
 
@@ -181,10 +214,11 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
     for (int rt = 0; rt < RT; ++rt) arow[rt] = wm * (BM / 2) + rt * 32 + lr;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
+        // GEMM1: the first CT/2 tiles are gate rows, the last CT/2 the matching up rows
         if (GEMM1)
-            brow[ct] = (ct < 2 ? 0 : 128) + wn * 64 + (ct & 1) * 32 + lr;
+            brow[ct] = (ct < CT / 2 ? 0 : 128) + wn * (128 / WN) + (ct % (CT / 2)) * 32 + lr;
         else
-            brow[ct] = wn * 128 + ct * 32 + lr;
+            brow[ct] = wn * (TILE_N / WN) + ct * 32 + lr;
     }
     f32x16 acc[RT][CT];
 #pragma unroll
@@ -194,40 +228,75 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0.0f;
 
+    auto frags = [&](const uint8_t *base, int sub, u32x4 (&fa)[RT], u32x4 (&fb)[CT]) {
+        const int chunk = 2 * sub + lh;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            fa[rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB + swz(arow[rt], chunk) * 16);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+            fb[ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
+                                                      swz(brow[ct], chunk) * 16);
+    };
+    // 4 sub-steps of 16 (bf16) or 32 (e4m3) K per step; the fragments of
+    // sub-step s+1 are read from LDS while the MFMAs of sub-step s run.
     auto compute = [&](int buf) {
         const uint8_t *base = lds + buf * BUF;
+        u32x4 fa0[RT], fb0[CT], fa1[RT], fb1[CT];
+        frags(base, 0, fa0, fb0);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int chunk = 2 * s + lh;
-            u32x4 fa[RT], fb[CT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                fa[rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB +
-                                                          swz(arow[rt], chunk) * 16);
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-                fb[ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
-                                                          swz(brow[ct], chunk) * 16);
+        for (int sub = 0; sub < 4; sub += 2) {
+            frags(base, sub + 1, fa1, fb1);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32<QUANT>(fa[rt], fb[ct], acc[rt][ct]);
+                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32<QUANT>(fa0[rt], fb0[ct], acc[rt][ct]);
+            if (sub + 2 < 4) frags(base, sub + 2, fa0, fb0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32<QUANT>(fa1[rt], fb1[ct], acc[rt][ct]);
         }
     };
 
-    // ---- main loop: prefetch step k+1 into registers while computing step k --
-    if (kbeg < kend) {
-        gload(kbeg);
-        lstore(0);
+    // ---- main loop -------------------------------------------------------
+    // LDS holds step j (double-buffered); NSTAGE register sets hold steps
+    // j+1 .. j+NSTAGE in flight, so a global load has about NSTAGE steps of
+    // compute to land. One iteration: load step j+NSTAGE into the set that
+    // held step j, compute step j, move step j+1 from its set into the other
+    // LDS buffer, barrier. Unrolled by 2*NSTAGE so every set / buffer index is
+    // a compile-time constant; loads past the end are clamped to the last
+    // step (cache hits) to keep the wait counts exact.
+    const int nsteps = (kend - kbeg) / KS;
+    if (nsteps > 0) {
+        auto kof = [&](int i) { return kbeg + min(i, nsteps - 1) * KS; };
+        Stage r[NSTAGE];
+#pragma unroll
+        for (int s = 0; s < NSTAGE; ++s) gload(r[s], kof(s));
+        lstore(r[0], 0);
         __syncthreads();
-        int buf = 0;
-        for (int kk = kbeg; kk < kend; kk += KS) {
-            const bool more = kk + KS < kend;
-            if (more) gload(kk + KS);
-            compute(buf);
-            if (more) lstore(buf ^ 1);
-            __syncthreads();
-            buf ^= 1;
+        constexpr int UNR = 2 * NSTAGE;
+        int j = 0;
+        for (; j + UNR <= nsteps; j += UNR) {
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                gload(r[u % NSTAGE], kof(j + u + NSTAGE));
+                __builtin_amdgcn_sched_barrier(0);
+                compute(u & 1);
+                lstore(r[(u + 1) % NSTAGE], (u + 1) & 1);
+                __syncthreads();
+            }
+        }
+        // the remaining steps (fewer than UNR), same pattern
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            if (j + u < nsteps) {
+                gload(r[u % NSTAGE], kof(j + u + NSTAGE));
+                __builtin_amdgcn_sched_barrier(0);
+                compute(u & 1);
+                lstore(r[(u + 1) % NSTAGE], (u + 1) & 1);
+                __syncthreads();
+            }
         }
     }
 
@@ -250,9 +319,9 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
                 }
                 float m = 0.0f;
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int n = nt * 128 + wn * 64 + c * 32 + lr;
-                    float g = acc[rt][c][v], u = acc[rt][c + 2][v];
+                for (int c = 0; c < CT / 2; ++c) {
+                    const int n = nt * 128 + wn * (128 / WN) + c * 32 + lr;
+                    float g = acc[rt][c][v], u = acc[rt][c + CT / 2][v];
                     if constexpr (QUANT == 1) {
                         g = g * sx * p.w_scale[(size_t)e * Ntot + n];
                         u = u * sx * p.w_scale[(size_t)e * Ntot + f + n];
@@ -283,7 +352,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
                 float *dst = accg + (size_t)(a / p.k) * p.d;
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    const int n = nt * TILE_N + wn * 128 + ct * 32 + lr;
+                    const int n = nt * TILE_N + wn * (TILE_N / WN) + ct * 32 + lr;
                     float y = acc[rt][ct][v];
                     if constexpr (QUANT == 1) y *= p.w_scale[(size_t)e * Ntot + n];
                     atomic_add_f32(dst + n, wgt * y);
@@ -293,12 +362,17 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(TiledParams p) {
     }
 }
 
+#ifndef MOE_TILED_WAVES
+#define MOE_TILED_WAVES 8
+#endif
+
 template <int QUANT, bool GEMM1>
 hipError_t dispatch_bm(const TiledParams &p, int BM, dim3 grid, hipStream_t s) {
+    constexpr int W = MOE_TILED_WAVES;
     if (BM == 64)
-        k_gemm_tiled<QUANT, GEMM1, 64><<<grid, 256, 0, s>>>(p);
+        k_gemm_tiled<QUANT, GEMM1, 64, W><<<grid, 64 * W, 0, s>>>(p);
     else if (BM == 128)
-        k_gemm_tiled<QUANT, GEMM1, 128><<<grid, 256, 0, s>>>(p);
+        k_gemm_tiled<QUANT, GEMM1, 128, W><<<grid, 64 * W, 0, s>>>(p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
