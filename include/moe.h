@@ -147,7 +147,7 @@ int moe_quant_act(const void *x, int rows, int cols, int group, uint8_t *codes, 
  *                     h_scale [P].
  *   quant FP8_BLOCK:  h [P, f] e4m3 codes per 1x128 block, h_scale [P, f/128].
  *   For fp8, x is quantised inside (into ws) with the matching group.
- * B must be 16, 32, 64 or 128. */
+ * B must be 16, 32, 64, 128 or 256. */
 size_t moe_gemm1_workspace_bytes(int T, int d, int f, int E, int k, int B, int quant);
 int moe_gemm1_swiglu(int T, int d, int f, int E, int k, int B, int quant,
                      const void *x, const void *w13, const float *w13_scale,

@@ -19,6 +19,13 @@
 #ifndef MOE_G2_CT
 #define MOE_G2_CT 4
 #endif
+// rows per tiled-kernel tile (0: the sort block size)
+#ifndef MOE_G1_BM
+#define MOE_G1_BM 0
+#endif
+#ifndef MOE_G2_BM
+#define MOE_G2_BM 0
+#endif
 
 namespace moe {
 // implemented in gemm_stream.hip / gemm_tiled.hip / moe_1stage.hip
@@ -27,8 +34,8 @@ bool stream_gemm2_supported(const GemmShape &sh);
 hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s);
 hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream_t s);
 bool tiled_gemm_supported(const GemmShape &sh);
-hipError_t launch_tiled_gemm1(const Gemm1Args &g, hipStream_t s);
-hipError_t launch_tiled_gemm2(const Gemm2Args &g, int ksplit, hipStream_t s);
+hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, hipStream_t s);
+hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int ksplit, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -84,7 +91,7 @@ int cu_count_cached() {
     return cached[dev];
 }
 
-bool valid_B(int B) { return B == 16 || B == 32 || B == 64 || B == 128; }
+bool valid_B(int B) { return B == 16 || B == 32 || B == 64 || B == 128 || B == 256; }
 
 int check_shape(int T, int d, int f, int E, int k, int B, int quant) {
     if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
@@ -94,7 +101,7 @@ int check_shape(int T, int d, int f, int E, int k, int B, int quant) {
     if (d % 128 || f % 128)
         return fail(MOE_ERR_UNSUPPORTED, "d=%d and f=%d must be multiples of 128", d, f);
     if (quant < 0 || quant > 2) return fail(MOE_ERR_INVALID_ARG, "bad quant %d", quant);
-    if (!valid_B(B)) return fail(MOE_ERR_INVALID_ARG, "B=%d must be 16, 32, 64 or 128", B);
+    if (!valid_B(B)) return fail(MOE_ERR_INVALID_ARG, "B=%d must be 16, 32, 64, 128 or 256", B);
     if ((int64_t)T * k > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "T*k=%lld above 2^24", (long long)T * k);
     if ((int64_t)T * d >= (int64_t(1) << 31) || ((int64_t)T * k + (int64_t)E * B) * f >= (int64_t(1) << 31))
         return fail(MOE_ERR_UNSUPPORTED, "activation buffers above 2^31 elements");
@@ -206,7 +213,7 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     if (use_tiled(B)) {
         if (!tiled_gemm_supported(g.sh))
             return fail(MOE_ERR_UNSUPPORTED, "no tiled GEMM1 kernel for B=%d quant=%d d=%d", B, quant, d);
-        HIP_TRY(launch_tiled_gemm1(g, s), "GEMM1 launch");
+        HIP_TRY(launch_tiled_gemm1(g, MOE_G1_BM, s), "GEMM1 launch");
     } else {
         if (!stream_gemm1_supported(g.sh))
             return fail(MOE_ERR_UNSUPPORTED, "no GEMM1 kernel for B=%d", B);
@@ -244,7 +251,7 @@ int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, c
         return fail(MOE_ERR_UNSUPPORTED, "no GEMM2 kernel for B=%d quant=%d d=%d", B, quant, d);
     if (!acc_zeroed) HIP_TRY(launch_fill_f32(acc, (size_t)T * d, 0.0f, s), "fill launch");
     if (tiled)
-        HIP_TRY(launch_tiled_gemm2(g, ksplit, s), "GEMM2 launch");
+        HIP_TRY(launch_tiled_gemm2(g, MOE_G2_BM, ksplit, s), "GEMM2 launch");
     else
         HIP_TRY(launch_stream_gemm2(g, MOE_G2_CT, ksplit, s), "GEMM2 launch");
     HIP_TRY(launch_finalize(acc, static_cast<uint16_t *>(out), (size_t)T * d, s), "finalize launch");
@@ -436,8 +443,12 @@ static int resolve(int T, int d, int f, int E, int k, int quant, int *B, int *st
         if (*stage == 0) *stage = c.stage;
     }
     if (*stage != 1 && *stage != 2) return fail(MOE_ERR_INVALID_ARG, "bad stage %d", *stage);
-    if (*stage == 1) return fail(MOE_ERR_UNSUPPORTED, "the one-stage kernel is not built");
-    return check_shape(T, d, f, E, k, *B, quant);
+    int rc = check_shape(T, d, f, E, k, *B, quant);
+    if (rc) return rc;
+    if (*stage == 1 && !onestage_supported(GemmShape{T, d, f, E, k, *B, quant}))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "the one-stage kernel takes bf16 with B = 16 or 32 (got quant=%d B=%d)", quant, *B);
+    return MOE_OK;
 }
 
 size_t fused_moe_workspace_bytes(int T, int d, int f, int E, int k, int quant, int B, int stage) {
@@ -468,15 +479,28 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     hipStream_t s = (hipStream_t)stream;
     Carver cw(ws);
     FusedWs w = carve_fused(cw, T, d, f, E, k, quant, B, true);
+    // the one-stage path needs a cleared accumulator before its kernel; the
+    // routing+sort workgroup clears small ones on the way
+    const size_t acc_n = (size_t)T * d;
+    const bool zero_in_sort = stage == 1 && logits && acc_n <= (size_t(1) << 20);
     if (logits) {
         HIP_TRY(launch_route_sort(logits, T, k, E, B, score, renorm, w.topk_ids, w.topk_w,
                                   w.sorted_ids, w.sorted_w, w.seid, w.counts, w.offsets,
-                                  w.num_valid, s),
+                                  w.num_valid, s, zero_in_sort ? w.acc : nullptr,
+                                  zero_in_sort ? (int)acc_n : 0),
                 "route+sort launch");
     } else {
         HIP_TRY(launch_sort(topk_ids, topk_w, T, k, E, B, w.sorted_ids, w.sorted_w, w.seid,
                             w.counts, w.offsets, w.num_valid, s),
                 "sort launch");
+    }
+    if (stage == 1) {
+        if (!zero_in_sort) HIP_TRY(launch_fill_f32(w.acc, acc_n, 0.0f, s), "fill launch");
+        HIP_TRY(launch_moe_1stage(GemmShape{T, d, f, E, k, B, quant}, x, w13, w2, w.sorted_ids,
+                                  w.sorted_w, w.seid, w.acc, s),
+                "one-stage launch");
+        HIP_TRY(launch_finalize(w.acc, static_cast<uint16_t *>(out), acc_n, s), "finalize launch");
+        return MOE_OK;
     }
     // GEMM1 also clears GEMM2's accumulator (same stream, so it is done first)
     rc = run_gemm1(T, d, f, E, k, B, quant, x, w13, w13_scale, w.sorted_ids, w.seid, w.num_valid,

@@ -10,7 +10,9 @@
 // its MFMA fragments straight from global memory: lane l serves row/column
 // l % 16 and the 32-byte piece (l / 16) of each 128-byte K step, i.e. a wave
 // reads whole 128-byte lines of 16 rows. The same K permutation is used for
-// both operands, so the v_mfma_f32_16x16x32 sums are the plain dot products.
+// both operands, so the MFMA sums are the plain dot products
+// (v_mfma_f32_16x16x32_bf16 twice, or one v_mfma_scale_f32_16x16x128_f8f6f4
+// with unit scales, per step).
 // No LDS: weights are used by exactly one workgroup, which is the decode
 // (weight-streaming, HBM-bound) regime.
 //
@@ -95,19 +97,15 @@ __device__ __forceinline__ f32x4 mma_step(const Frag &a, const Frag &b, f32x4 ac
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.hi),
                                                        __builtin_bit_cast(bf16x8, b.hi), acc, 0, 0, 0);
     } else {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const long a0 = __builtin_bit_cast(long, u32x2{a.lo.x, a.lo.y});
-        const long a1 = __builtin_bit_cast(long, u32x2{a.lo.z, a.lo.w});
-        const long a2 = __builtin_bit_cast(long, u32x2{a.hi.x, a.hi.y});
-        const long a3 = __builtin_bit_cast(long, u32x2{a.hi.z, a.hi.w});
-        const long b0 = __builtin_bit_cast(long, u32x2{b.lo.x, b.lo.y});
-        const long b1 = __builtin_bit_cast(long, u32x2{b.lo.z, b.lo.w});
-        const long b2 = __builtin_bit_cast(long, u32x2{b.hi.x, b.hi.y});
-        const long b3 = __builtin_bit_cast(long, u32x2{b.hi.z, b.hi.w});
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a0, b0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a1, b1, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2, b2, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a3, b3, acc, 0, 0, 0);
+        // one e4m3 MFMA over the whole 128-byte step (K = 128) with unit
+        // E8M0 scales (127 = 2^0); both operands use the same lane/byte
+        // layout, so the sum is the plain dot product
+        typedef int i32x8 __attribute__((ext_vector_type(8)));
+        const i32x8 av = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w,
+                          (int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w};
+        const i32x8 bv = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w,
+                          (int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
     }
     return acc;
 }

@@ -8,8 +8,9 @@
 // Workgroup tile: one sort block (BM = B rows of one expert) x 256 weight
 // rows (GEMM1: 128 gate rows + the 128 matching up rows, so SwiGLU fuses into
 // the epilogue; GEMM2: 256 output columns), K in steps of 128 bytes per row.
-// 4 waves in a 2 x 2 arrangement, each owning (BM/2) x 128 of the tile with
-// v_mfma_f32_32x32x16 (bf16, or e4m3 twice per 16-byte fragment).
+// 8 waves in a 2 x 4 arrangement, each owning (BM/2) x 64 of the tile, with
+// v_mfma_f32_32x32x16_bf16 or, for e4m3, v_mfma_scale_f32_32x32x64_f8f6f4
+// with unit scales (per-row / per-channel fp32 scales go in the epilogue).
 //
 // Operands are staged through LDS, double-buffered, one barrier per K step.
 // Each 128-byte row segment is stored as 8 chunks of 16 bytes whose position
@@ -74,20 +75,21 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 #endif
 }
 
-template <int QUANT>
-__device__ __forceinline__ f32x16 mma32(const u32x4 &a, const u32x4 &b, f32x16 acc) {
-    if constexpr (QUANT == 0) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-    } else {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const long a0 = __builtin_bit_cast(long, u32x2{a.x, a.y});
-        const long a1 = __builtin_bit_cast(long, u32x2{a.z, a.w});
-        const long b0 = __builtin_bit_cast(long, u32x2{b.x, b.y});
-        const long b1 = __builtin_bit_cast(long, u32x2{b.z, b.w});
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a0, b0, acc, 0, 0, 0);
-        return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a1, b1, acc, 0, 0, 0);
-    }
+__device__ __forceinline__ f32x16 mma32_bf16(const u32x4 &a, const u32x4 &b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+// e4m3 x e4m3 over K = 64 (32 bytes per lane: two LDS chunks) with unit
+// E8M0 scales; A and B use the same lane/byte layout.
+__device__ __forceinline__ f32x16 mma32_fp8(const u32x4 &a0, const u32x4 &a1, const u32x4 &b0,
+                                            const u32x4 &b1, f32x16 acc) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const i32x8 bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                      (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
 }
 
 // BM: rows per sort block (64 or 128). QUANT 0 (bf16) or 1 (e4m3, per-row
@@ -121,6 +123,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 
     // ---- which tile -------------------------------------------------------
     const int ntiles = GEMM1 ? p.f / 128 : p.d / TILE_N;
+    // tiles of BM rows; the sort block B is a multiple of BM, so a tile never
+    // straddles two experts
     const int nblocks = *p.num_valid / BM;
     const int total = nblocks * ntiles;
     const int per_xcd = (total + 7) / 8;
@@ -133,10 +137,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     const int r = logical - group * GROUP_M * ntiles;
     const int nt = r / gm;
     const int blk = group * GROUP_M + r % gm;
-    const int e = p.seid[blk];
+    const int e = p.seid[blk * BM / p.B];
     if (e < 0) return;
 
     const int sentinel = p.T * p.k;
+    // a tile of padding only (the tail of a larger sort block)
+    if (p.sorted_ids[blk * BM] >= sentinel) return;
     const int K = GEMM1 ? p.d : p.f;
     const int Ntot = GEMM1 ? 2 * p.f : p.d;
     const int slot0 = blk * BM;
@@ -228,8 +234,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0.0f;
 
-    auto frags = [&](const uint8_t *base, int sub, u32x4 (&fa)[RT], u32x4 (&fb)[CT]) {
-        const int chunk = 2 * sub + lh;
+    auto frags_at = [&](const uint8_t *base, int chunk, u32x4 (&fa)[RT], u32x4 (&fb)[CT]) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
             fa[rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB + swz(arow[rt], chunk) * 16);
@@ -238,24 +243,50 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             fb[ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
                                                       swz(brow[ct], chunk) * 16);
     };
-    // 4 sub-steps of 16 (bf16) or 32 (e4m3) K per step; the fragments of
-    // sub-step s+1 are read from LDS while the MFMAs of sub-step s run.
-    auto compute = [&](int buf) {
+    // bf16: 4 sub-steps of K = 16 (lane half lh takes chunk 2s + lh); the
+    // fragments of sub-step s+1 are read while the MFMAs of sub-step s run.
+    // e4m3: 2 sub-steps of K = 64 (lane half lh takes chunks 4s + 2lh and
+    // 4s + 2lh + 1). The next step's staged operands (`st`, already in
+    // registers) are written to the other LDS buffer right after the first
+    // fragment reads, so that the LDS writes overlap the MFMAs instead of
+    // forming a burst before the barrier.
+    auto compute = [&](int buf, const Stage &st) {
         const uint8_t *base = lds + buf * BUF;
-        u32x4 fa0[RT], fb0[CT], fa1[RT], fb1[CT];
-        frags(base, 0, fa0, fb0);
+        if constexpr (QUANT == 0) {
+            u32x4 fa0[RT], fb0[CT], fa1[RT], fb1[CT];
+            frags_at(base, lh, fa0, fb0);
+            lstore(st, buf ^ 1);
 #pragma unroll
-        for (int sub = 0; sub < 4; sub += 2) {
-            frags(base, sub + 1, fa1, fb1);
+            for (int sub = 0; sub < 4; sub += 2) {
+                frags_at(base, 2 * (sub + 1) + lh, fa1, fb1);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32_bf16(fa0[rt], fb0[ct], acc[rt][ct]);
+                if (sub + 2 < 4) frags_at(base, 2 * (sub + 2) + lh, fa0, fb0);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32_bf16(fa1[rt], fb1[ct], acc[rt][ct]);
+            }
+        } else {
+            u32x4 fa0[RT], fb0[CT], fa1[RT], fb1[CT];
+            u32x4 ga0[RT], gb0[CT], ga1[RT], gb1[CT];
+            frags_at(base, 2 * lh, fa0, fb0);
+            frags_at(base, 2 * lh + 1, fa1, fb1);
+            lstore(st, buf ^ 1);
+            frags_at(base, 4 + 2 * lh, ga0, gb0);
+            frags_at(base, 4 + 2 * lh + 1, ga1, gb1);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32<QUANT>(fa0[rt], fb0[ct], acc[rt][ct]);
-            if (sub + 2 < 4) frags(base, sub + 2, fa0, fb0);
+                for (int ct = 0; ct < CT; ++ct)
+                    acc[rt][ct] = mma32_fp8(fa0[rt], fa1[rt], fb0[ct], fb1[ct], acc[rt][ct]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32<QUANT>(fa1[rt], fb1[ct], acc[rt][ct]);
+                for (int ct = 0; ct < CT; ++ct)
+                    acc[rt][ct] = mma32_fp8(ga0[rt], ga1[rt], gb0[ct], gb1[ct], acc[rt][ct]);
         }
     };
 
@@ -282,8 +313,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             for (int u = 0; u < UNR; ++u) {
                 gload(r[u % NSTAGE], kof(j + u + NSTAGE));
                 __builtin_amdgcn_sched_barrier(0);
-                compute(u & 1);
-                lstore(r[(u + 1) % NSTAGE], (u + 1) & 1);
+                compute(u & 1, r[(u + 1) % NSTAGE]);
                 __syncthreads();
             }
         }
@@ -293,8 +323,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             if (j + u < nsteps) {
                 gload(r[u % NSTAGE], kof(j + u + NSTAGE));
                 __builtin_amdgcn_sched_barrier(0);
-                compute(u & 1);
-                lstore(r[(u + 1) % NSTAGE], (u + 1) & 1);
+                compute(u & 1, r[(u + 1) % NSTAGE]);
                 __syncthreads();
             }
         }
@@ -393,11 +422,18 @@ unsigned grid_tiles(int NB, int ntiles) {
 }  // namespace
 
 bool tiled_gemm_supported(const GemmShape &sh) {
-    return (sh.B == 64 || sh.B == 128) && (sh.quant == 0 || sh.quant == 1) && sh.f % 128 == 0 &&
-           sh.d % 256 == 0;
+    return (sh.B == 64 || sh.B == 128 || sh.B == 256) && (sh.quant == 0 || sh.quant == 1) &&
+           sh.f % 128 == 0 && sh.d % 256 == 0;
 }
 
-hipError_t launch_tiled_gemm1(const Gemm1Args &g, hipStream_t s) {
+// Rows per kernel tile: 64 or 128, a divisor of the sort block B (a 256-row
+// sort block runs as two 128-row tiles); other values pick min(B, 128).
+int tile_rows(int B, int bm) {
+    if (bm <= 0 || bm > B || B % bm || bm > 128) bm = B < 128 ? B : 128;
+    return bm;
+}
+
+hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, hipStream_t s) {
     const GemmShape &sh = g.sh;
     TiledParams p{};
     p.a = static_cast<const uint8_t *>(g.a);
@@ -413,13 +449,14 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, hipStream_t s) {
     p.kchunk = sh.d;
     p.zero = g.zero;
     p.zero_n = g.zero_n;
+    bm = tile_rows(sh.B, bm);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
-    const int NB = (P + sh.B - 1) / sh.B;
+    const int NB = (P + bm - 1) / bm;
     const dim3 grid(grid_tiles(NB, sh.f / 128), 1);
-    return dispatch<true>(p, sh.quant, sh.B, grid, s);
+    return dispatch<true>(p, sh.quant, bm, grid, s);
 }
 
-hipError_t launch_tiled_gemm2(const Gemm2Args &g, int ksplit, hipStream_t s) {
+hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int ksplit, hipStream_t s) {
     const GemmShape &sh = g.sh;
     TiledParams p{};
     p.a = static_cast<const uint8_t *>(g.h);
@@ -439,10 +476,11 @@ hipError_t launch_tiled_gemm2(const Gemm2Args &g, int ksplit, hipStream_t s) {
     const int steps_per = (steps + ksplit - 1) / ksplit;
     p.kchunk = steps_per * KS;
     ksplit = (steps + steps_per - 1) / steps_per;
+    bm = tile_rows(sh.B, bm);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
-    const int NB = (P + sh.B - 1) / sh.B;
+    const int NB = (P + bm - 1) / bm;
     const dim3 grid(grid_tiles(NB, sh.d / TILE_N), ksplit);
-    return dispatch<false>(p, sh.quant, sh.B, grid, s);
+    return dispatch<false>(p, sh.quant, bm, grid, s);
 }
 
 }  // namespace moe

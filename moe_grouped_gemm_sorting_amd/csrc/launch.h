@@ -19,7 +19,8 @@ hipError_t launch_sort(const int32_t *ids, const float *w, int T, int k, int E, 
 hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, int score,
                              int renorm, int32_t *ids, float *w, int32_t *sorted_ids,
                              float *sorted_w, int32_t *sorted_expert_ids, int32_t *counts,
-                             int32_t *offsets, int32_t *num_valid, hipStream_t s);
+                             int32_t *offsets, int32_t *num_valid, hipStream_t s,
+                             float *zero = nullptr, int zero_n = 0);
 
 // codes [rows, cols], scales [rows, cols / group]
 hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, uint8_t *codes,
@@ -65,9 +66,9 @@ struct Gemm2Args {
     float *acc;             // fp32 [T, d], zeroed by the caller
 };
 
-hipError_t launch_gemm1(const Gemm1Args &a, hipStream_t s);
-hipError_t launch_gemm2(const Gemm2Args &a, hipStream_t s);
-bool gemm1_supported(const GemmShape &sh);
-bool gemm2_supported(const GemmShape &sh);
+bool onestage_supported(const GemmShape &sh);
+hipError_t launch_moe_1stage(const GemmShape &sh, const void *x, const void *w13, const void *w2,
+                             const int32_t *sorted_ids, const float *sorted_w,
+                             const int32_t *sorted_expert_ids, float *acc, hipStream_t s);
 
 }  // namespace moe

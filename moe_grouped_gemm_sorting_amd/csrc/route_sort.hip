@@ -285,7 +285,12 @@ __global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
     const float *__restrict__ logits, int T, int k, int E, int B, int score, int renorm,
     int32_t *__restrict__ ids, float *__restrict__ wts, int P, int NB,
     int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w, int32_t *__restrict__ seid,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ num_valid) {
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ num_valid,
+    float *__restrict__ zero, int zero_n) {
+    // optionally clear a (small) fp32 accumulator for the next stage
+    if (zero)
+        for (int i = threadIdx.x; i < zero_n / 4; i += SORT_THREADS)
+            reinterpret_cast<float4 *>(zero)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (PER_LANE == 0) {
         for (int t = threadIdx.x; t < T; t += SORT_THREADS)
             topk_thread(logits, t, E, k, score, renorm, ids, wts);
@@ -301,14 +306,15 @@ __global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
 hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, int score,
                              int renorm, int32_t *ids, float *w, int32_t *sorted_ids,
                              float *sorted_w, int32_t *sorted_expert_ids, int32_t *counts,
-                             int32_t *offsets, int32_t *num_valid, hipStream_t s) {
+                             int32_t *offsets, int32_t *num_valid, hipStream_t s, float *zero,
+                             int zero_n) {
     const int P = T * k + E * B - k;
     const int NB = (P + B - 1) / B;
     const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + E + E + 1);
 #define MOE_ROUTE_SORT(PL)                                                                    \
     k_route_sort<PL><<<1, SORT_THREADS, lds, s>>>(logits, T, k, E, B, score, renorm, ids, w, P, \
                                                    NB, sorted_ids, sorted_w, sorted_expert_ids, \
-                                                   counts, offsets, num_valid)
+                                                   counts, offsets, num_valid, zero, zero_n)
     if (E <= 64) MOE_ROUTE_SORT(0);
     else if (E <= 128) MOE_ROUTE_SORT(2);
     else if (E <= 256) MOE_ROUTE_SORT(4);

@@ -48,7 +48,7 @@ def test_two_stage_small_all_outputs(wl):
     ref, rid, rw = oracle_layer(wl, x, logits, ws)
     ids = torch.from_numpy(rid).to(DEV)
     w = torch.from_numpy(rw).to(DEV)
-    for B in (16, 32, 64, 128):
+    for B in (16, 32, 64, 128, 256):
         if B >= 64 and not _tiled_ok(wl):
             with pytest.raises(moe.MoeError):
                 _run_two_stage(wl, x, ids, w, ws, B, 1)
@@ -120,3 +120,44 @@ def test_fused_full_size_sampled(name):
     assert err <= TOL[wl.quant]
     # tokens outside the sample still got finite values
     assert torch.isfinite(out.float()).all()
+
+
+ONE_STAGE = [w for w in SMALL if w.quant == "bf16"] + [
+    workloads.Workload("decode_t1", T=1, d=4096, f=14336, E=8, k=2, seed=31),
+    workloads.Workload("decode_t4", T=4, d=4096, f=14336, E=8, k=2, seed=32),
+]
+
+
+@pytest.mark.parametrize("wl", ONE_STAGE, ids=lambda w: w.name)
+def test_one_stage_all_outputs(wl):
+    """The one-stage kernel (gate/up, SwiGLU and down per block and f-chunk)
+    against the oracle, at both block sizes it takes."""
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    ref, _, _ = oracle_layer(wl, x, logits, ws)
+    for B in (16, 32):
+        out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, score=wl.score, B=B,
+                            stage=1)
+        torch.cuda.synchronize()
+        err, norm = rel_err(bf16_to_f64(bits(out)), ref)
+        log(f"one-stage {wl.name} B={B}: err={err:.3e} norm={norm:.3e}")
+        assert err <= TOL["bf16"], (B, err)
+
+
+def test_one_stage_full_decode_shape_and_unsupported():
+    wl = workloads.get("mixtral_decode")
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, B=32, stage=1)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle_layer(wl, x, logits, ws)
+    err, _ = rel_err(bf16_to_f64(bits(out)), ref)
+    assert err <= TOL["bf16"]
+    with pytest.raises(moe.MoeError):   # 64-row blocks are not taken by the one-stage kernel
+        moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, B=64, stage=1)
+    fp8 = workloads.Workload("fp8s1", T=4, d=256, f=256, E=4, k=2, quant="fp8_token", seed=33)
+    xf, lf = fp8.activations(DEV)
+    wf = fp8.weights(DEV)
+    with pytest.raises(moe.MoeError):   # per-row h quantisation needs the whole row first
+        moe.fused_moe(xf, wf["w13"], wf["w2"], fp8.k, logits=lf, quant="fp8_token",
+                      w13_scale=wf["w13_scale"], w2_scale=wf["w2_scale"], B=16, stage=1)
