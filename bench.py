@@ -34,6 +34,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_token": 5000.0, "fp8_block": 5000.0}
 METRIC = "fused-MoE tokens/s + % HBM BW (decode) / % MFMA peak (prefill), Mixtral"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["moe_grouped_gemm_sorting_amd/csrc/gemm_stream.hip",
+                  "moe_grouped_gemm_sorting_amd/csrc/gemm_tiled.hip",
                   "moe_grouped_gemm_sorting_amd/csrc/common.h"]
 
 
@@ -62,11 +63,66 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens the CPU oracle runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --calibrate-copy` into HBM bytes per GEMM1 launch and "
+                         "record them in profiles/traffic.json (no GPU needed)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def _pmc_values(run_dir, counter):
+    """Counter values per kernel name (one per dispatch) from a rocprofv3 CSV."""
+    import csv
+    import glob
+    path = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)[0]
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def record_traffic(workload, fetch_dir, write_dir):
+    """HBM bytes per GEMM1 launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    each scaled by what the same counter reads for the 1 GiB device copy."""
+    import workloads
+    wl = workloads.get(workload)
+    import moe_grouped_gemm_sorting_amd as moe
+    B, _, _ = moe.moe_select_config(wl.T, wl.d, wl.f, wl.E, wl.k, wl.quant, cu_count=256)
+    want = ("k_gemm_tiled" if B >= 64 else "k_gemm_stream")
+    out = {}
+    for name, d, ctr in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        m = _pmc_values(d, ctr)
+        # the calibration copy is the largest copy dispatch of the run
+        copy = max((max(v) for k, v in m.items() if "copy" in k.lower()), default=None)
+        g1 = [sum(v) / len(v) for k, v in m.items() if want in k and "true" in k]
+        if copy is None or not g1:
+            raise SystemExit(f"{ctr}: copy kernel or GEMM1 kernel not found in {d}")
+        factor = COPY_BYTES / (copy * 1024.0)
+        out[name] = {"counter_kib": g1[0], "copy_counter_kib": copy, "factor": factor,
+                     "bytes": g1[0] * 1024.0 * factor}
+    rec = {"kernel": f"{want} GEMM1 (B={B})", "fetch": out["fetch"], "write": out["write"],
+           "bytes_per_launch": round(out["fetch"]["bytes"] + out["write"]["bytes"]),
+           "source_hash": kernel_source_hash()}
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        data = {}
+    data[wl.name] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1)
+    print(json.dumps(rec))
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        record_traffic(args.workload, *args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer is built and measured on a single MI355X "
               "(no sharding, no collectives); run it with --gpus 1", file=sys.stderr)
