@@ -19,7 +19,7 @@
 #ifndef MOE_G2_CT
 #define MOE_G2_CT 4
 #endif
-// rows per tiled-kernel tile (0: the sort block size)
+// rows per tiled-kernel tile (0: the library's choice)
 #ifndef MOE_G1_BM
 #define MOE_G1_BM 0
 #endif
@@ -139,9 +139,13 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
 }
 
 // Block size: at least the average rows per expert, so that most experts'
-// weights are streamed once; 64/128-row blocks go to the LDS-tiled kernels.
+// weights are streamed once; 64/128/256-row blocks go to the LDS-tiled
+// kernels. With many rows per expert, bf16 takes 256-row blocks, whose
+// 256 x 256 gate/up tiles need a third fewer operand bytes per MFMA than
+// 128 x 256 tiles (measured: Mixtral prefill GEMM1 -8%, GEMM2 unchanged).
 int choose_B(int T, int E, int k, int quant) {
     const double rows = (double)T * k / E;
+    if (quant == 0 && rows >= 512) return 256;
     if (quant != 2 && rows >= 96) return 128;
     if (quant != 2 && rows >= 48) return 64;
     if (rows <= 4) return 16;
@@ -213,7 +217,9 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     if (use_tiled(B)) {
         if (!tiled_gemm_supported(g.sh))
             return fail(MOE_ERR_UNSUPPORTED, "no tiled GEMM1 kernel for B=%d quant=%d d=%d", B, quant, d);
-        HIP_TRY(launch_tiled_gemm1(g, MOE_G1_BM, s), "GEMM1 launch");
+        // bf16 256-row blocks run as 256-row gate/up tiles
+        const int bm = MOE_G1_BM > 0 ? MOE_G1_BM : (quant == 0 && B == 256 ? 256 : 128);
+        HIP_TRY(launch_tiled_gemm1(g, bm, s), "GEMM1 launch");
     } else {
         if (!stream_gemm1_supported(g.sh))
             return fail(MOE_ERR_UNSUPPORTED, "no GEMM1 kernel for B=%d", B);

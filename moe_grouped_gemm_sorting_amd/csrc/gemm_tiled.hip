@@ -52,12 +52,14 @@ constexpr int TILE_N = 256;     // weight rows per workgroup
 constexpr int ROWB = 128;       // bytes per row per K step
 constexpr int WAVES = 8;
 constexpr int NTHR = 64 * WAVES;
-constexpr int NBUF = 3;         // LDS stages
 constexpr int HROW = 272;       // bytes per row of the staged h tile (256 + 16 against bank conflicts)
 #ifndef MOE_GROUP_M
 #define MOE_GROUP_M 8
 #endif
 constexpr int GROUP_M = MOE_GROUP_M;  // sort blocks per tile group
+#ifndef MOE_TILED_SCHED
+#define MOE_TILED_SCHED 0
+#endif
 
 struct TiledParams {
     const uint8_t *a;
@@ -136,6 +138,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
     constexpr int NQA = BM / 8 / WAVES;         // ... of which activation rows
     constexpr int RT = BM / 64;                 // 32-row tiles per wave
     constexpr int CT = 2;                       // 32-column tiles per wave
+    constexpr int NBUF = BM >= 256 ? 2 : 3;     // LDS stages (160 KB of LDS per CU)
     static_assert(BM % (8 * WAVES) == 0, "tile rows");
     static_assert(BM * HROW <= NBUF * BUF, "h staging");
     __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * BUF];
@@ -301,6 +304,16 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32_bf16(fa1[rt], fb1[ct], acc[rt][ct]);
             }
+#if MOE_TILED_SCHED
+            // reads of sub-step s+1 interleaved with the MFMAs of sub-step s
+            __builtin_amdgcn_sched_group_barrier(0x100, RT + CT, 0);
+#pragma unroll
+            for (int i = 0; i < 3 * RT * CT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, RT * CT, 0);
+#endif
         } else {
             u32x4 fa0[RT], fb0[CT], fa1[RT], fb1[CT];
             u32x4 ga0[RT], gb0[CT], ga1[RT], gb1[CT];
@@ -318,37 +331,47 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
                     acc[rt][ct] = mma32_fp8(ga0[rt], ga1[rt], gb0[ct], gb1[ct], acc[rt][ct]);
+#if MOE_TILED_SCHED
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RT + CT), 0);
+#pragma unroll
+            for (int i = 0; i < RT * CT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, RT * CT, 0);
+#endif
         }
     };
 
     // ---- main loop -------------------------------------------------------
-    // Step j: issue the loads of step j+2 into stage (j+2) % 3 (read during
-    // step j-1, which every wave has finished: barrier), multiply stage j % 3,
-    // wait for this wave's loads of step j+1, barrier (so all of step j+1 has
-    // landed and stage j % 3 is free). Unrolled by 3 so that the stage offsets
-    // are constants; loads past the end are clamped to the last step, which
-    // keeps the wait counts exact and lands in a stage nobody reads.
+    // With S = NBUF stages, step j: issue the loads of step j+S-1 into stage
+    // (j+S-1) % S (read during step j-1, which every wave has finished:
+    // barrier), multiply stage j % S, wait for this wave's loads of step j+1,
+    // barrier (so all of step j+1 has landed and stage j % S is free).
+    // Unrolled by S so that the stage offsets are constants; loads past the
+    // end are clamped to the last step, which keeps the wait counts exact and
+    // lands in a stage nobody reads.
     const int nsteps = (kend - kbeg) / KS;
     if (nsteps > 0) {
         auto kof = [&](int i) { return kbeg + min(i, nsteps - 1) * KS; };
-        issue(0, kof(0));
-        issue(1, kof(1));
-        wait_vmem<NQ>();
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b) issue(b, kof(b));
+        wait_vmem<NQ * (NBUF - 2)>();
         __syncthreads();
         auto step = [&](int j, int b) {
-            issue((b + 2) % NBUF, kof(j + 2));
+            issue((b + NBUF - 1) % NBUF, kof(j + NBUF - 1));
             compute(b);
-            wait_vmem<NQ>();
+            wait_vmem<NQ * (NBUF - 2)>();
             __syncthreads();
         };
         int j = 0;
         for (; j + NBUF <= nsteps; j += NBUF) {
-            step(j, 0);
-            step(j + 1, 1);
-            step(j + 2, 2);
+#pragma unroll
+            for (int b = 0; b < NBUF; ++b) step(j + b, b);
         }
-        if (j < nsteps) step(j, 0);
-        if (j + 1 < nsteps) step(j + 1, 1);
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b)
+            if (j + b < nsteps) step(j + b, b);
     }
     wait_vmem<0>();
     __syncthreads();   // the clamped loads have landed; metadata is visible
@@ -432,6 +455,8 @@ hipError_t dispatch_bm(const TiledParams &p, int BM, dim3 grid, hipStream_t s) {
         k_gemm_tiled<QUANT, GEMM1, 64><<<grid, NTHR, 0, s>>>(p);
     else if (BM == 128)
         k_gemm_tiled<QUANT, GEMM1, 128><<<grid, NTHR, 0, s>>>(p);
+    else if (QUANT == 0 && BM == 256)
+        k_gemm_tiled<0, GEMM1, 256><<<grid, NTHR, 0, s>>>(p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -456,10 +481,11 @@ bool tiled_gemm_supported(const GemmShape &sh) {
            sh.f % 128 == 0 && sh.d % 256 == 0;
 }
 
-// Rows per kernel tile: 64 or 128, a divisor of the sort block B (a 256-row
-// sort block runs as two 128-row tiles); other values pick min(B, 128).
-int tile_rows(int B, int bm) {
-    if (bm <= 0 || bm > B || B % bm || bm > 128) bm = B < 128 ? B : 128;
+// Rows per kernel tile: 64, 128 or (bf16) 256, a divisor of the sort block
+// B; other values pick min(B, 128).
+int tile_rows(int B, int bm, int quant) {
+    const int maxbm = quant == 0 ? 256 : 128;
+    if (bm <= 0 || bm > B || B % bm || bm > maxbm) bm = B < 128 ? B : 128;
     return bm;
 }
 
@@ -479,7 +505,7 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, hipStream_t s) {
     p.kchunk = sh.d;
     p.zero = g.zero;
     p.zero_n = g.zero_n;
-    bm = tile_rows(sh.B, bm);
+    bm = tile_rows(sh.B, bm, sh.quant);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + bm - 1) / bm;
     const dim3 grid(grid_tiles(NB, sh.f / 128), 1);
@@ -506,7 +532,7 @@ hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int ksplit, hipStream_
     const int steps_per = (steps + ksplit - 1) / ksplit;
     p.kchunk = steps_per * KS;
     ksplit = (steps + steps_per - 1) / steps_per;
-    bm = tile_rows(sh.B, bm);
+    bm = tile_rows(sh.B, bm, sh.quant);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + bm - 1) / bm;
     const dim3 grid(grid_tiles(NB, sh.d / TILE_N), ksplit);

@@ -103,6 +103,6 @@ def test_select_config_is_host_only_and_valid(lib):
                   (4096, 4096, 14336, 8, 2, "bf16"), (512, 4096, 14336, 8, 2, "fp8_token"),
                   (128, 7168, 2048, 256, 8, "fp8_block"), (1, 4096, 14336, 8, 2, "bf16")]:
         B, stage, ks = moe.moe_select_config(*shape, cu_count=256)
-        assert B in (16, 32, 64, 128) and stage in (1, 2) and ks >= 1
+        assert B in (16, 32, 64, 128, 256) and stage in (1, 2) and ks >= 1
     with pytest.raises(moe.MoeError):
         moe.moe_select_config(4, 100, 256, 4, 2, "bf16", cu_count=256)
