@@ -19,12 +19,18 @@
 #ifndef MOE_G2_CT
 #define MOE_G2_CT 4
 #endif
-// rows per tiled-kernel tile (0: the library's choice)
+// tiled-kernel tile shape: rows and weight rows (0: the library's choice)
 #ifndef MOE_G1_BM
 #define MOE_G1_BM 0
 #endif
 #ifndef MOE_G2_BM
 #define MOE_G2_BM 0
+#endif
+#ifndef MOE_G1_TN
+#define MOE_G1_TN 0
+#endif
+#ifndef MOE_G2_TN
+#define MOE_G2_TN 0
 #endif
 
 namespace moe {
@@ -34,8 +40,9 @@ bool stream_gemm2_supported(const GemmShape &sh);
 hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s);
 hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream_t s);
 bool tiled_gemm_supported(const GemmShape &sh);
-hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, hipStream_t s);
-hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int ksplit, hipStream_t s);
+int tiled_tile_cols(int B, int quant, bool gemm1, int bm, int tn);
+hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s);
+hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hipStream_t s);
 }  // namespace moe
 
 using namespace moe;
@@ -127,7 +134,7 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
     const int64_t blocks = std::min<int64_t>(max_blocks(T, k, E, B), std::min<int64_t>(E, rows) + rows / B);
     int64_t ntiles;
     if (use_tiled(B)) {
-        ntiles = d / 256;
+        ntiles = d / tiled_tile_cols(B, quant, false, MOE_G2_BM, MOE_G2_TN);
     } else {
         const int CT = (d % 256 == 0) ? 4 : 2;
         ntiles = d / (64 * CT);
@@ -143,9 +150,13 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
 // kernels. With many rows per expert, bf16 takes 256-row blocks, whose
 // 256 x 256 gate/up tiles need a third fewer operand bytes per MFMA than
 // 128 x 256 tiles (measured: Mixtral prefill GEMM1 -8%, GEMM2 unchanged).
+// e4m3 takes 256-row blocks from about 100 rows per expert on: its 256 x 128
+// tiles then read each expert's weights once, and the MFMAs of padding-only
+// row quarters are skipped.
 int choose_B(int T, int E, int k, int quant) {
     const double rows = (double)T * k / E;
     if (quant == 0 && rows >= 512) return 256;
+    if (quant == 1 && rows >= 96) return 256;
     if (quant != 2 && rows >= 96) return 128;
     if (quant != 2 && rows >= 48) return 64;
     if (rows <= 4) return 16;
@@ -217,9 +228,7 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     if (use_tiled(B)) {
         if (!tiled_gemm_supported(g.sh))
             return fail(MOE_ERR_UNSUPPORTED, "no tiled GEMM1 kernel for B=%d quant=%d d=%d", B, quant, d);
-        // bf16 256-row blocks run as 256-row gate/up tiles
-        const int bm = MOE_G1_BM > 0 ? MOE_G1_BM : (quant == 0 && B == 256 ? 256 : 128);
-        HIP_TRY(launch_tiled_gemm1(g, bm, s), "GEMM1 launch");
+        HIP_TRY(launch_tiled_gemm1(g, MOE_G1_BM, MOE_G1_TN, s), "GEMM1 launch");
     } else {
         if (!stream_gemm1_supported(g.sh))
             return fail(MOE_ERR_UNSUPPORTED, "no GEMM1 kernel for B=%d", B);
@@ -257,7 +266,7 @@ int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, c
         return fail(MOE_ERR_UNSUPPORTED, "no GEMM2 kernel for B=%d quant=%d d=%d", B, quant, d);
     if (!acc_zeroed) HIP_TRY(launch_fill_f32(acc, (size_t)T * d, 0.0f, s), "fill launch");
     if (tiled)
-        HIP_TRY(launch_tiled_gemm2(g, MOE_G2_BM, ksplit, s), "GEMM2 launch");
+        HIP_TRY(launch_tiled_gemm2(g, MOE_G2_BM, MOE_G2_TN, ksplit, s), "GEMM2 launch");
     else
         HIP_TRY(launch_stream_gemm2(g, MOE_G2_CT, ksplit, s), "GEMM2 launch");
     HIP_TRY(launch_finalize(acc, static_cast<uint16_t *>(out), (size_t)T * d, s), "finalize launch");

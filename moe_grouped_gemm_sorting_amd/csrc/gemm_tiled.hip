@@ -16,8 +16,9 @@
 // Operand staging: gfx950's global_load_lds_dwordx4 moves 16 bytes per lane
 // from global memory straight into LDS (lane l's bytes land at M0 + 16 l), so
 // no registers or LDS-store instructions carry the operands. Three LDS stages
-// form a ring: while step j is multiplied out of one stage, the loads of
-// steps j+1 and j+2 are in flight into the other two, one barrier per step.
+// (two for 256-row tiles) form a ring: while step j is multiplied out of one
+// stage, the loads of the next steps are in flight into the others, one
+// barrier per step.
 // The loads are issued from inline assembly, with the vmcnt waits written out,
 // because the compiler, which cannot tell the stages apart, would otherwise
 // wait for every outstanding load at each barrier.
@@ -48,18 +49,19 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int TILE_N = 256;     // weight rows per workgroup
-constexpr int ROWB = 128;       // bytes per row per K step
 constexpr int WAVES = 8;
 constexpr int NTHR = 64 * WAVES;
-constexpr int HROW = 272;       // bytes per row of the staged h tile (256 + 16 against bank conflicts)
 #ifndef MOE_GROUP_M
 #define MOE_GROUP_M 8
 #endif
 constexpr int GROUP_M = MOE_GROUP_M;  // sort blocks per tile group
-#ifndef MOE_TILED_SCHED
-#define MOE_TILED_SCHED 0
+constexpr int ROWB = 128;       // bytes per row per K step
+// K rotation: bit 2q for GEMM1 of quant q, bit 2q+1 for GEMM2
+#ifndef MOE_TILED_ROTATE
+#define MOE_TILED_ROTATE 0xC
 #endif
+constexpr int CH = ROWB / 16;   // 16-byte chunks per row segment
+// bytes per row per K step for 128- and 256-row tiles
 
 struct TiledParams {
     const uint8_t *a;
@@ -74,15 +76,15 @@ struct TiledParams {
     float *out_scale;
     int T, d, f, k, B;
     int kchunk;
+    int rotate;     // start each tile's K loop at a step that depends on its column tile
     float *zero;
     size_t zero_n;
 };
 
 // Chunk position of (row, chunk) inside the row's 128 bytes (an involution
-// in chunk). A fragment read takes one chunk column of consecutive rows: any
-// 8 consecutive rows land on 8 different positions (32-bank LDS, 8 lanes per
-// cycle) and any 16 on 16 different (row parity, position) pairs (64 banks,
-// 16 lanes per cycle).
+// in chunk). A fragment read takes one chunk column of 16 consecutive rows
+// per LDS cycle (64 banks of 4 bytes = 16 chunks), which land on 16
+// different (row parity, position) pairs.
 __device__ __forceinline__ int swz(int row, int chunk) {
     return chunk ^ (row & 7) ^ ((row >> 3) & 1);
 }
@@ -126,20 +128,25 @@ __device__ __forceinline__ f32x16 mma32_fp8(const u32x4 &a0, const u32x4 &a1, co
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
 }
 
-// BM: rows per tile (64 or 128). QUANT 0 (bf16) or 1 (e4m3, per-row
-// activation scale and per-channel weight scale applied in the epilogue).
-template <int QUANT, bool GEMM1, int BM>
+// BM: rows per tile (64, 128 or 256); TN: weight rows per tile (256, or 128
+// for 256-row tiles; GEMM1 takes TN/2 gate rows and the TN/2 matching up
+// rows). QUANT 0 (bf16) or 1 (e4m3, per-row activation scale and
+// per-channel weight scale applied in the epilogue). The 8 waves form a
+// WM x WN grid, each wave owning (BM / WM) rows x 64 weight rows.
+template <int QUANT, bool GEMM1, int BM, int TN>
 __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
     constexpr int ES = QUANT == 0 ? 2 : 1;
     constexpr int KS = ROWB / ES;               // K elements per step
-    constexpr int ROWS = BM + TILE_N;           // LDS rows per stage (activations first)
+    constexpr int ROWS = BM + TN;               // LDS rows per stage (activations first)
     constexpr int BUF = ROWS * ROWB;            // bytes per stage
-    constexpr int NQ = ROWS / 8 / WAVES;        // DMA instructions per wave per step
-    constexpr int NQA = BM / 8 / WAVES;         // ... of which activation rows
-    constexpr int RT = BM / 64;                 // 32-row tiles per wave
+    constexpr int NQ = BUF / 1024 / WAVES;      // DMA instructions per wave per step
+    constexpr int NQA = BM * ROWB / 1024 / WAVES;  // ... of which activation rows
+    constexpr int WN = TN / 64, WM = WAVES / WN;
+    constexpr int RT = BM / WM / 32;            // 32-row tiles per wave
     constexpr int CT = 2;                       // 32-column tiles per wave
-    constexpr int NBUF = BM >= 256 ? 2 : 3;     // LDS stages (160 KB of LDS per CU)
-    static_assert(BM % (8 * WAVES) == 0, "tile rows");
+    constexpr int NBUF = BUF <= 48 * 1024 ? 3 : 2;  // LDS stages (of 160 KB of LDS)
+    constexpr int HROW = TN + 16;               // bytes per row of the staged h tile (+16 against bank conflicts)
+    static_assert(BM % (8 * WAVES) == 0 && TN % 64 == 0 && RT >= 1, "tile shape");
     static_assert(BM * HROW <= NBUF * BUF, "h staging");
     __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * BUF];
     __shared__ __attribute__((aligned(16))) int row_tok[BM];     // token, or -1 for padding
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
     };
 
     // ---- which tile -------------------------------------------------------
-    const int ntiles = GEMM1 ? p.f / 128 : p.d / TILE_N;
+    const int ntiles = GEMM1 ? p.f / (TN / 2) : p.d / TN;
     // tiles of BM rows; the sort block B is a multiple of BM, so a tile never
     // straddles two experts
     const int nblocks = *p.num_valid / BM;
@@ -190,81 +197,125 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
     const int kbeg = blockIdx.y * p.kchunk;
     const int kend = min(K, kbeg + p.kchunk);
 
-    // ---- per-row metadata for the epilogue ---------------------------------
-    if (tid < BM) {
-        const int slot = slot0 + tid;
-        const int a = p.sorted_ids[slot];
-        const bool ok = a < sentinel;
-        row_tok[tid] = ok ? a / p.k : -1;
-        float sc = 1.0f;
-        if constexpr (GEMM1) {
-            if constexpr (QUANT == 1) sc = ok ? p.a_scale[a / p.k] : 0.0f;
-        } else {
-            sc = ok ? p.sorted_w[slot] : 0.0f;
-            if constexpr (QUANT == 1) sc *= p.a_scale[slot];
-        }
-        row_scale[tid] = sc;
-    }
+    // ---- prologue ------------------------------------------------------------
+    // Order matters: the compiler waits for its own loads with vmcnt counts
+    // that know nothing of the DMA, so every load whose result is used before
+    // the K loop is issued first; the weight DMA (which needs only the
+    // expert) goes out while they are in flight; the activation DMA, whose
+    // row addresses need the sorted ids, comes last, so that the K loop's
+    // wait counts cover exactly the DMA. Epilogue metadata stays in registers
+    // until after the K loop.
     const int lr = lane & 31, lh = lane >> 5;
-    const int wm = wave & 1, wn = wave >> 1;
+    // waves w and w + 4 share a SIMD: they get the same columns and row
+    // blocks BM/2 apart, so that when the second half of a tile is padding
+    // (whose MFMAs are skipped) every SIMD still has one busy wave
+    const int wn = wave % WN, wm = wave / WN;
+    const uint8_t *wexp = p.w + (size_t)e * Ntot * K * ES;
+
+    // Instruction i of wave w fills the stage's kilobyte w + 8 i, i.e. 8
+    // rows; lane l writes row 8 (w + 8 i) + l / 8 at chunk position l % 8,
+    // which holds the row's logical chunk swz(row, l % 8). 32-bit byte
+    // offsets from wave-uniform bases keep the address registers few (the
+    // host guarantees every operand matrix is below 4 GiB). Padding rows read
+    // token 0's row: their products are never used (each output row depends
+    // on its own A row only), and the epilogue writes zeros for them.
+    int arow_src[NQA];
+#pragma unroll
+    for (int i = 0; i < NQA; ++i) {
+        const int row = 8 * (wave + WAVES * i) + (lane >> 3);
+        arow_src[i] = GEMM1 ? p.sorted_ids[slot0 + row] : slot0 + row;
+    }
+    int meta_a = sentinel;
+    float meta_w = 0.0f, meta_s = 1.0f;
+    if (tid < BM) {
+        meta_a = p.sorted_ids[slot0 + tid];
+        if constexpr (!GEMM1) {
+            meta_w = p.sorted_w[slot0 + tid];
+            if constexpr (QUANT == 1) meta_s = p.a_scale[slot0 + tid];
+        }
+    }
     // per-channel weight scales of this lane's columns (e4m3)
     float wsc[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
         wsc[ct] = 1.0f;
         if constexpr (QUANT == 1) {
-            const int n = GEMM1 ? ct * p.f + nt * 128 + wn * 32 + lr : nt * TILE_N + wn * 64 + ct * 32 + lr;
+            const int n = GEMM1 ? ct * p.f + nt * (TN / 2) + wn * 32 + lr : nt * TN + wn * 64 + ct * 32 + lr;
             wsc[ct] = p.w_scale[(size_t)e * Ntot + n];
         }
     }
 
-    // ---- LDS DMA sources -----------------------------------------------------
-    // Instruction i of wave w fills stage rows 8 (w + 8 i) .. +7; lane l
-    // writes row 8 (w + 8 i) + l / 8 at chunk position l % 8, which holds the
-    // row's logical chunk swz(row, l % 8). 32-bit byte offsets from
-    // wave-uniform bases keep the address registers few (the host guarantees
-    // every operand matrix is below 4 GiB). Padding rows read token 0's row:
-    // their products are never used (each output row depends on its own A row
-    // only), and the epilogue writes zeros for them.
-    const uint8_t *wexp = p.w + (size_t)e * Ntot * K * ES;
     uint32_t goff[NQ];
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
+    for (int i = NQA; i < NQ; ++i) {
         const int row = 8 * (wave + WAVES * i) + (lane >> 3);
-        const int chunk = swz(row, lane & 7);
-        if (i < NQA) {
-            int src;
-            if constexpr (GEMM1) {
-                const int a = p.sorted_ids[slot0 + row];
-                src = a < sentinel ? a / p.k : 0;
-            } else {
-                src = slot0 + row;
-            }
-            goff[i] = (uint32_t)src * (uint32_t)(K * ES) + chunk * 16;
-        } else {
-            const int rb = row - BM;   // 0..255
-            const int n = GEMM1 ? (rb < 128 ? 0 : p.f - 128) + nt * 128 + rb : nt * TILE_N + rb;
-            goff[i] = (uint32_t)n * (uint32_t)(K * ES) + chunk * 16;
-        }
+        const int rb = row - BM;   // 0..TN-1
+        const int n = GEMM1 ? (rb < TN / 2 ? 0 : p.f - TN / 2) + nt * (TN / 2) + rb : nt * TN + rb;
+        goff[i] = (uint32_t)n * (uint32_t)(K * ES) + swz(row, lane & 7) * 16;
     }
     const uint32_t m0w = lds_addr(lds) + (uint32_t)wave * 1024u;
-    auto issue = [&](int buf, int kk) {
+    auto issue_part = [&](int buf, int kk, int i0, int i1) {
         const uint8_t *ab = p.a + (size_t)kk * ES;
         const uint8_t *bb = wexp + (size_t)kk * ES;
 #pragma unroll
-        for (int i = 0; i < NQ; ++i)
+        for (int i = 0; i < NQ; ++i) {
+            if (i < i0 || i >= i1) continue;
             dma16(i < NQA ? ab : bb, goff[i], m0w + (uint32_t)(buf * BUF + i * WAVES * 1024));
+        }
     };
+    auto issue = [&](int buf, int kk) { issue_part(buf, kk, 0, NQ); };
+    static_assert(NBUF <= 3, "the first K step's wait count assumes at most 3 stages");
+    const int nsteps = (kend - kbeg) / KS;
+    // K steps in the order rot, rot+1, ..., nsteps-1, 0, ..., rot-1: tiles of
+    // different column tiles then read different 128-byte columns of their
+    // weight rows at any moment, which spreads the HBM traffic over channels
+    // and banks (rows a power of two apart otherwise meet in the same ones).
+    // Tiles of one column tile keep the same order, so the sort blocks of an
+    // expert still share each weight step in L2.
+    const int rot = (p.rotate && nsteps > 0) ? nt % nsteps : 0;
+    auto kof = [&](int i) {
+        int st = min(i, nsteps - 1) + rot;
+        if (st >= nsteps) st -= nsteps;
+        return kbeg + st * KS;
+    };
+    // weight rows of the first NBUF-1 steps
+    if (nsteps > 0) {
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b) issue_part(b, kof(b), NQA, NQ);
+    }
+    // activation rows (the compiler's wait for the sorted ids is here)
+#pragma unroll
+    for (int i = 0; i < NQA; ++i) {
+        const int row = 8 * (wave + WAVES * i) + (lane >> 3);
+        int src = arow_src[i];
+        if constexpr (GEMM1) src = src < sentinel ? src / p.k : 0;
+        goff[i] = (uint32_t)src * (uint32_t)(K * ES) + swz(row, lane & 7) * 16;
+    }
+    const bool meta_ok = meta_a < sentinel;
+    const int meta_tok = meta_ok ? meta_a / p.k : -1;
+    if constexpr (GEMM1) {
+        if constexpr (QUANT == 1) meta_s = meta_ok ? p.a_scale[meta_tok] : 0.0f;
+    } else {
+        meta_s = meta_ok ? meta_w * meta_s : 0.0f;
+    }
+    if (nsteps > 0) {
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b) issue_part(b, kof(b), 0, NQA);
+    }
 
     // ---- compute assignment -------------------------------------------------
     int arow[RT], brow[CT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) arow[rt] = wm * (BM / 2) + rt * 32 + lr;
+    for (int rt = 0; rt < RT; ++rt) arow[rt] = wm * (BM / WM) + rt * 32 + lr;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
         // GEMM1: tile 0 is gate rows, tile 1 the matching up rows
-        brow[ct] = GEMM1 ? ct * 128 + wn * 32 + lr : wn * 64 + ct * 32 + lr;
+        brow[ct] = GEMM1 ? ct * (TN / 2) + wn * 32 + lr : wn * 64 + ct * 32 + lr;
     }
+    // the wave's rows hold no assignment (padding is at the end of each
+    // expert's segment, so the first row decides): skip its MFMAs
+    const bool wave_live =
+        __builtin_amdgcn_readfirstlane(p.sorted_ids[slot0 + wm * (BM / WM)]) < sentinel;
     f32x16 acc[RT][CT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -282,64 +333,42 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
             fb[ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
                                                       swz(brow[ct], chunk) * 16);
     };
-    // bf16: 4 sub-steps of K = 16 (lane half lh takes chunk 2s + lh); the
+    // bf16: CH/2 sub-steps of K = 16 (lane half lh takes chunk 2s + lh); the
     // fragments of sub-step s+1 are read while the MFMAs of sub-step s run.
-    // e4m3: 2 sub-steps of K = 64 (lane half lh takes chunks 4s + 2lh and
+    // e4m3: CH/4 sub-steps of K = 64 (lane half lh takes chunks 4s + 2lh and
     // 4s + 2lh + 1), all fragments read up front.
     auto compute = [&](int buf) {
+        if (!wave_live) return;
         const uint8_t *base = lds + buf * BUF;
         if constexpr (QUANT == 0) {
-            u32x4 fa0[RT], fb0[CT], fa1[RT], fb1[CT];
-            frags_at(base, lh, fa0, fb0);
+            constexpr int NSUB = CH / 2;
+            u32x4 fa[2][RT], fb[2][CT];
+            frags_at(base, lh, fa[0], fb[0]);
 #pragma unroll
-            for (int sub = 0; sub < 4; sub += 2) {
-                frags_at(base, 2 * (sub + 1) + lh, fa1, fb1);
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32_bf16(fa0[rt], fb0[ct], acc[rt][ct]);
-                if (sub + 2 < 4) frags_at(base, 2 * (sub + 2) + lh, fa0, fb0);
+            for (int sub = 0; sub < NSUB; ++sub) {
+                if (sub + 1 < NSUB) frags_at(base, 2 * (sub + 1) + lh, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = mma32_bf16(fa1[rt], fb1[ct], acc[rt][ct]);
+                    for (int ct = 0; ct < CT; ++ct)
+                        acc[rt][ct] = mma32_bf16(fa[sub & 1][rt], fb[sub & 1][ct], acc[rt][ct]);
             }
-#if MOE_TILED_SCHED
-            // reads of sub-step s+1 interleaved with the MFMAs of sub-step s
-            __builtin_amdgcn_sched_group_barrier(0x100, RT + CT, 0);
-#pragma unroll
-            for (int i = 0; i < 3 * RT * CT; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, RT * CT, 0);
-#endif
         } else {
-            u32x4 fa0[RT], fb0[CT], fa1[RT], fb1[CT];
-            u32x4 ga0[RT], gb0[CT], ga1[RT], gb1[CT];
-            frags_at(base, 2 * lh, fa0, fb0);
-            frags_at(base, 2 * lh + 1, fa1, fb1);
-            frags_at(base, 4 + 2 * lh, ga0, gb0);
-            frags_at(base, 4 + 2 * lh + 1, ga1, gb1);
+            constexpr int NSUB = CH / 4;
+            u32x4 fa[NSUB][2][RT], fb[NSUB][2][CT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    acc[rt][ct] = mma32_fp8(fa0[rt], fa1[rt], fb0[ct], fb1[ct], acc[rt][ct]);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    acc[rt][ct] = mma32_fp8(ga0[rt], ga1[rt], gb0[ct], gb1[ct], acc[rt][ct]);
-#if MOE_TILED_SCHED
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RT + CT), 0);
-#pragma unroll
-            for (int i = 0; i < RT * CT; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            for (int sub = 0; sub < NSUB; ++sub) {
+                frags_at(base, 4 * sub + 2 * lh, fa[sub][0], fb[sub][0]);
+                frags_at(base, 4 * sub + 2 * lh + 1, fa[sub][1], fb[sub][1]);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, RT * CT, 0);
-#endif
+#pragma unroll
+            for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        acc[rt][ct] = mma32_fp8(fa[sub][0][rt], fa[sub][1][rt], fb[sub][0][ct],
+                                                fb[sub][1][ct], acc[rt][ct]);
         }
     };
 
@@ -351,12 +380,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
     // Unrolled by S so that the stage offsets are constants; loads past the
     // end are clamped to the last step, which keeps the wait counts exact and
     // lands in a stage nobody reads.
-    const int nsteps = (kend - kbeg) / KS;
     if (nsteps > 0) {
-        auto kof = [&](int i) { return kbeg + min(i, nsteps - 1) * KS; };
-#pragma unroll
-        for (int b = 0; b < NBUF - 1; ++b) issue(b, kof(b));
-        wait_vmem<NQ * (NBUF - 2)>();
+        // stage 0 has landed once only the activation rows of the later
+        // prologue stages are pending (everything older has completed)
+        wait_vmem<NQA * (NBUF - 2)>();
         __syncthreads();
         auto step = [&](int j, int b) {
             issue((b + NBUF - 1) % NBUF, kof(j + NBUF - 1));
@@ -373,6 +400,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
         for (int b = 0; b < NBUF - 1; ++b)
             if (j + b < nsteps) step(j + b, b);
     }
+    if (tid < BM) {
+        row_tok[tid] = meta_tok;
+        row_scale[tid] = meta_s;
+    }
     wait_vmem<0>();
     __syncthreads();   // the clamped loads have landed; metadata is visible
 
@@ -386,7 +417,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int row0 = wm * (BM / 2) + rt * 32 + 8 * q + 4 * lh;
+                const int row0 = wm * (BM / WM) + rt * 32 + 8 * q + 4 * lh;
                 const int4 tok4 = *reinterpret_cast<const int4 *>(&row_tok[row0]);
                 float4 sc4 = make_float4(1.f, 1.f, 1.f, 1.f);
                 if constexpr (QUANT == 1) sc4 = *reinterpret_cast<const float4 *>(&row_scale[row0]);
@@ -405,13 +436,14 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
             }
         }
         __syncthreads();
-        // 16 lanes per row, 16 bytes each: the tile's 256-byte row segments
+        // TN/16 lanes per row, 16 bytes each: the tile's TN-byte row segments
+        constexpr int RC = TN / 16;
         uint8_t *h = reinterpret_cast<uint8_t *>(p.out);
 #pragma unroll
-        for (int it = 0; it < BM * 16 / NTHR; ++it) {
-            const int idx = tid + NTHR * it, row = idx >> 4, c = idx & 15;
+        for (int it = 0; it < BM * RC / NTHR; ++it) {
+            const int idx = tid + NTHR * it, row = idx / RC, c = idx % RC;
             const u32x4 val = *reinterpret_cast<const u32x4 *>(hs + row * HROW + c * 16);
-            *reinterpret_cast<u32x4 *>(h + ((size_t)(slot0 + row) * p.f + nt * 128) * 2 + c * 16) = val;
+            *reinterpret_cast<u32x4 *>(h + ((size_t)(slot0 + row) * p.f + nt * (TN / 2)) * 2 + c * 16) = val;
             if constexpr (QUANT == 1) {
                 float m = 0.0f;
 #pragma unroll
@@ -420,7 +452,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
                     m = fmaxf(m, fabsf(bf16_bits_to_f32(val[w] >> 16)));
                 }
 #pragma unroll
-                for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                for (int o = 1; o < RC; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
                 if (c == 0) atomic_max_nonneg(p.out_scale + slot0 + row, m);
             }
         }
@@ -430,7 +462,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int row0 = wm * (BM / 2) + rt * 32 + 8 * q + 4 * lh;
+                const int row0 = wm * (BM / WM) + rt * 32 + 8 * q + 4 * lh;
                 const int4 tok4 = *reinterpret_cast<const int4 *>(&row_tok[row0]);
                 const float4 sc4 = *reinterpret_cast<const float4 *>(&row_scale[row0]);
                 const int tk[4] = {tok4.x, tok4.y, tok4.z, tok4.w};
@@ -438,7 +470,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (tk[i] < 0) continue;
-                    float *dst = accg + (size_t)tk[i] * p.d + nt * TILE_N + wn * 64 + lr;
+                    float *dst = accg + (size_t)tk[i] * p.d + nt * TN + wn * 64 + lr;
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         atomic_add_f32(dst + ct * 32, sw[i] * (acc[rt][ct][4 * q + i] * wsc[ct]));
@@ -450,22 +482,24 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
 }
 
 template <int QUANT, bool GEMM1>
-hipError_t dispatch_bm(const TiledParams &p, int BM, dim3 grid, hipStream_t s) {
-    if (BM == 64)
-        k_gemm_tiled<QUANT, GEMM1, 64><<<grid, NTHR, 0, s>>>(p);
-    else if (BM == 128)
-        k_gemm_tiled<QUANT, GEMM1, 128><<<grid, NTHR, 0, s>>>(p);
-    else if (QUANT == 0 && BM == 256)
-        k_gemm_tiled<0, GEMM1, 256><<<grid, NTHR, 0, s>>>(p);
+hipError_t dispatch_shape(const TiledParams &p, int BM, int TN, dim3 grid, hipStream_t s) {
+    if (BM == 64 && TN == 256)
+        k_gemm_tiled<QUANT, GEMM1, 64, 256><<<grid, NTHR, 0, s>>>(p);
+    else if (BM == 128 && TN == 256)
+        k_gemm_tiled<QUANT, GEMM1, 128, 256><<<grid, NTHR, 0, s>>>(p);
+    else if (BM == 256 && TN == 128)
+        k_gemm_tiled<QUANT, GEMM1, 256, 128><<<grid, NTHR, 0, s>>>(p);
+    else if (QUANT == 0 && BM == 256 && TN == 256)
+        k_gemm_tiled<0, GEMM1, 256, 256><<<grid, NTHR, 0, s>>>(p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 template <bool GEMM1>
-hipError_t dispatch(const TiledParams &p, int quant, int BM, dim3 grid, hipStream_t s) {
-    if (quant == 0) return dispatch_bm<0, GEMM1>(p, BM, grid, s);
-    if (quant == 1) return dispatch_bm<1, GEMM1>(p, BM, grid, s);
+hipError_t dispatch(const TiledParams &p, int quant, int BM, int TN, dim3 grid, hipStream_t s) {
+    if (quant == 0) return dispatch_shape<0, GEMM1>(p, BM, TN, grid, s);
+    if (quant == 1) return dispatch_shape<1, GEMM1>(p, BM, TN, grid, s);
     return hipErrorInvalidValue;
 }
 
@@ -481,15 +515,33 @@ bool tiled_gemm_supported(const GemmShape &sh) {
            sh.f % 128 == 0 && sh.d % 256 == 0;
 }
 
-// Rows per kernel tile: 64, 128 or (bf16) 256, a divisor of the sort block
-// B; other values pick min(B, 128).
-int tile_rows(int B, int bm, int quant) {
-    const int maxbm = quant == 0 ? 256 : 128;
-    if (bm <= 0 || bm > B || B % bm || bm > maxbm) bm = B < 128 ? B : 128;
-    return bm;
+// Tile shape (rows BM, weight rows TN) for sort blocks of B rows; bm / tn
+// > 0 request a shape, which must be one of the instantiated ones and BM must
+// divide B. The library's choice: a 64/128-row block is one 64/128 x 256 tile;
+// a 256-row block runs bf16 gate/up as 256 x 256 tiles (a third fewer
+// operand bytes per MFMA than 128 x 256), bf16 down as two 128 x 256 tiles,
+// and e4m3 as 256 x 128 tiles (whose weight columns each cover a whole
+// expert of up to 256 rows, so every weight byte leaves HBM once).
+struct TileShape {
+    int bm, tn;
+};
+
+TileShape tile_shape(int B, int quant, bool gemm1, int bm, int tn) {
+    auto valid = [&](int m, int n) {
+        if (m <= 0 || m > B || B % m) return false;
+        return (n == 256 && (m == 64 || m == 128 || (m == 256 && quant == 0))) || (n == 128 && m == 256);
+    };
+    if (valid(bm, tn)) return {bm, tn};
+    if (B < 256) return {B, 256};
+    if (quant == 1) return {256, 128};
+    return gemm1 ? TileShape{256, 256} : TileShape{128, 256};
 }
 
-hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, hipStream_t s) {
+int tiled_tile_cols(int B, int quant, bool gemm1, int bm, int tn) {
+    return tile_shape(B, quant, gemm1, bm, tn).tn;
+}
+
+hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s) {
     const GemmShape &sh = g.sh;
     TiledParams p{};
     p.a = static_cast<const uint8_t *>(g.a);
@@ -503,16 +555,17 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, hipStream_t s) {
     p.out_scale = g.h_scale;
     p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
     p.kchunk = sh.d;
+    p.rotate = MOE_TILED_ROTATE & (1 << (2 * sh.quant));
     p.zero = g.zero;
     p.zero_n = g.zero_n;
-    bm = tile_rows(sh.B, bm, sh.quant);
+    const TileShape ts = tile_shape(sh.B, sh.quant, true, bm, tn);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
-    const int NB = (P + bm - 1) / bm;
-    const dim3 grid(grid_tiles(NB, sh.f / 128), 1);
-    return dispatch<true>(p, sh.quant, bm, grid, s);
+    const int NB = (P + ts.bm - 1) / ts.bm;
+    const dim3 grid(grid_tiles(NB, sh.f / (ts.tn / 2)), 1);
+    return dispatch<true>(p, sh.quant, ts.bm, ts.tn, grid, s);
 }
 
-hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int ksplit, hipStream_t s) {
+hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hipStream_t s) {
     const GemmShape &sh = g.sh;
     TiledParams p{};
     p.a = static_cast<const uint8_t *>(g.h);
@@ -531,12 +584,13 @@ hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int ksplit, hipStream_
     if (ksplit > steps) ksplit = steps;
     const int steps_per = (steps + ksplit - 1) / ksplit;
     p.kchunk = steps_per * KS;
+    p.rotate = MOE_TILED_ROTATE & (2 << (2 * sh.quant));
     ksplit = (steps + steps_per - 1) / steps_per;
-    bm = tile_rows(sh.B, bm, sh.quant);
+    const TileShape ts = tile_shape(sh.B, sh.quant, false, bm, tn);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
-    const int NB = (P + bm - 1) / bm;
-    const dim3 grid(grid_tiles(NB, sh.d / TILE_N), ksplit);
-    return dispatch<false>(p, sh.quant, bm, grid, s);
+    const int NB = (P + ts.bm - 1) / ts.bm;
+    const dim3 grid(grid_tiles(NB, sh.d / ts.tn), ksplit);
+    return dispatch<false>(p, sh.quant, ts.bm, ts.tn, grid, s);
 }
 
 }  // namespace moe
