@@ -40,6 +40,7 @@ struct StreamParams {
     float *out_scale;        // GEMM1 quant 1: row amax [P]; quant 2: h_scale [P, f/128]
     int T, d, f, k, B;
     int kchunk;              // K elements per blockIdx.y
+    int rotate;              // start the K loop at a step given by the column tile
     float *zero;             // optional fp32 buffer cleared by the grid on the way
     size_t zero_n;           // its length (a multiple of 4)
 };
@@ -56,6 +57,10 @@ struct Frag {
 
 #ifndef MOE_STREAM_NT
 #define MOE_STREAM_NT 0
+#endif
+// K rotation: bit 0 GEMM1, bit 1 GEMM2
+#ifndef MOE_STREAM_ROTATE
+#define MOE_STREAM_ROTATE 1
 #endif
 
 __device__ __forceinline__ Frag load_frag(const uint8_t *p) {
@@ -129,7 +134,8 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t
                                              const bool (&arow_ok)[RT],
                                              const uint8_t *const (&wrow)[NT],
                                              const float *const (&sap)[RT][4],
-                                             const float *const (&swp)[NT], int kbeg, int kend) {
+                                             const float *const (&swp)[NT], int kbeg, int kend,
+                                             int rot) {
     constexpr int ES = Elem<QUANT>::bytes;
     constexpr int KS = Elem<QUANT>::kstep;
     constexpr int DEPTH = MOE_STREAM_DEPTH;
@@ -170,7 +176,12 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t
     // hit the cache.
     const int nsteps = (kend - kbeg) / KS;
     if (nsteps <= 0) return;
-    auto kof = [&](int i) { return kbeg + min(i, nsteps - 1) * KS; };
+    rot %= nsteps;
+    auto kof = [&](int i) {
+        int st = min(i, nsteps - 1) + rot;
+        if (st >= nsteps) st -= nsteps;
+        return kbeg + st * KS;
+    };
 #pragma unroll
     for (int s = 0; s < DEPTH - 1; ++s) load(bf[s], kof(s));
     int i = 0;
@@ -286,10 +297,13 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
             swp[nt] = p.w_scale + ((size_t)e * (Ntot / 128) + nrow / 128) * (K / 128);
         }
     }
+    // K steps start at a step given by the column tile: weight rows a power
+    // of two apart otherwise meet in the same HBM channels at the same moment
+    const int rot = p.rotate ? (int)blockIdx.x : 0;
     if (RT == 2 && live[RT - 1])
-        stream_kloop<QUANT, RT, RT, NT>(acc, arow, arow_ok, wrow, sap, swp, kbeg, kend);
+        stream_kloop<QUANT, RT, RT, NT>(acc, arow, arow_ok, wrow, sap, swp, kbeg, kend, rot);
     else
-        stream_kloop<QUANT, RT, 1, NT>(acc, arow, arow_ok, wrow, sap, swp, kbeg, kend);
+        stream_kloop<QUANT, RT, 1, NT>(acc, arow, arow_ok, wrow, sap, swp, kbeg, kend, rot);
 
     // ------------------------------------------------------------ epilogue
     if constexpr (GEMM1) {
@@ -438,6 +452,7 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
     p.out_scale = g.h_scale;
     p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
     p.kchunk = sh.d;
+    p.rotate = MOE_STREAM_ROTATE & 1;
     p.zero = g.zero;
     p.zero_n = g.zero_n;
     if (sh.quant == 2) CT = 2;  // one 128-column quant block per workgroup
@@ -466,6 +481,7 @@ hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream
     if (ksplit > steps) ksplit = steps;
     const int steps_per = (steps + ksplit - 1) / ksplit;
     p.kchunk = steps_per * KS;
+    p.rotate = MOE_STREAM_ROTATE & 2;
     ksplit = (steps + steps_per - 1) / steps_per;
     const int RT = sh.B / 16;
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
