@@ -27,6 +27,10 @@ SMALL = [
     workloads.Workload("single_token", T=1, d=256, f=256, E=8, k=2, seed=27),
     workloads.Workload("tiled_bf16", T=300, d=512, f=384, E=4, k=2, seed=29),
     workloads.Workload("tiled_fp8", T=260, d=768, f=256, E=3, k=2, quant="fp8_token", seed=30),
+    # 400 rows per expert: a second, partly padded 256-row block (padding row quarters skip
+    # their MFMAs in the 256-row tiles)
+    workloads.Workload("spill_bf16", T=400, d=512, f=384, E=2, k=2, seed=31),
+    workloads.Workload("spill_fp8", T=400, d=512, f=384, E=2, k=2, quant="fp8_token", seed=32),
 ]
 
 
