@@ -31,7 +31,14 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// z * sigmoid(z) from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32; about 1 ulp each): the relative error, near 1e-6,
+// is far below the bf16 rounding that follows. exp2 overflowing to +inf for
+// very negative z gives 1/inf = 0, the limit.
+__device__ __forceinline__ float silu(float z) {
+    constexpr float kLog2e = 1.44269504088896341f;
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
 
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {

@@ -49,8 +49,6 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int WAVES = 8;
-constexpr int NTHR = 64 * WAVES;
 #ifndef MOE_GROUP_M
 #define MOE_GROUP_M 8
 #endif
@@ -133,8 +131,9 @@ __device__ __forceinline__ f32x16 mma32_fp8(const u32x4 &a0, const u32x4 &a1, co
 // rows). QUANT 0 (bf16) or 1 (e4m3, per-row activation scale and
 // per-channel weight scale applied in the epilogue). The 8 waves form a
 // WM x WN grid, each wave owning (BM / WM) rows x 64 weight rows.
-template <int QUANT, bool GEMM1, int BM, int TN>
-__global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
+template <int QUANT, bool GEMM1, int BM, int TN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
+    constexpr int NTHR = 64 * WAVES;
     constexpr int ES = QUANT == 0 ? 2 : 1;
     constexpr int KS = ROWB / ES;               // K elements per step
     constexpr int ROWS = BM + TN;               // LDS rows per stage (activations first)
@@ -144,9 +143,11 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
     constexpr int WN = TN / 64, WM = WAVES / WN;
     constexpr int RT = BM / WM / 32;            // 32-row tiles per wave
     constexpr int CT = 2;                       // 32-column tiles per wave
-    constexpr int NBUF = BUF <= 48 * 1024 ? 3 : 2;  // LDS stages (of 160 KB of LDS)
+    // LDS stages (of 160 KB of LDS); 4-wave workgroups take two stages so
+    // that two of them share a CU
+    constexpr int NBUF = WAVES == 4 ? 2 : BUF <= 48 * 1024 ? 3 : 2;
     constexpr int HROW = TN + 16;               // bytes per row of the staged h tile (+16 against bank conflicts)
-    static_assert(BM % (8 * WAVES) == 0 && TN % 64 == 0 && RT >= 1, "tile shape");
+    static_assert(BM % (8 * WAVES) == 0 && TN % 64 == 0 && RT >= 1 && BM <= NTHR, "tile shape");
     static_assert(BM * HROW <= NBUF * BUF, "h staging");
     __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * BUF];
     __shared__ __attribute__((aligned(16))) int row_tok[BM];     // token, or -1 for padding
@@ -484,13 +485,15 @@ __global__ __launch_bounds__(NTHR) void k_gemm_tiled(TiledParams p) {
 template <int QUANT, bool GEMM1>
 hipError_t dispatch_shape(const TiledParams &p, int BM, int TN, dim3 grid, hipStream_t s) {
     if (BM == 64 && TN == 256)
-        k_gemm_tiled<QUANT, GEMM1, 64, 256><<<grid, NTHR, 0, s>>>(p);
+        k_gemm_tiled<QUANT, GEMM1, 64, 256, 8><<<grid, 512, 0, s>>>(p);
     else if (BM == 128 && TN == 256)
-        k_gemm_tiled<QUANT, GEMM1, 128, 256><<<grid, NTHR, 0, s>>>(p);
+        k_gemm_tiled<QUANT, GEMM1, 128, 256, 8><<<grid, 512, 0, s>>>(p);
     else if (BM == 256 && TN == 128)
-        k_gemm_tiled<QUANT, GEMM1, 256, 128><<<grid, NTHR, 0, s>>>(p);
+        k_gemm_tiled<QUANT, GEMM1, 256, 128, 8><<<grid, 512, 0, s>>>(p);
+    else if (BM == 128 && TN == 128)
+        k_gemm_tiled<QUANT, GEMM1, 128, 128, 4><<<grid, 256, 0, s>>>(p);
     else if (QUANT == 0 && BM == 256 && TN == 256)
-        k_gemm_tiled<0, GEMM1, 256, 256><<<grid, NTHR, 0, s>>>(p);
+        k_gemm_tiled<0, GEMM1, 256, 256, 8><<<grid, 512, 0, s>>>(p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -529,7 +532,8 @@ struct TileShape {
 TileShape tile_shape(int B, int quant, bool gemm1, int bm, int tn) {
     auto valid = [&](int m, int n) {
         if (m <= 0 || m > B || B % m) return false;
-        return (n == 256 && (m == 64 || m == 128 || (m == 256 && quant == 0))) || (n == 128 && m == 256);
+        return (n == 256 && (m == 64 || m == 128 || (m == 256 && quant == 0))) ||
+               (n == 128 && (m == 128 || m == 256));
     };
     if (valid(bm, tn)) return {bm, tn};
     if (B < 256) return {B, 256};
