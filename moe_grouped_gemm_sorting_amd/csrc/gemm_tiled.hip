@@ -143,9 +143,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     constexpr int WN = TN / 64, WM = WAVES / WN;
     constexpr int RT = BM / WM / 32;            // 32-row tiles per wave
     constexpr int CT = 2;                       // 32-column tiles per wave
-    // LDS stages (of 160 KB of LDS); 4-wave workgroups take two stages so
-    // that two of them share a CU
-    constexpr int NBUF = WAVES == 4 ? 2 : BUF <= 48 * 1024 ? 3 : 2;
+    constexpr int NBUF = BUF <= 48 * 1024 ? 3 : 2;  // LDS stages (of 160 KB of LDS)
     constexpr int HROW = TN + 16;               // bytes per row of the staged h tile (+16 against bank conflicts)
     static_assert(BM % (8 * WAVES) == 0 && TN % 64 == 0 && RT >= 1 && BM <= NTHR, "tile shape");
     static_assert(BM * HROW <= NBUF * BUF, "h staging");
@@ -490,8 +488,6 @@ hipError_t dispatch_shape(const TiledParams &p, int BM, int TN, dim3 grid, hipSt
         k_gemm_tiled<QUANT, GEMM1, 128, 256, 8><<<grid, 512, 0, s>>>(p);
     else if (BM == 256 && TN == 128)
         k_gemm_tiled<QUANT, GEMM1, 256, 128, 8><<<grid, 512, 0, s>>>(p);
-    else if (BM == 128 && TN == 128)
-        k_gemm_tiled<QUANT, GEMM1, 128, 128, 4><<<grid, 256, 0, s>>>(p);
     else if (QUANT == 0 && BM == 256 && TN == 256)
         k_gemm_tiled<0, GEMM1, 256, 256, 8><<<grid, 512, 0, s>>>(p);
     else
@@ -532,8 +528,7 @@ struct TileShape {
 TileShape tile_shape(int B, int quant, bool gemm1, int bm, int tn) {
     auto valid = [&](int m, int n) {
         if (m <= 0 || m > B || B % m) return false;
-        return (n == 256 && (m == 64 || m == 128 || (m == 256 && quant == 0))) ||
-               (n == 128 && (m == 128 || m == 256));
+        return (n == 256 && (m == 64 || m == 128 || (m == 256 && quant == 0))) || (n == 128 && m == 256);
     };
     if (valid(bm, tn)) return {bm, tn};
     if (B < 256) return {B, 256};
