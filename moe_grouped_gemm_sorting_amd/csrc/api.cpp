@@ -128,8 +128,8 @@ struct Config {
 bool use_tiled(int B) { return B >= 64; }
 
 int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
-    // about two workgroups per CU in the down projection (measured best on
-    // the Mixtral decode shape: 4 splits of K = 14336)
+    // the streaming kernel: about two workgroups per CU in the down projection
+    // (measured best on the Mixtral decode shape: 4 splits of K = 14336)
     const int64_t rows = (int64_t)T * k;
     const int64_t blocks = std::min<int64_t>(max_blocks(T, k, E, B), std::min<int64_t>(E, rows) + rows / B);
     int64_t ntiles;
@@ -141,7 +141,10 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
     }
     const int64_t base = std::max<int64_t>(1, ntiles * blocks);
     const int KS = quant == 0 ? 64 : 128;
-    int ks = (int)std::min<int64_t>((2 * (int64_t)cu + base - 1) / base, f / KS / 4);
+    // the tiled kernel holds one workgroup per CU: split only when there are
+    // fewer tiles than CUs (without a split, rows are stored, not added)
+    const int64_t target = use_tiled(B) ? cu : 2 * (int64_t)cu;
+    int ks = (int)std::min<int64_t>((target + base - 1) / base, f / KS / 4);
     return std::max(1, ks);
 }
 
@@ -241,7 +244,17 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     return MOE_OK;
 }
 
-float *carve_gemm2(Carver &c, int T, int d) { return c.take<float>((size_t)T * d); }
+// GEMM2's fp32 buffer: the token accumulator [T, d], or, for the tiled
+// kernel without K-split, the weighted rows by assignment [T*k, d] (the
+// larger of the two, so that one layout serves both).
+float *carve_gemm2(Carver &c, int T, int d, int k, int B) {
+    return c.take<float>((size_t)T * d * (use_tiled(B) ? k : 1));
+}
+
+// The tiled down projection without K-split stores each weighted row once
+// and a combine kernel sums each token's k rows: no atomics, no accumulator
+// clearing, and a fixed summation order.
+bool stored_rows(int B, int ksplit) { return use_tiled(B) && ksplit == 1; }
 
 int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, const void *h,
               const float *h_scale, const void *w2, const float *w2_scale,
@@ -264,6 +277,13 @@ int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, c
     const bool tiled = use_tiled(B);
     if (tiled ? !tiled_gemm_supported(g.sh) : !stream_gemm2_supported(g.sh))
         return fail(MOE_ERR_UNSUPPORTED, "no GEMM2 kernel for B=%d quant=%d d=%d", B, quant, d);
+    if (stored_rows(B, ksplit)) {
+        g.acc = nullptr;
+        g.yrows = acc;
+        HIP_TRY(launch_tiled_gemm2(g, MOE_G2_BM, MOE_G2_TN, 1, s), "GEMM2 launch");
+        HIP_TRY(launch_combine_rows(acc, T, k, d, static_cast<uint16_t *>(out), s), "combine launch");
+        return MOE_OK;
+    }
     if (!acc_zeroed) HIP_TRY(launch_fill_f32(acc, (size_t)T * d, 0.0f, s), "fill launch");
     if (tiled)
         HIP_TRY(launch_tiled_gemm2(g, MOE_G2_BM, MOE_G2_TN, ksplit, s), "GEMM2 launch");
@@ -302,7 +322,7 @@ FusedWs carve_fused(Carver &c, int T, int d, int f, int E, int k, int quant, int
     if (quant == 1) w.h_scale = c.take<float>(P);
     if (quant == 2) w.h_scale = c.take<float>(P * (f / 128));
     w.g1 = carve_gemm1(c, T, d, f, E, k, B, quant);
-    w.acc = carve_gemm2(c, T, d);
+    w.acc = carve_gemm2(c, T, d, k, B);
     return w;
 }
 
@@ -409,7 +429,7 @@ int moe_gemm1_swiglu(int T, int d, int f, int E, int k, int B, int quant, const 
 size_t moe_gemm2_workspace_bytes(int T, int d, int f, int E, int k, int B, int quant) {
     if (check_shape(T, d, f, E, k, B, quant) != MOE_OK) return 0;
     Carver c(nullptr);
-    carve_gemm2(c, T, d);
+    carve_gemm2(c, T, d, k, B);
     return c.bytes();
 }
 
@@ -427,12 +447,12 @@ int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int k
     if (quant != 0 && (!w2_scale || !h_scale))
         return fail(MOE_ERR_INVALID_ARG, "fp8 needs w2_scale and h_scale");
     Carver c(nullptr);
-    carve_gemm2(c, T, d);
+    carve_gemm2(c, T, d, k, B);
     if (ws_bytes < c.bytes() || (c.bytes() > 0 && !ws))
         return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, c.bytes());
     if (T == 0) return MOE_OK;
     Carver cw(ws);
-    float *acc = carve_gemm2(cw, T, d);
+    float *acc = carve_gemm2(cw, T, d, k, B);
     return run_gemm2(T, d, f, E, k, B, quant, ksplit, h, h_scale, w2, w2_scale, sorted_ids,
                      sorted_w, sorted_expert_ids, num_valid, out, acc, (hipStream_t)stream);
 }
@@ -527,8 +547,11 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
         return MOE_OK;
     }
     // GEMM1 also clears GEMM2's accumulator (same stream, so it is done first)
+    // unless GEMM2 stores whole rows
+    if (ksplit <= 0) ksplit = auto_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
+    const bool clear = !stored_rows(B, ksplit);
     rc = run_gemm1(T, d, f, E, k, B, quant, x, w13, w13_scale, w.sorted_ids, w.seid, w.num_valid,
-                   w.h, w.h_scale, w.g1, s, w.acc, (size_t)T * d);
+                   w.h, w.h_scale, w.g1, s, clear ? w.acc : nullptr, clear ? (size_t)T * d : 0);
     if (rc) return rc;
     return run_gemm2(T, d, f, E, k, B, quant, ksplit, w.h, w.h_scale, w2, w2_scale, w.sorted_ids,
                      w.sorted_w, w.seid, w.num_valid, out, w.acc, s, true);

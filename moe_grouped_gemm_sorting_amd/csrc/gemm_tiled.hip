@@ -77,6 +77,7 @@ struct TiledParams {
     int rotate;     // start each tile's K loop at a step that depends on its column tile
     float *zero;
     size_t zero_n;
+    float *yrows;   // GEMM2 without K-split: weighted rows [T*k, d] by assignment, stored (no atomics)
 };
 
 // Chunk position of (row, chunk) inside the row's 128 bytes (an involution
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     static_assert(BM % (8 * WAVES) == 0 && TN % 64 == 0 && RT >= 1 && BM <= NTHR, "tile shape");
     static_assert(BM * HROW <= NBUF * BUF, "h staging");
     __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * BUF];
-    __shared__ __attribute__((aligned(16))) int row_tok[BM];     // token, or -1 for padding
+    __shared__ __attribute__((aligned(16))) int row_asg[BM];     // assignment t*k+j, or -1 for padding
     __shared__ __attribute__((aligned(16))) float row_scale[BM];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -291,9 +292,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
         goff[i] = (uint32_t)src * (uint32_t)(K * ES) + swz(row, lane & 7) * 16;
     }
     const bool meta_ok = meta_a < sentinel;
-    const int meta_tok = meta_ok ? meta_a / p.k : -1;
+    const int meta_asg = meta_ok ? meta_a : -1;
     if constexpr (GEMM1) {
-        if constexpr (QUANT == 1) meta_s = meta_ok ? p.a_scale[meta_tok] : 0.0f;
+        if constexpr (QUANT == 1) meta_s = meta_ok ? p.a_scale[meta_a / p.k] : 0.0f;
     } else {
         meta_s = meta_ok ? meta_w * meta_s : 0.0f;
     }
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             if (j + b < nsteps) step(j + b, b);
     }
     if (tid < BM) {
-        row_tok[tid] = meta_tok;
+        row_asg[tid] = meta_asg;
         row_scale[tid] = meta_s;
     }
     wait_vmem<0>();
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row0 = wm * (BM / WM) + rt * 32 + 8 * q + 4 * lh;
-                const int4 tok4 = *reinterpret_cast<const int4 *>(&row_tok[row0]);
+                const int4 tok4 = *reinterpret_cast<const int4 *>(&row_asg[row0]);
                 float4 sc4 = make_float4(1.f, 1.f, 1.f, 1.f);
                 if constexpr (QUANT == 1) sc4 = *reinterpret_cast<const float4 *>(&row_scale[row0]);
                 const int tk[4] = {tok4.x, tok4.y, tok4.z, tok4.w};
@@ -456,23 +457,33 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             }
         }
     } else {
+        // rows weighted by routing weight (and activation scale); with
+        // yrows each row is stored at its assignment, else added atomically
+        // into the token's accumulator row
         float *accg = reinterpret_cast<float *>(p.out);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row0 = wm * (BM / WM) + rt * 32 + 8 * q + 4 * lh;
-                const int4 tok4 = *reinterpret_cast<const int4 *>(&row_tok[row0]);
+                const int4 asg4 = *reinterpret_cast<const int4 *>(&row_asg[row0]);
                 const float4 sc4 = *reinterpret_cast<const float4 *>(&row_scale[row0]);
-                const int tk[4] = {tok4.x, tok4.y, tok4.z, tok4.w};
+                const int as[4] = {asg4.x, asg4.y, asg4.z, asg4.w};
                 const float sw[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (tk[i] < 0) continue;
-                    float *dst = accg + (size_t)tk[i] * p.d + nt * TN + wn * 64 + lr;
+                    if (as[i] < 0) continue;
+                    const int col = nt * TN + wn * 64 + lr;
+                    if (p.yrows) {
+                        float *dst = p.yrows + (size_t)as[i] * p.d + col;
 #pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-                        atomic_add_f32(dst + ct * 32, sw[i] * (acc[rt][ct][4 * q + i] * wsc[ct]));
+                        for (int ct = 0; ct < CT; ++ct) dst[ct * 32] = sw[i] * (acc[rt][ct][4 * q + i] * wsc[ct]);
+                    } else {
+                        float *dst = accg + (size_t)(as[i] / p.k) * p.d + col;
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct)
+                            atomic_add_f32(dst + ct * 32, sw[i] * (acc[rt][ct][4 * q + i] * wsc[ct]));
+                    }
                 }
             }
         }
@@ -576,11 +587,13 @@ hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hi
     p.seid = g.sorted_expert_ids;
     p.num_valid = g.num_valid;
     p.out = g.acc;
+    p.yrows = g.yrows;
     p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
     const int KS = sh.quant == 0 ? 64 : 128;
     const int steps = sh.f / KS;
     if (ksplit < 1) ksplit = 1;
     if (ksplit > steps) ksplit = steps;
+    if (g.yrows) ksplit = 1;   // stored rows take the whole reduction
     const int steps_per = (steps + ksplit - 1) / ksplit;
     p.kchunk = steps_per * KS;
     p.rotate = MOE_TILED_ROTATE & (2 << (2 * sh.quant));
