@@ -14,7 +14,10 @@
 // (v_mfma_f32_16x16x32_bf16 twice, or one v_mfma_scale_f32_16x16x128_f8f6f4
 // with unit scales, per step).
 // No LDS: weights are used by exactly one workgroup, which is the decode
-// (weight-streaming, HBM-bound) regime.
+// (weight-streaming, HBM-bound) regime. GEMM1 starts each workgroup's K loop
+// at a step given by its column tile: weight rows 8 KiB apart would otherwise
+// all be read at the same 128-byte column at once, which piles the requests
+// onto the same HBM channels.
 //
 //   GEMM1: C[slot, n] over K = d, n in gate rows n0.. and up rows f + n0..,
 //          epilogue h = silu(gate) * up -> bf16 (quant 0/1) or e4m3 per
@@ -70,8 +73,9 @@ __device__ __forceinline__ Frag load_frag(const uint8_t *p) {
     return f;
 }
 
-// Weights are read once per call: nontemporal loads keep them from evicting
-// reused data (activations, h) from the caches.
+// Weight fragments. Nontemporal loads (MOE_STREAM_NT) would keep the weights,
+// read once per call, from evicting activations from the caches, but measured
+// slower; they are off.
 __device__ __forceinline__ Frag load_frag_stream(const uint8_t *p) {
 #if MOE_STREAM_NT
     Frag f;

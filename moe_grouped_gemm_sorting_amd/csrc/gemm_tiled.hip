@@ -5,13 +5,15 @@
 // entries/19116, talk summary at 5:58), run as the two stages of the AITER
 // walk-through (itsolotime.com/th/archives/32381, section 3.2).
 //
-// Workgroup tile: BM rows of one expert (BM = 64 or 128; a 256-row sort block
-// runs as two tiles) x 256 weight rows (GEMM1: 128 gate rows + the 128
-// matching up rows, so SwiGLU fuses into the epilogue; GEMM2: 256 output
-// columns), K in steps of 128 bytes per row. 8 waves in a 2 x 4 arrangement,
-// each owning (BM/2) x 64 of the tile, with v_mfma_f32_32x32x16_bf16 or, for
+// Workgroup tile: BM rows of one expert (BM = 64, 128 or 256, a divisor of
+// the sort block) x TN weight rows (TN = 256, or 128 for 256-row tiles;
+// GEMM1 takes TN/2 gate rows and the TN/2 matching up rows, so SwiGLU fuses
+// into the epilogue; GEMM2 takes TN output columns), K in steps of 128 bytes
+// per row. 8 waves in a WM x WN grid (WN = TN/64), each owning (BM/WM) x 64
+// of the tile as 32x32 accumulators, with v_mfma_f32_32x32x16_bf16 or, for
 // e4m3, v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales (per-row /
-// per-channel fp32 scales go in the epilogue).
+// per-channel fp32 scales go in the epilogue). Waves whose rows are all
+// padding skip their MFMAs.
 //
 // Operand staging: gfx950's global_load_lds_dwordx4 moves 16 bytes per lane
 // from global memory straight into LDS (lane l's bytes land at M0 + 16 l), so
@@ -35,11 +37,13 @@
 // and share its L2. The tile count comes from num_valid on the device, so
 // no XCD is left with the padding blocks.
 //
-// Epilogue: the tile's per-row metadata (destination token, routing weight,
-// activation scale) is fetched into LDS before the K loop. GEMM1 writes the
-// bf16 h tile into LDS and copies it out in 16-byte row segments (and, for
-// e4m3, takes each row's amax there with one atomic per row and tile); GEMM2
-// adds its weighted rows into the fp32 accumulator with atomics.
+// Epilogue: the tile's per-row metadata (assignment, routing weight,
+// activation scale) is loaded before the K loop and kept in registers until
+// after it. GEMM1 writes the bf16 h tile into LDS and copies it out in
+// 16-byte row segments (and, for e4m3, takes each row's amax there with one
+// atomic per row and tile). GEMM2 either stores its weighted rows at their
+// assignments (no K-split; a combine kernel sums each token's rows) or adds
+// them into the token's fp32 accumulator row with atomics.
 #include "common.h"
 #include "launch.h"
 
