@@ -31,6 +31,8 @@ SMALL = [
     # their MFMAs in the 256-row tiles)
     workloads.Workload("spill_bf16", T=400, d=512, f=384, E=2, k=2, seed=31),
     workloads.Workload("spill_fp8", T=400, d=512, f=384, E=2, k=2, quant="fp8_token", seed=32),
+    # top-8: the tiled down projection's per-token combine sums eight rows
+    workloads.Workload("top8_tiled", T=160, d=512, f=256, E=16, k=8, score="sigmoid", seed=34),
 ]
 
 
@@ -165,3 +167,25 @@ def test_one_stage_full_decode_shape_and_unsupported():
     with pytest.raises(moe.MoeError):   # per-row h quantisation needs the whole row first
         moe.fused_moe(xf, wf["w13"], wf["w2"], fp8.k, logits=lf, quant="fp8_token",
                       w13_scale=wf["w13_scale"], w2_scale=wf["w2_scale"], B=16, stage=1)
+
+
+@pytest.mark.parametrize("B", (64, 128, 256))
+def test_stored_row_combine_is_repeatable(B):
+    """Without K-split the tiled down projection stores each weighted row once
+    and sums a token's rows in a fixed order: repeated calls give the same
+    bits (the atomic K-split path only meets the tolerance)."""
+    wl = workloads.get("mixtral_prefill").replace(name="rep", T=384, f=1024, seed=35)
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    ids, w = moe.moe_topk(logits, wl.k, wl.score)
+    srt = moe.moe_sort(ids, w, wl.E, B)
+    h, hs = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, B, wl.quant, ws["w13_scale"])
+    outs = [moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B, wl.quant, ws["w2_scale"],
+                                  ksplit=1) for _ in range(3)]
+    split = moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B, wl.quant, ws["w2_scale"],
+                                  ksplit=4)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert np.array_equal(bits(o), bits(outs[0]))
+    err, _ = rel_err(bf16_to_f64(bits(split)), bf16_to_f64(bits(outs[0])))
+    assert err <= 1e-2
