@@ -136,6 +136,19 @@ __device__ __forceinline__ f32x16 mma32_fp8(const u32x4 &a0, const u32x4 &a1, co
 // rows). QUANT 0 (bf16) or 1 (e4m3, per-row activation scale and
 // per-channel weight scale applied in the epilogue). The 8 waves form a
 // WM x WN grid, each wave owning (BM / WM) rows x 64 weight rows.
+template <int I>
+struct IC {
+    static constexpr int value = I;
+};
+// f(IC<0>{}), ..., f(IC<N-1>{})
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(IC<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 template <int QUANT, bool GEMM1, int BM, int TN, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     constexpr int NTHR = 64 * WAVES;
@@ -229,6 +242,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
         const int row = 8 * (wave + WAVES * i) + (lane >> 3);
         arow_src[i] = GEMM1 ? p.sorted_ids[slot0 + row] : slot0 + row;
     }
+    // live 32-row groups of the tile: padding sits at the end of the
+    // expert's segment, so they form a prefix (bit g: row 32 g is real)
+    const uint64_t live32 =
+        __ballot(lane < BM / 32 && p.sorted_ids[slot0 + 32 * min(lane, BM / 32 - 1)] < sentinel);
     int meta_a = sentinel;
     float meta_w = 0.0f, meta_s = 1.0f;
     if (tid < BM) {
@@ -267,7 +284,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             dma16(i < NQA ? ab : bb, goff[i], m0w + (uint32_t)(buf * BUF + i * WAVES * 1024));
         }
     };
-    auto issue = [&](int buf, int kk) { issue_part(buf, kk, 0, NQ); };
     static_assert(NBUF <= 3, "the first K step's wait count assumes at most 3 stages");
     const int nsteps = (kend - kbeg) / KS;
     // K steps in the order rot, rot+1, ..., nsteps-1, 0, ..., rot-1: tiles of
@@ -302,10 +318,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     } else {
         meta_s = meta_ok ? meta_w * meta_s : 0.0f;
     }
-    if (nsteps > 0) {
-#pragma unroll
-        for (int b = 0; b < NBUF - 1; ++b) issue_part(b, kof(b), 0, NQA);
-    }
 
     // ---- compute assignment -------------------------------------------------
     int arow[RT], brow[CT];
@@ -318,8 +330,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     }
     // the wave's rows hold no assignment (padding is at the end of each
     // expert's segment, so the first row decides): skip its MFMAs
-    const bool wave_live =
-        __builtin_amdgcn_readfirstlane(p.sorted_ids[slot0 + wm * (BM / WM)]) < sentinel;
+    const bool wave_live = (live32 >> (wm * (BM / WM) / 32)) & 1;
     f32x16 acc[RT][CT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -384,15 +395,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // Unrolled by S so that the stage offsets are constants; loads past the
     // end are clamped to the last step, which keeps the wait counts exact and
     // lands in a stage nobody reads.
-    if (nsteps > 0) {
+    // Activation load i of every wave covers rows [64 i, 64 i + 64) of the
+    // tile, so only the first NQAL = ceil(real rows / 64) of them carry real
+    // rows; the others are not issued. Their LDS rows keep stale bytes, which
+    // reach only the accumulators of padding rows (never stored). The loop
+    // is instantiated per NQAL so that every wait count stays a constant.
+    auto kloop = [&](auto nqal_c) {
+        constexpr int NQAL = decltype(nqal_c)::value;
+        constexpr int NQL = NQAL + (NQ - NQA);   // loads per wave per step
+        if (nsteps <= 0) return;
+#pragma unroll
+        for (int b = 0; b < NBUF - 1; ++b) issue_part(b, kof(b), 0, NQAL);
         // stage 0 has landed once only the activation rows of the later
         // prologue stages are pending (everything older has completed)
-        wait_vmem<NQA * (NBUF - 2)>();
+        wait_vmem<NQAL * (NBUF - 2)>();
         __syncthreads();
         auto step = [&](int j, int b) {
-            issue((b + NBUF - 1) % NBUF, kof(j + NBUF - 1));
+            const int nb = (b + NBUF - 1) % NBUF, kk = kof(j + NBUF - 1);
+            issue_part(nb, kk, 0, NQAL);
+            issue_part(nb, kk, NQA, NQ);
             compute(b);
-            wait_vmem<NQ * (NBUF - 2)>();
+            wait_vmem<NQL * (NBUF - 2)>();
             __syncthreads();
         };
         int j = 0;
@@ -403,7 +426,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
         for (int b = 0; b < NBUF - 1; ++b)
             if (j + b < nsteps) step(j + b, b);
-    }
+    };
+    const int nqal = min(NQA, (__popcll(live32) + 1) / 2);
+    static_for<NQA>([&](auto ic) {
+        if (nqal == decltype(ic)::value + 1) kloop(IC<decltype(ic)::value + 1>{});
+    });
     if (tid < BM) {
         row_asg[tid] = meta_asg;
         row_scale[tid] = meta_s;
