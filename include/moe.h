@@ -139,7 +139,8 @@ int moe_quant_act(const void *x, int rows, int cols, int group, uint8_t *codes, 
  *   A_i = x[a / k] (zero when a = T*k),
  *   h[i, n] = bf16( silu(A_i . Wg_e[n]) * (A_i . Wu_e[n]) ),  n < f,
  * with fp32 accumulation. Blocks at or past num_valid / B are skipped (their
- * h rows are left untouched).
+ * h rows are left untouched); the h (and h_scale) rows of padding slots
+ * (sorted_ids[i] == T*k) are unspecified, and moe_gemm2_combine ignores them.
  *   x [T, d] bf16; w13 / w13_scale as in the header comment;
  *   sorted_ids [P], sorted_expert_ids [NB], num_valid [1] from moe_sort.
  *   quant BF16:       h [P, f] bf16, h_scale unused (may be NULL).

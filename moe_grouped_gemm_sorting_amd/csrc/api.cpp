@@ -238,8 +238,8 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
         HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
     }
     if (quant == 1)
-        HIP_TRY(launch_quant_h_rows(w.hb, w.amax, (int)P, f, num_valid, static_cast<uint8_t *>(h),
-                                    h_scale, s),
+        HIP_TRY(launch_quant_h_rows(w.hb, w.amax, (int)P, f, num_valid, sorted_ids, T * k,
+                                    static_cast<uint8_t *>(h), h_scale, s),
                 "h quantisation launch");
     return MOE_OK;
 }

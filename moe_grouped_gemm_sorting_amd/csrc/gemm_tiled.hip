@@ -39,9 +39,9 @@
 //
 // Epilogue: the tile's per-row metadata (assignment, routing weight,
 // activation scale) is loaded before the K loop and kept in registers until
-// after it. GEMM1 writes the bf16 h tile into LDS and copies it out in
-// 16-byte row segments (and, for e4m3, takes each row's amax there with one
-// atomic per row and tile). GEMM2 either stores its weighted rows at their
+// after it. GEMM1 writes the bf16 h tile into LDS and copies its real rows
+// out in 16-byte row segments (and, for e4m3, takes each row's amax there
+// with one atomic per row and tile). GEMM2 either stores its weighted rows at their
 // assignments (no K-split; a combine kernel sums each token's rows) or adds
 // them into the token's fp32 accumulator row with atomics.
 #include "common.h"
@@ -473,6 +473,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
         for (int it = 0; it < BM * RC / NTHR; ++it) {
             const int idx = tid + NTHR * it, row = idx / RC, c = idx % RC;
+            // padding rows are not stored (their h rows are unspecified); a
+            // row's RC lanes are consecutive, so they skip together
+            if (row_asg[row] < 0) continue;
             const u32x4 val = *reinterpret_cast<const u32x4 *>(hs + row * HROW + c * 16);
             *reinterpret_cast<u32x4 *>(h + ((size_t)(slot0 + row) * p.f + nt * (TN / 2)) * 2 + c * 16) = val;
             if constexpr (QUANT == 1) {

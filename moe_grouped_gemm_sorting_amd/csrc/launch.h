@@ -28,8 +28,8 @@ hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, ui
 
 // h rows: bf16 [rows, cols] with row amax [rows] -> e4m3 codes + scale [rows]
 hipError_t launch_quant_h_rows(const uint16_t *h, const float *amax, int rows, int cols,
-                               const int32_t *num_valid, uint8_t *codes, float *scales,
-                               hipStream_t s);
+                               const int32_t *num_valid, const int32_t *sorted_ids,
+                               int sentinel, uint8_t *codes, float *scales, hipStream_t s);
 
 hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
 

@@ -14,14 +14,19 @@ namespace moe {
 // One workgroup of 256 threads per row. Thread t owns the 8-element chunks
 // t, t + 256, ... (16-byte loads). GROUP_ROW: one scale for the whole row;
 // otherwise one scale per 128 columns (16 consecutive chunks = 16 lanes).
+// With num_valid (rows of h by sort slot), rows at or past num_valid and
+// rows of padding slots (sorted_ids[r] == sentinel) are skipped.
 template <bool GROUP_ROW>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t *__restrict__ x,
                                                     const float *__restrict__ row_amax,
                                                     const int32_t *__restrict__ num_valid,
-                                                    int cols, uint8_t *__restrict__ codes,
+                                                    const int32_t *__restrict__ sorted_ids,
+                                                    int sentinel, int cols,
+                                                    uint8_t *__restrict__ codes,
                                                     float *__restrict__ scales) {
     const int r = blockIdx.x;
     if (num_valid && r >= *num_valid) return;
+    if (sorted_ids && sorted_ids[r] >= sentinel) return;
     const int tid = threadIdx.x;
     const int nchunk = cols / 8;
     const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)r * cols);
@@ -94,17 +99,18 @@ hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, ui
                             float *scales, hipStream_t s) {
     if (rows == 0) return hipSuccess;
     if (group == cols)
-        k_quant_rows<true><<<rows, 256, 0, s>>>(x, nullptr, nullptr, cols, codes, scales);
+        k_quant_rows<true><<<rows, 256, 0, s>>>(x, nullptr, nullptr, nullptr, 0, cols, codes, scales);
     else
-        k_quant_rows<false><<<rows, 256, 0, s>>>(x, nullptr, nullptr, cols, codes, scales);
+        k_quant_rows<false><<<rows, 256, 0, s>>>(x, nullptr, nullptr, nullptr, 0, cols, codes, scales);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_h_rows(const uint16_t *h, const float *amax, int rows, int cols,
-                               const int32_t *num_valid, uint8_t *codes, float *scales,
-                               hipStream_t s) {
+                               const int32_t *num_valid, const int32_t *sorted_ids,
+                               int sentinel, uint8_t *codes, float *scales, hipStream_t s) {
     if (rows == 0) return hipSuccess;
-    k_quant_rows<true><<<rows, 256, 0, s>>>(h, amax, num_valid, cols, codes, scales);
+    k_quant_rows<true><<<rows, 256, 0, s>>>(h, amax, num_valid, sorted_ids, sentinel, cols, codes,
+                                            scales);
     return hipGetLastError();
 }
 
