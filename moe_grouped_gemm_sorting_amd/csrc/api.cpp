@@ -20,6 +20,10 @@
 #define MOE_G2_CT 4
 #endif
 // tiled-kernel tile shape: rows and weight rows (0: the library's choice)
+// routing runs inside the sort's single workgroup while T * E is at most this
+#ifndef MOE_FUSE_ROUTE_MAX
+#define MOE_FUSE_ROUTE_MAX 512
+#endif
 #ifndef MOE_G1_BM
 #define MOE_G1_BM 0
 #endif
@@ -517,10 +521,11 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     // the one-stage path needs a cleared accumulator before its kernel; the
     // routing+sort workgroup clears small ones on the way
     const size_t acc_n = (size_t)T * d;
-    // Routing runs inside the sort's single workgroup for small T (one launch
-    // less); for large T the many-workgroup routing kernel is much faster
-    // (T = 4096: about 5 us against 80 us inside the sort's workgroup).
-    const bool fuse_route = (int64_t)T * E <= 64 * 1024;
+    // Routing runs inside the sort's single workgroup for small T * E (one
+    // launch less); beyond that the one-wave-per-token routing kernel plus the
+    // sort is faster (whole layer, MI355X: T=128, E=256 1692 -> 1595 us;
+    // T=4096, E=8 2930 -> 2870 us; T=32, E=8 unchanged).
+    const bool fuse_route = (int64_t)T * E <= MOE_FUSE_ROUTE_MAX;
     const bool zero_in_sort = stage == 1 && logits && fuse_route && acc_n <= (size_t(1) << 20);
     if (logits && fuse_route) {
         HIP_TRY(launch_route_sort(logits, T, k, E, B, score, renorm, w.topk_ids, w.topk_w,
