@@ -45,8 +45,10 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s);
 hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream_t s);
 bool tiled_gemm_supported(const GemmShape &sh);
 int tiled_tile_cols(int B, int quant, bool gemm1, int bm, int tn);
+int tiled_tile_rows(int B, int quant, bool gemm1, int bm, int tn);
 hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s);
 hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hipStream_t s);
+int tiled_gemm2_parts(int f, int quant, int ksplit);
 }  // namespace moe
 
 using namespace moe;
@@ -138,15 +140,21 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
     const int64_t blocks = std::min<int64_t>(max_blocks(T, k, E, B), std::min<int64_t>(E, rows) + rows / B);
     int64_t ntiles;
     if (use_tiled(B)) {
-        ntiles = d / tiled_tile_cols(B, quant, false, MOE_G2_BM, MOE_G2_TN);
+        ntiles = (int64_t)(d / tiled_tile_cols(B, quant, false, MOE_G2_BM, MOE_G2_TN)) *
+                 (B / tiled_tile_rows(B, quant, false, MOE_G2_BM, MOE_G2_TN));
     } else {
         const int CT = (d % 256 == 0) ? 4 : 2;
         ntiles = d / (64 * CT);
     }
     const int64_t base = std::max<int64_t>(1, ntiles * blocks);
     const int KS = quant == 0 ? 64 : 128;
-    // the tiled kernel holds one workgroup per CU: split only when there are
-    // fewer tiles than CUs (without a split, rows are stored, not added)
+    // the tiled kernel holds one workgroup per CU: split when there are fewer
+    // tiles than CUs; bf16 (MFMA-bound) also splits in two under four rounds
+    // of tiles, which halves the idle tail of the last round (Mixtral
+    // prefill, 560 tiles of 256 x 256: 1110 -> 1015 us). e4m3 at one full
+    // round of tiles got slower (121 -> 130 us).
+    if (use_tiled(B) && base >= cu)
+        return (quant == 0 && base < 4 * (int64_t)cu && f / KS >= 8) ? 2 : 1;
     const int64_t target = use_tiled(B) ? cu : 2 * (int64_t)cu;
     int ks = (int)std::min<int64_t>((target + base - 1) / base, f / KS / 4);
     return std::max(1, ks);
@@ -155,8 +163,9 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
 // Block size: at least the average rows per expert, so that most experts'
 // weights are streamed once; 64/128/256-row blocks go to the LDS-tiled
 // kernels. With many rows per expert, bf16 takes 256-row blocks, whose
-// 256 x 256 gate/up tiles need a third fewer operand bytes per MFMA than
-// 128 x 256 tiles (measured: Mixtral prefill GEMM1 -8%, GEMM2 unchanged).
+// 256 x 256 tiles need a third fewer operand bytes per MFMA than 128 x 256
+// tiles (measured at Mixtral prefill: GEMM1 -8%; GEMM2 -9% together with
+// the two-part split of K).
 // e4m3 takes 256-row blocks from about 100 rows per expert on: its 256 x 128
 // tiles then read each expert's weights once, and the MFMAs of padding-only
 // row quarters are skipped.
@@ -248,17 +257,21 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     return MOE_OK;
 }
 
+// K parts of the tiled down projection whose weighted rows are stored
+constexpr int STORED_SPLITS = 2;
+
 // GEMM2's fp32 buffer: the token accumulator [T, d], or, for the tiled
-// kernel without K-split, the weighted rows by assignment [T*k, d] (the
-// larger of the two, so that one layout serves both).
+// kernel, the weighted rows by K part and assignment [STORED_SPLITS][T*k, d]
+// (the larger of the two, so that one layout serves both).
 float *carve_gemm2(Carver &c, int T, int d, int k, int B) {
-    return c.take<float>((size_t)T * d * (use_tiled(B) ? k : 1));
+    return c.take<float>((size_t)T * d * (use_tiled(B) ? (size_t)k * STORED_SPLITS : 1));
 }
 
-// The tiled down projection without K-split stores each weighted row once
-// and a combine kernel sums each token's k rows: no atomics, no accumulator
-// clearing, and a fixed summation order.
-bool stored_rows(int B, int ksplit) { return use_tiled(B) && ksplit == 1; }
+// The tiled down projection split into at most STORED_SPLITS parts of K
+// stores each part's weighted rows, and a combine kernel sums each token's
+// k x parts rows: no atomics, no accumulator clearing, and a fixed
+// summation order.
+bool stored_rows(int B, int ksplit) { return use_tiled(B) && ksplit <= STORED_SPLITS; }
 
 int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, const void *h,
               const float *h_scale, const void *w2, const float *w2_scale,
@@ -284,8 +297,10 @@ int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, c
     if (stored_rows(B, ksplit)) {
         g.acc = nullptr;
         g.yrows = acc;
-        HIP_TRY(launch_tiled_gemm2(g, MOE_G2_BM, MOE_G2_TN, 1, s), "GEMM2 launch");
-        HIP_TRY(launch_combine_rows(acc, T, k, d, static_cast<uint16_t *>(out), s), "combine launch");
+        HIP_TRY(launch_tiled_gemm2(g, MOE_G2_BM, MOE_G2_TN, ksplit, s), "GEMM2 launch");
+        HIP_TRY(launch_combine_rows(acc, T, k, tiled_gemm2_parts(f, quant, ksplit), d,
+                                    static_cast<uint16_t *>(out), s),
+                "combine launch");
         return MOE_OK;
     }
     if (!acc_zeroed) HIP_TRY(launch_fill_f32(acc, (size_t)T * d, 0.0f, s), "fill launch");

@@ -41,9 +41,9 @@
 // activation scale) is loaded before the K loop and kept in registers until
 // after it. GEMM1 writes the bf16 h tile into LDS and copies its real rows
 // out in 16-byte row segments (and, for e4m3, takes each row's amax there
-// with one atomic per row and tile). GEMM2 either stores its weighted rows at their
-// assignments (no K-split; a combine kernel sums each token's rows) or adds
-// them into the token's fp32 accumulator row with atomics.
+// with one atomic per row and tile). GEMM2 either stores its weighted rows at
+// their K part and assignment (a combine kernel sums each token's rows) or
+// adds them into the token's fp32 accumulator row with atomics.
 #include "common.h"
 #include "launch.h"
 
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
                     if (as[i] < 0) continue;
                     const int col = nt * TN + wn * 64 + lr;
                     if (p.yrows) {
-                        float *dst = p.yrows + (size_t)as[i] * p.d + col;
+                        float *dst = p.yrows + ((size_t)blockIdx.y * p.T * p.k + as[i]) * p.d + col;
 #pragma unroll
                         for (int ct = 0; ct < CT; ++ct) dst[ct * 32] = sw[i] * (acc[rt][ct][4 * q + i] * wsc[ct]);
                     } else {
@@ -562,10 +562,10 @@ bool tiled_gemm_supported(const GemmShape &sh) {
 // Tile shape (rows BM, weight rows TN) for sort blocks of B rows; bm / tn
 // > 0 request a shape, which must be one of the instantiated ones and BM must
 // divide B. The library's choice: a 64/128-row block is one 64/128 x 256 tile;
-// a 256-row block runs bf16 gate/up as 256 x 256 tiles (a third fewer
-// operand bytes per MFMA than 128 x 256), bf16 down as two 128 x 256 tiles,
-// and e4m3 as 256 x 128 tiles (whose weight columns each cover a whole
-// expert of up to 256 rows, so every weight byte leaves HBM once).
+// a 256-row block runs bf16 as 256 x 256 tiles (a third fewer operand bytes
+// per MFMA than 128 x 256) and e4m3 as 256 x 128 tiles (whose weight columns
+// each cover a whole expert of up to 256 rows, so every weight byte leaves
+// HBM once).
 struct TileShape {
     int bm, tn;
 };
@@ -578,11 +578,15 @@ TileShape tile_shape(int B, int quant, bool gemm1, int bm, int tn) {
     if (valid(bm, tn)) return {bm, tn};
     if (B < 256) return {B, 256};
     if (quant == 1) return {256, 128};
-    return gemm1 ? TileShape{256, 256} : TileShape{128, 256};
+    return {256, 256};
 }
 
 int tiled_tile_cols(int B, int quant, bool gemm1, int bm, int tn) {
     return tile_shape(B, quant, gemm1, bm, tn).tn;
+}
+
+int tiled_tile_rows(int B, int quant, bool gemm1, int bm, int tn) {
+    return tile_shape(B, quant, gemm1, bm, tn).bm;
 }
 
 hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s) {
@@ -609,6 +613,15 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s)
     return dispatch<true>(p, sh.quant, ts.bm, ts.tn, grid, s);
 }
 
+// Parts of K for a requested split: ceil(steps / ceil(steps / ksplit)), each
+// non-empty.
+int tiled_gemm2_parts(int f, int quant, int ksplit) {
+    const int steps = f / (quant == 0 ? 64 : 128);
+    ksplit = ksplit < 1 ? 1 : (ksplit > steps ? steps : ksplit);
+    const int steps_per = (steps + ksplit - 1) / ksplit;
+    return (steps + steps_per - 1) / steps_per;
+}
+
 hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hipStream_t s) {
     const GemmShape &sh = g.sh;
     TiledParams p{};
@@ -627,11 +640,10 @@ hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hi
     const int steps = sh.f / KS;
     if (ksplit < 1) ksplit = 1;
     if (ksplit > steps) ksplit = steps;
-    if (g.yrows) ksplit = 1;   // stored rows take the whole reduction
     const int steps_per = (steps + ksplit - 1) / ksplit;
     p.kchunk = steps_per * KS;
     p.rotate = MOE_TILED_ROTATE & (2 << (2 * sh.quant));
-    ksplit = (steps + steps_per - 1) / steps_per;
+    ksplit = tiled_gemm2_parts(sh.f, sh.quant, ksplit);
     const TileShape ts = tile_shape(sh.B, sh.quant, false, bm, tn);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + ts.bm - 1) / ts.bm;

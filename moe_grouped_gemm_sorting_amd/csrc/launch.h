@@ -37,7 +37,8 @@ hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
 hipError_t launch_finalize(const float *acc, uint16_t *out, size_t n, hipStream_t s);
 
 // out[t, :] = bf16(sum over j < k of rows[t*k + j, :]) (j ascending), rows fp32 [T*k, d]
-hipError_t launch_combine_rows(const float *rows, int T, int k, int d, uint16_t *out, hipStream_t s);
+hipError_t launch_combine_rows(const float *rows, int T, int k, int parts, int d, uint16_t *out,
+                               hipStream_t s);
 
 struct GemmShape {
     int T, d, f, E, k, B, quant;
@@ -67,7 +68,7 @@ struct Gemm2Args {
     const float *sorted_w;
     const int32_t *sorted_expert_ids, *num_valid;
     float *acc;             // fp32 [T, d], zeroed by the caller
-    float *yrows;           // tiled kernel, no K-split: rows [T*k, d] by assignment instead of acc
+    float *yrows;           // tiled kernel: rows [parts][T*k, d] by K part and assignment instead of acc
 };
 
 bool onestage_supported(const GemmShape &sh);

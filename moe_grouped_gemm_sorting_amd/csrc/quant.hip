@@ -159,10 +159,14 @@ hipError_t launch_finalize(const float *acc, uint16_t *out, size_t n, hipStream_
 // The combine over stored rows: each token's k weighted expert rows, which
 // GEMM2 wrote at the token's assignments t*k + j, summed in fp32 in
 // ascending j and rounded once to bf16. d is a multiple of 4.
+// rows: `parts` slabs of [T*k, d] (one per part of a split reduction); a
+// token's sum takes its rows in ascending j and, within a row, the parts in
+// ascending order.
 __global__ __launch_bounds__(256) void k_combine_rows(const float *__restrict__ rows, int T, int k,
-                                                      int d, uint16_t *__restrict__ out) {
+                                                      int parts, int d, uint16_t *__restrict__ out) {
     const int d4 = d / 4;
     const size_t n4 = (size_t)T * d4;
+    const size_t slab4 = (size_t)T * k * d4;
     const size_t stride = (size_t)gridDim.x * 256;
     const float4 *r4 = reinterpret_cast<const float4 *>(rows);
     uint2 *o4 = reinterpret_cast<uint2 *>(out);
@@ -170,24 +174,28 @@ __global__ __launch_bounds__(256) void k_combine_rows(const float *__restrict__ 
         const size_t t = i / d4, c = i - t * d4;
         const float4 *src = r4 + t * k * d4 + c;
         float4 v = src[0];
-        for (int j = 1; j < k; ++j) {
-            const float4 u = src[(size_t)j * d4];
-            v.x += u.x;
-            v.y += u.y;
-            v.z += u.z;
-            v.w += u.w;
+        for (int j = 0; j < k; ++j) {
+            for (int q = 0; q < parts; ++q) {
+                if (j == 0 && q == 0) continue;
+                const float4 u = src[(size_t)q * slab4 + (size_t)j * d4];
+                v.x += u.x;
+                v.y += u.y;
+                v.z += u.z;
+                v.w += u.w;
+            }
         }
         o4[i] = make_uint2(f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
                            f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
     }
 }
 
-hipError_t launch_combine_rows(const float *rows, int T, int k, int d, uint16_t *out, hipStream_t s) {
+hipError_t launch_combine_rows(const float *rows, int T, int k, int parts, int d, uint16_t *out,
+                               hipStream_t s) {
     const size_t n4 = (size_t)T * (d / 4);
     if (n4 == 0) return hipSuccess;
     size_t blocks = (n4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    k_combine_rows<<<(unsigned)blocks, 256, 0, s>>>(rows, T, k, d, out);
+    k_combine_rows<<<(unsigned)blocks, 256, 0, s>>>(rows, T, k, parts, d, out);
     return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ def test_two_stage_small_all_outputs(wl):
             with pytest.raises(moe.MoeError):
                 _run_two_stage(wl, x, ids, w, ws, B, 1)
             continue
-        for ksplit in (1, 3):
+        for ksplit in (1, 2, 3):
             log(f"two-stage {wl.name} B={B} ksplit={ksplit}")
             out = _run_two_stage(wl, x, ids, w, ws, B, ksplit)
             torch.cuda.synchronize()
@@ -171,9 +171,9 @@ def test_one_stage_full_decode_shape_and_unsupported():
 
 @pytest.mark.parametrize("B", (64, 128, 256))
 def test_stored_row_combine_is_repeatable(B):
-    """Without K-split the tiled down projection stores each weighted row once
-    and sums a token's rows in a fixed order: repeated calls give the same
-    bits (the atomic K-split path only meets the tolerance)."""
+    """With at most two K parts the tiled down projection stores each part's
+    weighted rows and sums a token's rows in a fixed order: repeated calls
+    give the same bits (the atomic K-split path only meets the tolerance)."""
     wl = workloads.get("mixtral_prefill").replace(name="rep", T=384, f=1024, seed=35)
     x, logits = wl.activations(DEV)
     ws = wl.weights(DEV)
@@ -182,10 +182,16 @@ def test_stored_row_combine_is_repeatable(B):
     h, hs = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, B, wl.quant, ws["w13_scale"])
     outs = [moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B, wl.quant, ws["w2_scale"],
                                   ksplit=1) for _ in range(3)]
+    halves = [moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B, wl.quant, ws["w2_scale"],
+                                    ksplit=2) for _ in range(2)]
     split = moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B, wl.quant, ws["w2_scale"],
                                   ksplit=4)
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert np.array_equal(bits(o), bits(outs[0]))
+    # two stored K parts: repeatable too, and equal to one part up to rounding
+    assert np.array_equal(bits(halves[1]), bits(halves[0]))
+    err, _ = rel_err(bf16_to_f64(bits(halves[0])), bf16_to_f64(bits(outs[0])))
+    assert err <= 1e-2
     err, _ = rel_err(bf16_to_f64(bits(split)), bf16_to_f64(bits(outs[0])))
     assert err <= 1e-2
