@@ -124,3 +124,23 @@ def test_e4m3_rounding_of_every_bf16_value():
     torch.cuda.synchronize()
     assert float(scales[0, 0]) == 1.0
     assert np.array_equal(codes.cpu().numpy()[0, :v.size], oracle.e4m3_encode(v))
+
+
+def test_empty_batch():
+    """T = 0: routing returns nothing, the sort matches the oracle (every slot
+    is padding, no valid block), and the whole layer returns an empty output."""
+    E, k, B = 8, 2, 32
+    ids, w = moe.moe_topk(torch.empty(0, E, dtype=torch.float32, device=DEV), k)
+    assert ids.shape == (0, k) and w.shape == (0, k)
+    _assert_sort_equal(np.zeros((0, k), np.int32), np.zeros((0, k), np.float32), E, B)
+    codes, scales = moe.moe_quant_act(torch.empty(0, 256, dtype=torch.bfloat16, device=DEV), 128)
+    assert codes.shape[0] == 0 and scales.shape[0] == 0
+    for quant in ("bf16", "fp8_token"):
+        wl = workloads.Workload("empty", T=0, d=256, f=256, E=E, k=k, quant=quant, seed=3)
+        ws = wl.weights(DEV)
+        x = torch.empty(0, wl.d, dtype=torch.bfloat16, device=DEV)
+        logits = torch.empty(0, E, dtype=torch.float32, device=DEV)
+        out = moe.fused_moe(x, ws["w13"], ws["w2"], k, logits=logits, quant=quant,
+                            w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"])
+        torch.cuda.synchronize()
+        assert out.shape == (0, wl.d)
