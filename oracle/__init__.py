@@ -19,6 +19,10 @@ passage it follows:
 * :func:`e4m3_encode` / :func:`e4m3_decode` / :func:`quant_rows` -- OCP FP8
   E4M3FN and the amax/448 scale rule used by the fp8 layers (quant types
   per_Token and per_1x128 named in the AITER article, sections 1.1 and 3.2).
+* :func:`fp4_encode` / :func:`fp4_decode` / :func:`mx_quant_rows` -- MXFP4,
+  the quant type per_1x32 (same article, sections 1.1, 2.2 and 3.2;
+  rocketrecap.com/entries/19188 glossary "MXFP4"), with the element format,
+  block size and scale rule of the published OCP MX format.
 """
 from __future__ import annotations
 
@@ -77,6 +81,14 @@ def _load():
         lib.oracle_moe.restype = i32
         lib.oracle_quant_rows.argtypes = [P, i32, i32, i32, P, P]
         lib.oracle_quant_rows.restype = i32
+        lib.oracle_fp4_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_fp4_decode.restype = f32
+        lib.oracle_fp4_encode.argtypes = [f32]
+        lib.oracle_fp4_encode.restype = ctypes.c_uint8
+        lib.oracle_mx_quant_group.argtypes = [P, i32, P, P]
+        lib.oracle_mx_quant_group.restype = ctypes.c_uint8
+        lib.oracle_mx_quant_rows.argtypes = [P, i32, i32, P, P]
+        lib.oracle_mx_quant_rows.restype = i32
         _lib = lib
     return _lib
 
@@ -120,6 +132,46 @@ def quant_group(values):
     deq = np.empty(v.size, np.float32)
     s = lib.oracle_quant_group(_ptr(v), v.size, _ptr(q), _ptr(deq))
     return q, np.float32(s), deq
+
+
+def fp4_decode(codes) -> np.ndarray:
+    """MXFP4 E2M1 codes (low 4 bits) to fp32."""
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([lib.oracle_fp4_decode(int(c)) for c in codes], dtype=np.float32)
+
+
+def fp4_encode(values) -> np.ndarray:
+    """fp32 to E2M1 codes (nearest, ties to the even code, saturating at +-6)."""
+    lib = _load()
+    values = np.asarray(values, dtype=np.float32).ravel()
+    return np.array([lib.oracle_fp4_encode(float(v)) for v in values], dtype=np.uint8)
+
+
+def mx_quant_group(values):
+    """One MXFP4 block: returns (codes one per byte, E8M0 scale code, dequantised values)."""
+    lib = _load()
+    v = _c(values, np.float32).ravel()
+    q = np.empty(v.size, np.uint8)
+    deq = np.empty(v.size, np.float32)
+    c = lib.oracle_mx_quant_group(_ptr(v), v.size, _ptr(q), _ptr(deq))
+    return q, int(c), deq
+
+
+def mx_quant_rows(x_bf16: np.ndarray):
+    """Dynamic MXFP4 quantisation of a bf16 matrix [rows, cols] (cols % 32 == 0).
+
+    Returns (codes uint8 [rows, cols // 2], two per byte with the even column
+    in the low nibble, E8M0 scales uint8 [rows, cols // 32])."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    rc = lib.oracle_mx_quant_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_mx_quant_rows failed ({rc})")
+    return codes, scales
 
 
 def quant_rows(x_bf16: np.ndarray, group: int):
@@ -180,7 +232,7 @@ def sort(topk_ids: np.ndarray, topk_w: np.ndarray, E: int, B: int) -> dict:
     return out
 
 
-QUANT = {"bf16": 0, "fp8_token": 1, "fp8_block": 2}
+QUANT = {"bf16": 0, "fp8_token": 1, "fp8_block": 2, "mxfp4": 3}
 
 
 def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
@@ -190,7 +242,9 @@ def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
 
     w13 / w2 (and the scales) are sequences indexed by expert holding numpy
     arrays (or None for experts no listed token selects): w13[e] [2f, d],
-    w2[e] [d, f]; bf16 as uint16 bits, or e4m3 codes as uint8.
+    w2[e] [d, f]; bf16 as uint16 bits, e4m3 codes as uint8 with fp32 scales,
+    or (mxfp4) E2M1 codes packed two per byte [2f, d/2] / [d, f/2] with E8M0
+    scales uint8 [2f, d/32] / [d, f/32].
     Returns (y fp32 [n, d], out bf16 bits uint16 [n, d])."""
     lib = _load()
     x = _c(x_bf16, np.uint16)
@@ -218,7 +272,8 @@ def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
     wdt = np.uint16 if q == 0 else np.uint8
     t13, t2 = table(w13, wdt), table(w2, wdt)
     if q:
-        s13, s2 = table(w13_scale, np.float32), table(w2_scale, np.float32)
+        sdt = np.uint8 if q == 3 else np.float32
+        s13, s2 = table(w13_scale, sdt), table(w2_scale, sdt)
     else:
         s13 = s2 = None
     y = np.empty((tok.size, d), np.float32)

@@ -28,6 +28,16 @@
  *    format (bias 7, 3 mantissa bits, max 448, no infinities, S.1111.111 is
  *    NaN) and the scale rule s = amax / 448 (s = 1 when amax = 0),
  *    q = round-to-nearest-even, saturating encode of v / s.
+ *  - oracle_fp4_encode / _decode / oracle_mx_quant_group: MXFP4, the
+ *    microscaling 4-bit float that the pages name as quant type per_1x32
+ *    (AITER article, sections 1.1, 3.2 and the gfx950 FP4 build flag of 2.2;
+ *    rocketrecap.com/entries/19188 glossary "MXFP4"). The pages give no
+ *    numerics; this follows the published OCP MX format: E2M1 elements
+ *    (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), 32 consecutive
+ *    elements share one E8M0 scale 2^(c - 127), the shared exponent is
+ *    floor(log2(amax)) - 2 (2 = exponent of the largest E2M1 value; -127
+ *    for an all-zero block), elements are round-to-nearest-even of v / 2^E,
+ *    saturating at +-6.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no BLAS, no
  * fast-math). Every exported function returns 0 on success and a negative
@@ -107,6 +117,67 @@ uint8_t oracle_e4m3_encode(float v)
         return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9)));
     int mant = (int)(r / ldexp(1.0, binade) * 8.0) - 8;
     return (uint8_t)(sign | ((binade + 7) << 3) | mant);
+}
+
+/* MXFP4 E2M1 decode: bit 3 sign, bits 2..1 exponent e (bias 1), bit 0
+ * mantissa m: value = 2^(e-1) * (1 + m/2) for e > 0, m/2 for e = 0. */
+float oracle_fp4_decode(uint8_t c)
+{
+    int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (float)(s ? -v : v);
+}
+
+/* E2M1 encode: round to nearest, ties to the even code (mantissa 0),
+ * saturating at +-6. The format has no NaN; NaN encodes as +-6. */
+uint8_t oracle_fp4_encode(float v)
+{
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs((double)v);
+    if (isnan(v) || a >= 6.0)
+        return (uint8_t)(sign | 7);
+    /* spacing of representable values: 0.5 below 2, 1 in [2, 4), 2 in [4, 6]; the even
+     * multiples of the spacing are exactly the codes with mantissa 0 */
+    double q = (a < 2.0) ? 0.5 : (a < 4.0 ? 1.0 : 2.0);
+    double r = nearbyint(a / q) * q; /* default mode: ties to even */
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    for (int c = 0; c < 8; ++c)
+        if (r == mag[c])
+            return (uint8_t)(sign | c);
+    return (uint8_t)(sign | 7); /* not reached */
+}
+
+/* One MXFP4 block of n values (n = 32 in the layer): shared exponent
+ * E = floor(log2(amax)) - 2, clamped to [-127, 127], and -127 when amax is 0;
+ * q_i = encode(v_i / 2^E). Writes the codes to q (one per byte, if not NULL)
+ * and the dequantised values decode(q_i) * 2^E to deq (if not NULL); returns
+ * the E8M0 scale code E + 127. */
+uint8_t oracle_mx_quant_group(const float *v, int n, uint8_t *q, float *deq)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax)
+            amax = a;
+    }
+    int E = -127;
+    if (amax > 0.0f) {
+        int ex;
+        frexp((double)amax, &ex); /* amax = m * 2^ex, m in [0.5, 1) */
+        E = (ex - 1) - 2;
+        if (E < -127)
+            E = -127;
+        if (E > 127)
+            E = 127;
+    }
+    for (int i = 0; i < n; ++i) {
+        uint8_t c = oracle_fp4_encode((float)ldexp((double)v[i], -E));
+        if (q)
+            q[i] = c;
+        if (deq)
+            deq[i] = (float)ldexp((double)oracle_fp4_decode(c), E);
+    }
+    return (uint8_t)(E + 127);
 }
 
 /* Quantise n values that share one scale. s = amax / 448 in fp32 (s = 1 if
@@ -273,25 +344,42 @@ int oracle_sort(const int32_t *topk_ids, const float *topk_w, int T, int k, int 
 
 /* quant: 0 = bf16 operands; 1 = e4m3 weights with one fp32 scale per output
  * channel and e4m3 activations with one scale per row; 2 = e4m3 weights with
- * one scale per 128x128 block and activations with one scale per 1x128 block.
+ * one scale per 128x128 block and activations with one scale per 1x128 block;
+ * 3 = MXFP4 weights and activations (E2M1 codes, one E8M0 scale per 32
+ * consecutive elements along the reduction dimension).
  * Weights are given per expert (entries of unused experts may be NULL):
  *   w13[e]: [2f, d] (rows 0..f-1 gate, f..2f-1 up), d contiguous,
- *           scales [2f] (quant 1) or [2f/128, d/128] (quant 2);
- *   w2[e]:  [d, f], f contiguous, scales [d] or [d/128, f/128].
+ *           scales fp32 [2f] (quant 1) or [2f/128, d/128] (quant 2);
+ *           quant 3: codes packed two per byte [2f, d/2] (even column in the
+ *           low nibble), E8M0 scales uint8 [2f, d/32];
+ *   w2[e]:  [d, f], f contiguous, scales [d] or [d/128, f/128]; quant 3:
+ *           codes [d, f/2], scales [d, f/32].
  * h_exact = 1 skips the rounding of h (pinning use only). */
 typedef struct {
     int d, f, quant;
     const void *w13, *w2;
-    const float *s13, *s2;
+    const void *s13, *s2;
 } expert_view;
+
+/* element (row, col) of an MXFP4 matrix with `cols` columns */
+static float mx_elem(const void *codes, const void *scales, int cols, int row, int col)
+{
+    uint8_t byte = ((const uint8_t *)codes)[(size_t)row * (cols / 2) + col / 2];
+    uint8_t c = (col & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+    int e = (int)((const uint8_t *)scales)[(size_t)row * (cols / 32) + col / 32] - 127;
+    return (float)ldexp((double)oracle_fp4_decode(c), e);
+}
 
 static float weight13(const expert_view *v, int row, int col)
 {
     size_t idx = (size_t)row * v->d + col;
     if (v->quant == 0)
         return bf16_bits_to_f32(((const uint16_t *)v->w13)[idx]);
+    if (v->quant == 3)
+        return mx_elem(v->w13, v->s13, v->d, row, col);
+    const float *sc = (const float *)v->s13;
     float code = oracle_e4m3_decode(((const uint8_t *)v->w13)[idx]);
-    float s = (v->quant == 1) ? v->s13[row] : v->s13[(size_t)(row / 128) * (v->d / 128) + col / 128];
+    float s = (v->quant == 1) ? sc[row] : sc[(size_t)(row / 128) * (v->d / 128) + col / 128];
     return code * s;
 }
 
@@ -300,15 +388,23 @@ static float weight2(const expert_view *v, int row, int col)
     size_t idx = (size_t)row * v->f + col;
     if (v->quant == 0)
         return bf16_bits_to_f32(((const uint16_t *)v->w2)[idx]);
+    if (v->quant == 3)
+        return mx_elem(v->w2, v->s2, v->f, row, col);
+    const float *sc = (const float *)v->s2;
     float code = oracle_e4m3_decode(((const uint8_t *)v->w2)[idx]);
-    float s = (v->quant == 1) ? v->s2[row] : v->s2[(size_t)(row / 128) * (v->f / 128) + col / 128];
+    float s = (v->quant == 1) ? sc[row] : sc[(size_t)(row / 128) * (v->f / 128) + col / 128];
     return code * s;
 }
 
-/* Replace v[0..n) by its quantise-dequantise image: one group (quant 1) or
- * groups of 128 (quant 2). */
+/* Replace v[0..n) by its quantise-dequantise image: one group (quant 1),
+ * groups of 128 (quant 2) or MXFP4 blocks of 32 (quant 3). */
 static void fake_quant(float *v, int n, int quant)
 {
+    if (quant == 3) {
+        for (int i = 0; i < n; i += 32)
+            oracle_mx_quant_group(v + i, 32, NULL, v + i);
+        return;
+    }
     int g = (quant == 1) ? n : 128;
     for (int i = 0; i < n; i += g)
         oracle_quant_group(v + i, g, NULL, v + i);
@@ -318,19 +414,21 @@ static float silu(float z) { return z / (1.0f + expf(-z)); }
 
 int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
                const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
-               const void *const *w13, const float *const *w13_scale,
-               const void *const *w2, const float *const *w2_scale,
+               const void *const *w13, const void *const *w13_scale,
+               const void *const *w2, const void *const *w2_scale,
                const int32_t *tokens, int n_tokens, float *y, uint16_t *out, int nthreads)
 {
     if (!x || !topk_ids || !topk_w || !w13 || !w2 || !tokens || !y || !out)
         return -1;
     if (T < 0 || d < 1 || f < 1 || E < 1 || k < 1 || k > E || n_tokens < 0)
         return -1;
-    if (quant < 0 || quant > 2)
+    if (quant < 0 || quant > 3)
         return -1;
     if (quant != 0 && (!w13_scale || !w2_scale))
         return -1;
     if (quant == 2 && (d % 128 || f % 128))
+        return -1;
+    if (quant == 3 && (d % 32 || f % 32))
         return -1;
     for (int i = 0; i < n_tokens; ++i) {
         int t = tokens[i];
@@ -394,6 +492,26 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
         free(h);
     }
     return bad ? -2 : 0;
+}
+
+/* Dynamic MXFP4 quantisation of a bf16 matrix [rows, cols] (cols % 32 == 0):
+ * codes packed two per byte [rows, cols / 2] (even column in the low nibble),
+ * E8M0 scales [rows, cols / 32]. */
+int oracle_mx_quant_rows(const uint16_t *x, int rows, int cols, uint8_t *codes, uint8_t *scales)
+{
+    if (!x || !codes || !scales || rows < 0 || cols < 32 || cols % 32)
+        return -1;
+    float buf[32];
+    uint8_t q[32];
+    for (int r = 0; r < rows; ++r)
+        for (int c = 0; c < cols; c += 32) {
+            for (int i = 0; i < 32; ++i)
+                buf[i] = bf16_bits_to_f32(x[(size_t)r * cols + c + i]);
+            scales[(size_t)r * (cols / 32) + c / 32] = oracle_mx_quant_group(buf, 32, q, NULL);
+            for (int i = 0; i < 32; i += 2)
+                codes[(size_t)r * (cols / 2) + (c + i) / 2] = (uint8_t)(q[i] | (q[i + 1] << 4));
+        }
+    return 0;
 }
 
 /* Dynamic activation quantisation of a bf16 matrix [rows, cols]: one scale

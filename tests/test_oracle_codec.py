@@ -127,3 +127,119 @@ def test_quant_rows_groups():
     codes_row, scales_row = oracle.quant_rows(bits, group=256)
     assert scales_row.shape == (5, 1)
     assert np.allclose(scales_row[:, 0], np.abs(xf).max(axis=1) / 448.0, rtol=1e-7, atol=0)
+
+
+# ---- MXFP4 (E2M1 elements, E8M0 block scales) ---------------------------
+
+def _minifloat_table(ebits: int, mbits: int, bias: int):
+    """Every code of a sign / exponent / mantissa float decoded from the field
+    definition: exponent 0 is subnormal (m / 2^mbits * 2^(1 - bias)), the
+    rest normal ((1 + m / 2^mbits) * 2^(e - bias)); special values ignored."""
+    n = 1 << (1 + ebits + mbits)
+    out = np.empty(n, np.float64)
+    for c in range(n):
+        s = c >> (ebits + mbits)
+        e = (c >> mbits) & ((1 << ebits) - 1)
+        m = c & ((1 << mbits) - 1)
+        frac = m / (1 << mbits)
+        v = frac * 2.0 ** (1 - bias) if e == 0 else (1 + frac) * 2.0 ** (e - bias)
+        out[c] = -v if s else v
+    return out
+
+
+def test_generic_minifloat_decoder_matches_torch_fp8():
+    """The field decoder used to pin E2M1 reproduces torch's e4m3fn and e5m2."""
+    e4m3 = _torch_e4m3_table()
+    gen = _minifloat_table(4, 3, 7)
+    ok = ~np.isnan(e4m3)
+    assert np.array_equal(gen[ok], e4m3[ok].astype(np.float64))
+    e5m2 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).double().numpy()
+    ok = np.isfinite(e5m2)
+    assert np.array_equal(_minifloat_table(5, 2, 15)[ok], e5m2[ok])
+
+
+def test_fp4_decode_all_codes():
+    ours = oracle.fp4_decode(np.arange(16)).astype(np.float64)
+    assert np.array_equal(ours, _minifloat_table(2, 1, 1))
+    assert list(ours[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _brute_fp4(values):
+    """Nearest E2M1 code by exhaustive search; ties go to the even code;
+    magnitudes of 6 and above saturate; the sign of zero is kept."""
+    table = _minifloat_table(2, 1, 1)
+    out = []
+    for v in values:
+        v = float(v)
+        neg = np.signbit(v)
+        a = abs(v)
+        if a >= 6.0:
+            out.append(15 if neg else 7)
+            continue
+        best = min(range(8), key=lambda c: (abs(table[c] - a), c & 1))
+        out.append(best | (8 if neg else 0))
+    return np.array(out, np.uint8)
+
+
+def test_fp4_encode_brute_force_midpoints_and_random():
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    mids = [(a + b) / 2 for a, b in zip(mags, mags[1:])]
+    vals = []
+    for m in mags + mids + [6.5, 7.0, 8.0, 100.0, 1e30]:
+        m32 = np.float32(m)
+        vals += [m32, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(np.inf))]
+    vals = np.array(vals, np.float32)
+    vals = np.concatenate([vals, -vals, np.random.default_rng(3).uniform(-9, 9, 4000).astype(np.float32)])
+    assert np.array_equal(oracle.fp4_encode(vals), _brute_fp4(vals))
+    assert oracle.fp4_encode([-0.0])[0] == 8 and oracle.fp4_encode([0.0])[0] == 0
+
+
+def test_mx_block_scale_rule_and_error_bound():
+    """Shared exponent E = floor(log2(amax)) - 2 (numpy frexp), E8M0 code E + 127
+    (torch's E8M0 encoding of 2^E), dequantised value = decode(code) * 2^E, and
+    every element within half the E2M1 spacing unless it saturates at 6 * 2^E."""
+    rng = np.random.default_rng(5)
+    blocks = []
+    for scale in [1e-30, 1e-6, 0.01, 1.0, 3.0, 1e4, 1e30]:
+        blocks.append(rng.standard_normal(32) * scale)
+    for p in [-20, 0, 3, 17]:   # amax exactly a power of two, and just below one
+        b = rng.uniform(-1, 1, 32) * 2.0 ** p
+        b[7] = 2.0 ** p
+        blocks.append(b.copy())
+        b[7] = np.nextafter(np.float32(2.0 ** p), np.float32(0))
+        blocks.append(b)
+    blocks.append(np.zeros(32))
+    table = _minifloat_table(2, 1, 1)
+    for b in blocks:
+        b = b.astype(np.float32)
+        q, code, deq = oracle.mx_quant_group(b)
+        amax = float(np.max(np.abs(b)))
+        if amax == 0:
+            assert code == 0 and not deq.any()
+            continue
+        E = int(np.frexp(np.float64(amax))[1]) - 1 - 2
+        assert code == E + 127
+        ref_code = torch.tensor([2.0 ** E], dtype=torch.float64).to(torch.float8_e8m0fnu).view(torch.uint8)
+        assert code == int(ref_code)
+        assert np.array_equal(deq.astype(np.float64), table[q] * 2.0 ** E)
+        r = np.abs(b.astype(np.float64)) / 2.0 ** E
+        spacing = np.where(r < 2, 0.5, np.where(r < 4, 1.0, 2.0))
+        sat = r >= 6
+        err = np.abs(deq.astype(np.float64) - b) / 2.0 ** E
+        assert np.all(err[~sat] <= spacing[~sat] / 2)
+        assert np.all(np.abs(deq[sat]) == np.float32(6.0 * 2.0 ** E))
+
+
+def test_mx_quant_rows_packs_blocks():
+    rng = np.random.default_rng(6)
+    x = torch.from_numpy(rng.standard_normal((5, 96)).astype(np.float32)).to(torch.bfloat16)
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    codes, scales = oracle.mx_quant_rows(xb)
+    assert codes.shape == (5, 48) and scales.shape == (5, 3)
+    xf = x.float().numpy()
+    for r in range(5):
+        for blk in range(3):
+            q, c, _ = oracle.mx_quant_group(xf[r, blk * 32:(blk + 1) * 32])
+            assert scales[r, blk] == c
+            packed = codes[r, blk * 16:(blk + 1) * 16]
+            assert np.array_equal(packed & 15, q[0::2]) and np.array_equal(packed >> 4, q[1::2])

@@ -34,11 +34,31 @@ def _oracle_moe(wl, x, ws, ids, w, **kw):
     return oracle.moe(_bits(x), ids, w, w13, w2, s13, s2, quant=wl.quant, **kw)
 
 
+def _mx_dequant(codes, scales):
+    """fp64 values of an MXFP4 matrix: nibbles through the E2M1 table (pinned
+    against the format's field definition) times 2^(E8M0 code - 127)."""
+    table = torch.from_numpy(oracle.fp4_decode(np.arange(16)).astype(np.float64))
+    lo, hi = (codes & 15).long(), (codes >> 4).long()
+    vals = torch.stack([table[lo], table[hi]], dim=-1).reshape(*codes.shape[:-1], -1)
+    exp = scales.double() - 127
+    return vals * torch.pow(2.0, exp).repeat_interleave(32, -1)
+
+
+def _mx_fake_quant(v):
+    """Quantise-dequantise rows of v in MXFP4 blocks of 32 (the pinned codec)."""
+    shp = v.shape
+    blocks = v.float().reshape(-1, 32).numpy()
+    out = np.stack([oracle.mx_quant_group(b)[2] for b in blocks])
+    return torch.from_numpy(out.astype(np.float64)).reshape(shp)
+
+
 def _dequant_weights(wl, ws):
     """fp64 weights [E, 2f, d], [E, d, f] from the stored values, via torch's
     e4m3 decoding (a library routine independent of the oracle's codec)."""
     if wl.quant == "bf16":
         return ws["w13"].double(), ws["w2"].double()
+    if wl.quant == "mxfp4":
+        return _mx_dequant(ws["w13"], ws["w13_scale"]), _mx_dequant(ws["w2"], ws["w2_scale"])
     c13 = ws["w13"].view(torch.float8_e4m3fn).double()
     c2 = ws["w2"].view(torch.float8_e4m3fn).double()
     if wl.quant == "fp8_token":
@@ -64,7 +84,9 @@ def dense_masked_reference(wl, x, ws, ids, w, round_h):
     X = x.double()
     W13, W2 = _dequant_weights(wl, ws)
     group = {"fp8_token": None, "fp8_block": 128}.get(wl.quant)
-    if wl.quant != "bf16":
+    if wl.quant == "mxfp4":
+        X = _mx_fake_quant(x.float())
+    elif wl.quant != "bf16":
         X = _torch_fake_quant(x.float(), wl.d if group is None else group)
     M = torch.zeros(wl.T, wl.E, dtype=torch.float64)
     for j in range(wl.k):
@@ -76,7 +98,9 @@ def dense_masked_reference(wl, x, ws, ids, w, round_h):
         h = g * torch.sigmoid(g) * u
         if round_h:
             h = h.float().to(torch.bfloat16).double()
-            if wl.quant != "bf16":
+            if wl.quant == "mxfp4":
+                h = _mx_fake_quant(h)
+            elif wl.quant != "bf16":
                 h = _torch_fake_quant(h, wl.f if group is None else group)
         y += M[:, e:e + 1] * (h @ W2[e].T)
     return y
@@ -94,6 +118,7 @@ SHAPES = [
     workloads.Workload("t4", T=10, d=128, f=256, E=4, k=2, quant="fp8_token", seed=9),
     workloads.Workload("t5", T=8, d=256, f=256, E=5, k=3, quant="fp8_block", score="sigmoid",
                        logits="zipf", seed=10),
+    workloads.Workload("t6", T=8, d=128, f=96, E=4, k=2, quant="mxfp4", seed=11),
 ]
 
 
@@ -143,13 +168,15 @@ def test_zero_input_gives_zero_output():
     assert not y.any() and not (out & 0x7FFF).any()
 
 
-@pytest.mark.parametrize("wl", [SHAPES[0], SHAPES[3]], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [SHAPES[0], SHAPES[3], SHAPES[5]], ids=lambda w: w.name)
 def test_metamorphic_down_scale_by_two_is_exact(wl):
     x, _, ws, ids, w = _layer(wl)
     y, _ = _oracle_moe(wl, x, ws, ids, w)
     ws2 = dict(ws)
     if wl.quant == "bf16":
         ws2["w2"] = (ws["w2"].float() * 2).to(torch.bfloat16)
+    elif wl.quant == "mxfp4":
+        ws2["w2_scale"] = ws["w2_scale"] + 1       # E8M0: one more binade
     else:
         ws2["w2_scale"] = ws["w2_scale"] * 2
     y2, _ = _oracle_moe(wl, x, ws2, ids, w)

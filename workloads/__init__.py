@@ -21,7 +21,13 @@ re-created):
 * fp8 weights are stored as OCP e4m3 codes with fp32 scales: one scale per
   output row (``fp8_token``) or per 128x128 block (``fp8_block``), each scale
   = amax / 448 of what it covers; codes come from torch's e4m3 cast after a
-  clamp to +-448 (input preparation only: the layer never quantises weights).
+  clamp to +-448 (input preparation only: the layer never quantises weights);
+* MXFP4 weights (``mxfp4``) are drawn directly as stored values, with no
+  rounding step: E2M1 codes uniform over all 16 codes, packed two per byte
+  (even column in the low nibble), and one E8M0 scale code per 32 consecutive
+  reduction elements, ``127 + floor(log2(1 / (2.25 sqrt(fan_in)))) - b`` with
+  b uniform in {0, 1} (2.25 is the mean magnitude of a uniform code), so the
+  entries have about the spread of the N(0, 1/sqrt(fan_in)) recipe.
 
 Values depend on the device used to draw them (torch's CPU and GPU generators
 differ); a test draws on one device and copies what the oracle needs.
@@ -44,7 +50,7 @@ class Workload:
     f: int
     E: int
     k: int
-    quant: str = "bf16"          # "bf16" | "fp8_token" | "fp8_block"
+    quant: str = "bf16"          # "bf16" | "fp8_token" | "fp8_block" | "mxfp4"
     score: str = "softmax"       # "softmax" | "sigmoid"
     logits: str = "normal"       # "normal" | "router" | "zipf"
     seed: int = 0
@@ -99,8 +105,23 @@ class Workload:
         full = s[:, None, :, None].expand(N // 128, 128, K // 128, 128).reshape(N, K)
         return self._codes(w, full), s.float().contiguous()
 
+    def _expert_mx(self, e: int, device):
+        g = torch.Generator(device=device).manual_seed(self.seed * 1000 + e)
+
+        def draw(N, K):
+            codes = torch.randint(0, 256, (N, K // 2), generator=g, device=device, dtype=torch.int32)
+            base = 127 + math.floor(math.log2(1.0 / (2.25 * math.sqrt(K))))
+            b = torch.randint(0, 2, (N, K // 32), generator=g, device=device, dtype=torch.int32)
+            return codes.to(torch.uint8), (base - b).to(torch.uint8)
+
+        a, sa = draw(2 * self.f, self.d)
+        b, sb = draw(self.d, self.f)
+        return dict(w13=a, w13_scale=sa, w2=b, w2_scale=sb)
+
     def expert(self, e: int, device="cpu"):
         """Weights of expert e: dict w13, w13_scale, w2, w2_scale (scales None for bf16)."""
+        if self.quant == "mxfp4":
+            return self._expert_mx(e, device)
         w13, w2 = self._expert_fp32(e, device)
         a, sa = self._store(w13)
         b, sb = self._store(w2)
@@ -109,9 +130,13 @@ class Workload:
     def weights(self, device="cpu"):
         """All experts stacked: w13 [E,2f,d], w2 [E,d,f] and scales."""
         wdt = torch.bfloat16 if self.quant == "bf16" else torch.uint8
-        w13 = torch.empty(self.E, 2 * self.f, self.d, dtype=wdt, device=device)
-        w2 = torch.empty(self.E, self.d, self.f, dtype=wdt, device=device)
-        if self.quant == "fp8_token":
+        pk = 2 if self.quant == "mxfp4" else 1   # elements per stored byte
+        w13 = torch.empty(self.E, 2 * self.f, self.d // pk, dtype=wdt, device=device)
+        w2 = torch.empty(self.E, self.d, self.f // pk, dtype=wdt, device=device)
+        if self.quant == "mxfp4":
+            s13 = torch.empty(self.E, 2 * self.f, self.d // 32, dtype=torch.uint8, device=device)
+            s2 = torch.empty(self.E, self.d, self.f // 32, dtype=torch.uint8, device=device)
+        elif self.quant == "fp8_token":
             s13 = torch.empty(self.E, 2 * self.f, device=device)
             s2 = torch.empty(self.E, self.d, device=device)
         elif self.quant == "fp8_block":
@@ -130,6 +155,8 @@ class Workload:
 
     # ---- algorithmic sizes (count each touched expert's weights once) -----
     def weight_bytes_per_expert(self) -> int:
+        if self.quant == "mxfp4":
+            return 3 * self.d * self.f // 2 + 3 * self.d * self.f // 32
         eb = 2 if self.quant == "bf16" else 1
         b = 3 * self.d * self.f * eb
         if self.quant == "fp8_token":
