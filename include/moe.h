@@ -132,6 +132,16 @@ int moe_sort(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, 
 int moe_quant_act(const void *x, int rows, int cols, int group, uint8_t *codes, float *scales,
                   void *stream);
 
+/* Dynamic MXFP4 quantisation (quant type per_1x32, AITER walk-through
+ * sections 1.1 and 3.2) of a bf16 matrix x [rows, cols], cols % 32 == 0: for
+ * each block of 32 consecutive columns, shared exponent
+ * E = floor(log2(amax)) - 2 (-127 for an all-zero block), E2M1 codes of
+ * x / 2^E rounded to nearest (ties to the even code) and saturated at +-6.
+ *   codes [rows, cols / 2] uint8 (out): two codes per byte, the even column
+ *   in the low nibble; scales [rows, cols / 32] uint8 (out): E8M0, E + 127. */
+int moe_quant_act_mx(const void *x, int rows, int cols, uint8_t *codes, uint8_t *scales,
+                     void *stream);
+
 /* Grouped GEMM 1 with fused SwiGLU: stage 1 of the two-stage MoE (AITER
  * walk-through, section 3.2: gate + up projections and the activation). For
  * every used block b (expert e = sorted_expert_ids[b]) and slot

@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "MoeError", "QUANT", "SCORE", "load_library", "library_path",
     "moe_sort_max_padded", "moe_sort_max_blocks", "moe_topk", "moe_sort", "moe_quant_act",
+    "moe_quant_act_mx",
     "moe_gemm1_workspace_bytes", "moe_gemm1_swiglu", "moe_gemm2_workspace_bytes",
     "moe_gemm2_combine", "fused_moe_workspace_bytes", "fused_moe", "moe_select_config",
 ]
@@ -56,6 +57,7 @@ def load_library():
         "moe_topk": (i32, [P, i32, i32, i32, i32, i32, P, P, P]),
         "moe_sort": (i32, [P, P, i32, i32, i32, i32, P, P, P, P, P, P, P]),
         "moe_quant_act": (i32, [P, i32, i32, i32, P, P, P]),
+        "moe_quant_act_mx": (i32, [P, i32, i32, P, P, P]),
         "moe_gemm1_workspace_bytes": (sz, [i32] * 7),
         "moe_gemm1_swiglu": (i32, [i32] * 7 + [P] * 8 + [P, sz, P]),
         "moe_gemm2_workspace_bytes": (sz, [i32] * 7),
@@ -171,6 +173,18 @@ def moe_quant_act(x: torch.Tensor, group: int):
     codes = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
     scales = torch.empty(rows, cols // group, dtype=torch.float32, device=x.device)
     _check(lib.moe_quant_act(_ptr(x), rows, cols, group, _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
+def moe_quant_act_mx(x: torch.Tensor):
+    """Dynamic MXFP4 quantisation of bf16 x [rows, cols]; returns (codes uint8
+    [rows, cols/2], two per byte, E8M0 scales uint8 [rows, cols/32])."""
+    lib = load_library()
+    _need(x, "x", (torch.bfloat16,))
+    rows, cols = x.shape
+    codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device)
+    _check(lib.moe_quant_act_mx(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(x)))
     return codes, scales
 
 

@@ -402,6 +402,17 @@ int moe_sort(const int32_t *topk_ids, const float *topk_w, int T, int k, int E, 
     return MOE_OK;
 }
 
+int moe_quant_act_mx(const void *x, int rows, int cols, uint8_t *codes, uint8_t *scales,
+                     void *stream) {
+    g_err[0] = 0;
+    if (rows < 0 || cols < 32 || cols % 32) return fail(MOE_ERR_INVALID_ARG, "bad MXFP4 shape rows=%d cols=%d", rows, cols);
+    if (rows > 0 && (!x || !codes || !scales)) return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    HIP_TRY(launch_quant_mx(static_cast<const uint16_t *>(x), rows, cols, codes, scales,
+                            (hipStream_t)stream),
+            "quant launch");
+    return MOE_OK;
+}
+
 int moe_quant_act(const void *x, int rows, int cols, int group, uint8_t *codes, float *scales,
                   void *stream) {
     g_err[0] = 0;

@@ -35,6 +35,29 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
 // (v_exp_f32, v_rcp_f32; about 1 ulp each): the relative error, near 1e-6,
 // is far below the bf16 rounding that follows. exp2 overflowing to +inf for
 // very negative z gives 1/inf = 0, the limit.
+// MXFP4 (per_1x32): E2M1 code of r (round to nearest, ties to the code with
+// mantissa 0, saturating at +-6): the magnitude code counts the rounding
+// thresholds below |r|, which are the midpoints between neighbouring values
+// (0.25 .. 5); a tie goes up where the upper neighbour has mantissa 0.
+__device__ __forceinline__ uint32_t e2m1_code(float r) {
+    const float a = fabsf(r);
+    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return m | ((__float_as_uint(r) >> 28) & 8u);
+}
+
+// Shared exponent of an MXFP4 block from its amax: floor(log2(amax)) - 2,
+// clamped to [-127, 127] (-127 for zero or subnormal amax), read off the
+// fp32 exponent field. Returns E; the E8M0 code is E + 127.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 255u);
+    return ef == 0 ? -127 : max(-127, ef - 127 - 2);
+}
+
+// 2^-E as an fp32 (E in [-127, 126], so 127 - E is a normal exponent field)
+__device__ __forceinline__ float mx_inv_scale(int E) { return __uint_as_float((uint32_t)(127 - E) << 23); }
+
 __device__ __forceinline__ float silu(float z) {
     constexpr float kLog2e = 1.44269504088896341f;
     return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));

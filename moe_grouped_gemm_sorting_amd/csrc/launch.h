@@ -22,6 +22,10 @@ hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, in
                              int32_t *offsets, int32_t *num_valid, hipStream_t s,
                              float *zero = nullptr, int zero_n = 0);
 
+// MXFP4: codes [rows, cols / 2] (two per byte), E8M0 scales [rows, cols / 32]
+hipError_t launch_quant_mx(const uint16_t *x, int rows, int cols, uint8_t *codes, uint8_t *scales,
+                           hipStream_t s);
+
 // codes [rows, cols], scales [rows, cols / group]
 hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, uint8_t *codes,
                             float *scales, hipStream_t s);

@@ -95,6 +95,51 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t *__restrict__
     }
 }
 
+// MXFP4 (per_1x32) quantisation: one thread per 32-element block of a row
+// (four 16-byte loads), codes packed two per byte (even column in the low
+// nibble), one E8M0 scale byte per block.
+__global__ __launch_bounds__(256) void k_quant_mx(const uint16_t *__restrict__ x, int rows, int cols,
+                                                  uint8_t *__restrict__ codes,
+                                                  uint8_t *__restrict__ scales) {
+    const int nb = cols / 32;
+    const size_t b = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= (size_t)rows * nb) return;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + b * 32);
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint4 q = src[c];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[8 * c + 2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+            v[8 * c + 2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+            amax = fmaxf(amax, fmaxf(fabsf(v[8 * c + 2 * i]), fabsf(v[8 * c + 2 * i + 1])));
+        }
+    }
+    const int E = mx_block_exp(amax);
+    const float inv = mx_inv_scale(E);
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code(v[8 * j + i] * inv) << (4 * i);
+        out[j] = word;
+    }
+    *reinterpret_cast<uint4 *>(codes + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+    scales[b] = (uint8_t)(E + 127);
+}
+
+hipError_t launch_quant_mx(const uint16_t *x, int rows, int cols, uint8_t *codes, uint8_t *scales,
+                           hipStream_t s) {
+    const size_t n = (size_t)rows * (cols / 32);
+    if (n == 0) return hipSuccess;
+    k_quant_mx<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, rows, cols, codes, scales);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, uint8_t *codes,
                             float *scales, hipStream_t s) {
     if (rows == 0) return hipSuccess;

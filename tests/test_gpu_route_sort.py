@@ -144,3 +144,25 @@ def test_empty_batch():
                             w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"])
         torch.cuda.synchronize()
         assert out.shape == (0, wl.d)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (3, 96), (17, 4096), (128, 7168), (5, 14336)])
+def test_quant_act_mx_bit_exact(rows, cols):
+    """MXFP4 (per_1x32) codes and E8M0 scales equal the oracle's, including an
+    all-zero block, a block at an exact power of two, E2M1 midpoints (ties)
+    and blocks with tiny (subnormal-range) or huge magnitudes."""
+    g = torch.Generator(device=DEV).manual_seed(rows * cols + 1)
+    x = torch.randn(rows, cols, generator=g, device=DEV) * 3
+    if cols >= 96:
+        x[0, 0:32] = 0                                  # all-zero block: E = -127
+        x[0, 32:64] = torch.tensor([4.0] + [0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.25] * 4
+                                   + [-0.75, -5.0, 6.5], device=DEV)   # ties at scale 1
+        x[0, 64:96] *= 1e-38                            # subnormal-range amax
+    if rows > 2:
+        x[2] *= 1e30
+    x = x.to(torch.bfloat16)
+    codes, scales = moe.moe_quant_act_mx(x)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quant_rows(bits(x))
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
