@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_token": 5000.0, "fp8_block": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_token": 5000.0, "fp8_block": 5000.0, "mxfp4": 10100.0}
 METRIC = "fused-MoE tokens/s + % HBM BW (decode) / % MFMA peak (prefill), Mixtral"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["moe_grouped_gemm_sorting_amd/csrc/gemm_stream.hip",
@@ -213,8 +213,11 @@ def main():
     # ---- algorithmic work ----------------------------------------------------
     counts = srt["expert_counts"].cpu().numpy()
     touched = int((counts > 0).sum())
-    eb = 2 if wl.quant == "bf16" else 1
-    w13_bytes = touched * 2 * wl.f * wl.d * eb
+    if wl.quant == "mxfp4":   # E2M1 codes two per byte + one E8M0 byte per 32
+        w13_bytes = touched * 2 * wl.f * (wl.d // 2 + wl.d // 32)
+    else:
+        eb = 2 if wl.quant == "bf16" else 1
+        w13_bytes = touched * 2 * wl.f * wl.d * eb
     if wl.quant == "fp8_token":
         w13_bytes += touched * 2 * wl.f * 4
     elif wl.quant == "fp8_block":
@@ -295,7 +298,7 @@ def main():
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.quant == "bf16" else "fp8_e4m3", "data": "synthetic",
+        "dtype": {"bf16": "bf16", "mxfp4": "mxfp4_e2m1"}.get(wl.quant, "fp8_e4m3"), "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "k": wl.k,
                    "quant": wl.quant, "score": wl.score, "B": B, "stage": stage,
                    "ksplit": ksplit, "parallelism": "single GPU"},

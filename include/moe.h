@@ -49,13 +49,25 @@
  *    sections 1.1 and 3.2. Dynamic quantisation uses s = amax / 448 (s = 1
  *    when amax = 0) and q = round-to-nearest-even of v / s, saturated to
  *    +-448.
+ *    quant = MOE_QUANT_MXFP4 ("per_1x32", the MXFP4 quant type of the same
+ *    sections): E2M1 weights and activations (values 0, 0.5, 1, 1.5, 2, 3,
+ *    4, 6 and negatives), two codes per byte with the even element in the
+ *    low nibble, and one E8M0 scale byte (2^(c - 127)) per 32 consecutive
+ *    elements along the reduction dimension. Activations and h are
+ *    quantised at run time as moe_quant_act_mx describes. Runs on the
+ *    streaming kernels (B = 16 or 32); d and f must be multiples of 256.
  *  - Weights are laid out with the reduction dimension contiguous:
  *      w13 [E, 2f, d]: rows 0..f-1 are the gate projection, rows f..2f-1
  *                      the up projection;
  *      w2  [E, d, f];
- *      scales: per-channel w13_scale [E, 2f], w2_scale [E, d];
+ *      scales: per-channel w13_scale [E, 2f], w2_scale [E, d] (fp32);
  *              per-block   w13_scale [E, 2f/128, d/128],
- *                          w2_scale  [E, d/128, f/128].
+ *                          w2_scale  [E, d/128, f/128] (fp32);
+ *              MXFP4: w13 codes [E, 2f, d/2] with w13_scale [E, 2f, d/32],
+ *                     w2 codes [E, d, f/2] with w2_scale [E, d, f/32]
+ *                     (uint8 E8M0).
+ *    Scale pointers are typed void: fp32 arrays for the e4m3 types, uint8
+ *    arrays for MXFP4.
  *  - d and f must be multiples of 128.
  */
 #ifndef MOE_H
@@ -76,7 +88,12 @@ enum moe_status {
     MOE_ERR_HIP = 4          /* a HIP runtime call failed (see moe_last_error) */
 };
 
-enum moe_quant { MOE_QUANT_BF16 = 0, MOE_QUANT_FP8_TOKEN = 1, MOE_QUANT_FP8_BLOCK = 2 };
+enum moe_quant {
+    MOE_QUANT_BF16 = 0,
+    MOE_QUANT_FP8_TOKEN = 1,
+    MOE_QUANT_FP8_BLOCK = 2,
+    MOE_QUANT_MXFP4 = 3
+};
 enum moe_score { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 
 /* Limits checked by every call. */
@@ -157,13 +174,15 @@ int moe_quant_act_mx(const void *x, int rows, int cols, uint8_t *codes, uint8_t 
  *   quant FP8_TOKEN:  h [P, f] e4m3 codes of the bf16 h quantised per row,
  *                     h_scale [P].
  *   quant FP8_BLOCK:  h [P, f] e4m3 codes per 1x128 block, h_scale [P, f/128].
- *   For fp8, x is quantised inside (into ws) with the matching group.
+ *   quant MXFP4:      h [P, f/2] E2M1 codes of the bf16 h per 1x32 block,
+ *                     h_scale [P, f/32] uint8 E8M0.
+ *   For fp8 and MXFP4, x is quantised inside (into ws) with the matching group.
  * B must be 16, 32, 64, 128 or 256. */
 size_t moe_gemm1_workspace_bytes(int T, int d, int f, int E, int k, int B, int quant);
 int moe_gemm1_swiglu(int T, int d, int f, int E, int k, int B, int quant,
-                     const void *x, const void *w13, const float *w13_scale,
+                     const void *x, const void *w13, const void *w13_scale,
                      const int32_t *sorted_ids, const int32_t *sorted_expert_ids,
-                     const int32_t *num_valid, void *h, float *h_scale,
+                     const int32_t *num_valid, void *h, void *h_scale,
                      void *ws, size_t ws_bytes, void *stream);
 
 /* Grouped GEMM 2 with the routing-weighted combine: stage 2 of the two-stage
@@ -179,7 +198,7 @@ int moe_gemm1_swiglu(int T, int d, int f, int E, int k, int B, int quant,
  *   h / h_scale in the format moe_gemm1_swiglu writes for the same quant. */
 size_t moe_gemm2_workspace_bytes(int T, int d, int f, int E, int k, int B, int quant);
 int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int ksplit,
-                      const void *h, const float *h_scale, const void *w2, const float *w2_scale,
+                      const void *h, const void *h_scale, const void *w2, const void *w2_scale,
                       const int32_t *sorted_ids, const float *sorted_w,
                       const int32_t *sorted_expert_ids, const int32_t *num_valid,
                       void *out, void *ws, size_t ws_bytes, void *stream);
@@ -196,8 +215,8 @@ int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int k
 size_t fused_moe_workspace_bytes(int T, int d, int f, int E, int k, int quant, int B, int stage);
 int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renorm,
               const float *logits, const int32_t *topk_ids, const float *topk_w,
-              const void *x, const void *w13, const float *w13_scale,
-              const void *w2, const float *w2_scale,
+              const void *x, const void *w13, const void *w13_scale,
+              const void *w2, const void *w2_scale,
               int B, int stage, int ksplit, void *out, void *ws, size_t ws_bytes, void *stream);
 
 /* The library's choice of block size B, stage and K-split for a shape

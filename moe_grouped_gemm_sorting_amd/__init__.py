@@ -25,7 +25,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmoe.so")
 _lib = None
 
-QUANT = {"bf16": 0, "fp8_token": 1, "fp8_block": 2}
+QUANT = {"bf16": 0, "fp8_token": 1, "fp8_block": 2, "mxfp4": 3}
 SCORE = {"softmax": 0, "sigmoid": 1}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE",
           4: "MOE_ERR_HIP"}
@@ -109,7 +109,19 @@ _W8 = (torch.uint8, torch.float8_e4m3fn)
 
 
 def _wdtypes(quant):
+    if quant == "mxfp4":
+        return (torch.uint8,)
     return (torch.bfloat16,) if quant == "bf16" else _W8
+
+
+def _sdtypes(quant):
+    """Scale dtype: fp32 for the e4m3 types, E8M0 bytes for MXFP4."""
+    return (torch.uint8,) if quant == "mxfp4" else (torch.float32,)
+
+
+def _pk(quant):
+    """Elements per stored byte of weights, activations codes and h."""
+    return 2 if quant == "mxfp4" else 1
 
 
 def _workspace(nbytes, device, workspace):
@@ -195,11 +207,13 @@ def moe_gemm1_workspace_bytes(T, d, f, E, k, B, quant="bf16") -> int:
 def moe_gemm1_swiglu(x, w13, sort: dict, k: int, B: int, quant: str = "bf16", w13_scale=None,
                      workspace=None):
     """Stage 1: grouped gate/up GEMM + SwiGLU. Returns (h, h_scale) in the
-    format of `quant` (bf16 [P, f]; or e4m3 codes [P, f] + scales)."""
+    format of `quant` (bf16 [P, f]; e4m3 codes [P, f] + fp32 scales; or MXFP4
+    codes [P, f/2] + E8M0 scales [P, f/32])."""
     lib = load_library()
     _need(x, "x", (torch.bfloat16,))
-    E, f2, d = w13.shape
+    E, f2, dk = w13.shape
     f = f2 // 2
+    d = dk * _pk(quant)
     _need(w13, "w13", _wdtypes(quant), x.device)
     T = x.shape[0]
     P = sort["sorted_ids"].numel()
@@ -208,6 +222,10 @@ def moe_gemm1_swiglu(x, w13, sort: dict, k: int, B: int, quant: str = "bf16", w1
     if q == 0:
         h = torch.empty(P, f, dtype=torch.bfloat16, device=dev)
         h_scale = None
+    elif quant == "mxfp4":
+        _need(w13_scale, "w13_scale", _sdtypes(quant), dev)
+        h = torch.empty(P, f // 2, dtype=torch.uint8, device=dev)
+        h_scale = torch.empty(P, f // 32, dtype=torch.uint8, device=dev)
     else:
         _need(w13_scale, "w13_scale", (torch.float32,), dev)
         h = torch.empty(P, f, dtype=torch.uint8, device=dev)
@@ -231,14 +249,15 @@ def moe_gemm2_combine(h, h_scale, w2, sort: dict, T: int, k: int, B: int, quant:
                       w2_scale=None, ksplit: int = 0, out=None, workspace=None):
     """Stage 2: grouped down GEMM + routing-weighted combine; returns out bf16 [T, d]."""
     lib = load_library()
-    E, d, f = w2.shape
+    E, d, fk = w2.shape
+    f = fk * _pk(quant)
     dev = w2.device
     _need(w2, "w2", _wdtypes(quant))
     q = QUANT[quant]
-    _need(h, "h", (torch.bfloat16,) if q == 0 else _W8, dev)
+    _need(h, "h", (torch.bfloat16,) if q == 0 else _wdtypes(quant), dev)
     if q:
-        _need(w2_scale, "w2_scale", (torch.float32,), dev)
-        _need(h_scale, "h_scale", (torch.float32,), dev)
+        _need(w2_scale, "w2_scale", _sdtypes(quant), dev)
+        _need(h_scale, "h_scale", _sdtypes(quant), dev)
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
     nbytes = moe_gemm2_workspace_bytes(T, d, f, E, k, B, quant)
@@ -274,8 +293,8 @@ def fused_moe(x, w13, w2, k: int, logits=None, topk_ids=None, topk_w=None, quant
         _need(topk_ids, "topk_ids", (torch.int32,), dev)
         _need(topk_w, "topk_w", (torch.float32,), dev)
     if q:
-        _need(w13_scale, "w13_scale", (torch.float32,), dev)
-        _need(w2_scale, "w2_scale", (torch.float32,), dev)
+        _need(w13_scale, "w13_scale", _sdtypes(quant), dev)
+        _need(w2_scale, "w2_scale", _sdtypes(quant), dev)
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
     nbytes = fused_moe_workspace_bytes(T, d, f, E, k, quant, B, stage)

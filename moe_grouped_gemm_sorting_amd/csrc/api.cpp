@@ -113,7 +113,9 @@ int check_shape(int T, int d, int f, int E, int k, int B, int quant) {
     if (d < 1 || f < 1) return fail(MOE_ERR_INVALID_ARG, "bad sizes d=%d f=%d", d, f);
     if (d % 128 || f % 128)
         return fail(MOE_ERR_UNSUPPORTED, "d=%d and f=%d must be multiples of 128", d, f);
-    if (quant < 0 || quant > 2) return fail(MOE_ERR_INVALID_ARG, "bad quant %d", quant);
+    if (quant < 0 || quant > 3) return fail(MOE_ERR_INVALID_ARG, "bad quant %d", quant);
+    if (quant == MOE_QUANT_MXFP4 && (d % 256 || f % 256))
+        return fail(MOE_ERR_UNSUPPORTED, "MXFP4 needs d=%d and f=%d multiples of 256", d, f);
     if (!valid_B(B)) return fail(MOE_ERR_INVALID_ARG, "B=%d must be 16, 32, 64, 128 or 256", B);
     if ((int64_t)T * k > (1 << 24)) return fail(MOE_ERR_UNSUPPORTED, "T*k=%lld above 2^24", (long long)T * k);
     if ((int64_t)T * d >= (int64_t(1) << 31) || ((int64_t)T * k + (int64_t)E * B) * f >= (int64_t(1) << 31))
@@ -147,7 +149,7 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
         ntiles = d / (64 * CT);
     }
     const int64_t base = std::max<int64_t>(1, ntiles * blocks);
-    const int KS = quant == 0 ? 64 : 128;
+    const int KS = quant == 0 ? 64 : (quant == MOE_QUANT_MXFP4 ? 256 : 128);   // K per 128-byte step
     // the tiled kernel holds one workgroup per CU: split when there are fewer
     // tiles than CUs; bf16 (MFMA-bound) also splits in two under four rounds
     // of tiles, which halves the idle tail of the last round (Mixtral
@@ -173,8 +175,10 @@ int choose_B(int T, int E, int k, int quant) {
     const double rows = (double)T * k / E;
     if (quant == 0 && rows >= 512) return 256;
     if (quant == 1 && rows >= 96) return 256;
-    if (quant != 2 && rows >= 96) return 128;
-    if (quant != 2 && rows >= 48) return 64;
+    // e4m3 1x128 and MXFP4 run on the streaming kernel only
+    const bool tiled_ok = quant == 0 || quant == 1;
+    if (tiled_ok && rows >= 96) return 128;
+    if (tiled_ok && rows >= 48) return 64;
     if (rows <= 4) return 16;
     return 32;
 }
@@ -191,6 +195,7 @@ Config choose(int T, int d, int f, int E, int k, int quant, int cu) {
 struct Gemm1Ws {
     uint8_t *qx = nullptr;
     float *sx = nullptr;
+    uint8_t *sxm = nullptr;   // MXFP4: E8M0 scales of x [T, d/32]
     uint16_t *hb = nullptr;
     float *amax = nullptr;
 };
@@ -198,7 +203,10 @@ struct Gemm1Ws {
 Gemm1Ws carve_gemm1(Carver &c, int T, int d, int f, int E, int k, int B, int quant) {
     Gemm1Ws w;
     const size_t P = (size_t)max_padded(T, k, E, B);
-    if (quant != 0) {
+    if (quant == MOE_QUANT_MXFP4) {
+        w.qx = c.take<uint8_t>((size_t)T * d / 2);
+        w.sxm = c.take<uint8_t>((size_t)T * (d / 32));
+    } else if (quant != 0) {
         w.qx = c.take<uint8_t>((size_t)T * d);
         w.sx = c.take<float>(quant == 1 ? (size_t)T : (size_t)T * (d / 128));
     }
@@ -210,9 +218,12 @@ Gemm1Ws carve_gemm1(Carver &c, int T, int d, int f, int E, int k, int B, int qua
 }
 
 int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x, const void *w13,
-              const float *w13_scale, const int32_t *sorted_ids, const int32_t *seid,
-              const int32_t *num_valid, void *h, float *h_scale, const Gemm1Ws &w, hipStream_t s,
+              const void *w13_scale_v, const int32_t *sorted_ids, const int32_t *seid,
+              const int32_t *num_valid, void *h, void *h_scale_v, const Gemm1Ws &w, hipStream_t s,
               float *zero = nullptr, size_t zero_n = 0) {
+    // fp32 scales (e4m3) or E8M0 bytes (MXFP4)
+    const float *w13_scale = quant == MOE_QUANT_MXFP4 ? nullptr : static_cast<const float *>(w13_scale_v);
+    float *h_scale = quant == MOE_QUANT_MXFP4 ? nullptr : static_cast<float *>(h_scale_v);
     Gemm1Args g{};
     g.zero = zero;
     g.zero_n = zero_n;
@@ -226,6 +237,14 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     if (quant == 0) {
         g.a = x;
         g.h = h;
+    } else if (quant == MOE_QUANT_MXFP4) {
+        HIP_TRY(launch_quant_mx(static_cast<const uint16_t *>(x), T, d, w.qx, w.sxm, s),
+                "activation quantisation launch");
+        g.a = w.qx;
+        g.a_mx = w.sxm;
+        g.w13_mx = static_cast<const uint8_t *>(w13_scale_v);
+        g.h = h;
+        g.h_mx = static_cast<uint8_t *>(h_scale_v);
     } else {
         HIP_TRY(launch_quant_act(static_cast<const uint16_t *>(x), T, d, quant == 1 ? d : 128, w.qx,
                                  w.sx, s),
@@ -274,16 +293,21 @@ float *carve_gemm2(Carver &c, int T, int d, int k, int B) {
 bool stored_rows(int B, int ksplit) { return use_tiled(B) && ksplit <= STORED_SPLITS; }
 
 int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, const void *h,
-              const float *h_scale, const void *w2, const float *w2_scale,
+              const void *h_scale_v, const void *w2, const void *w2_scale_v,
               const int32_t *sorted_ids, const float *sorted_w, const int32_t *seid,
               const int32_t *num_valid, void *out, float *acc, hipStream_t s,
               bool acc_zeroed = false) {
     Gemm2Args g{};
     g.sh = GemmShape{T, d, f, E, k, B, quant};
     g.h = h;
-    g.h_scale = h_scale;
     g.w2 = w2;
-    g.w2_scale = w2_scale;
+    if (quant == MOE_QUANT_MXFP4) {
+        g.h_mx = static_cast<const uint8_t *>(h_scale_v);
+        g.w2_mx = static_cast<const uint8_t *>(w2_scale_v);
+    } else {
+        g.h_scale = static_cast<const float *>(h_scale_v);
+        g.w2_scale = static_cast<const float *>(w2_scale_v);
+    }
     g.sorted_ids = sorted_ids;
     g.sorted_w = sorted_w;
     g.sorted_expert_ids = seid;
@@ -319,7 +343,7 @@ struct FusedWs {
             *num_valid = nullptr;
     float *sorted_w = nullptr;
     void *h = nullptr;
-    float *h_scale = nullptr;
+    void *h_scale = nullptr;   // fp32 (e4m3) or E8M0 bytes (MXFP4)
     Gemm1Ws g1;
     float *acc = nullptr;
 };
@@ -337,9 +361,10 @@ FusedWs carve_fused(Carver &c, int T, int d, int f, int E, int k, int quant, int
     w.counts = c.take<int32_t>(E);
     w.offsets = c.take<int32_t>(E + 1);
     w.num_valid = c.take<int32_t>(1);
-    w.h = c.take<uint8_t>(P * f * (quant == 0 ? 2 : 1));
+    w.h = c.take<uint8_t>(quant == MOE_QUANT_MXFP4 ? P * f / 2 : P * f * (quant == 0 ? 2 : 1));
     if (quant == 1) w.h_scale = c.take<float>(P);
     if (quant == 2) w.h_scale = c.take<float>(P * (f / 128));
+    if (quant == MOE_QUANT_MXFP4) w.h_scale = c.take<uint8_t>(P * (f / 32));
     w.g1 = carve_gemm1(c, T, d, f, E, k, B, quant);
     w.acc = carve_gemm2(c, T, d, k, B);
     return w;
@@ -435,16 +460,16 @@ size_t moe_gemm1_workspace_bytes(int T, int d, int f, int E, int k, int B, int q
 }
 
 int moe_gemm1_swiglu(int T, int d, int f, int E, int k, int B, int quant, const void *x,
-                     const void *w13, const float *w13_scale, const int32_t *sorted_ids,
+                     const void *w13, const void *w13_scale, const int32_t *sorted_ids,
                      const int32_t *sorted_expert_ids, const int32_t *num_valid, void *h,
-                     float *h_scale, void *ws, size_t ws_bytes, void *stream) {
+                     void *h_scale, void *ws, size_t ws_bytes, void *stream) {
     g_err[0] = 0;
     int rc = check_shape(T, d, f, E, k, B, quant);
     if (rc) return rc;
     if (!w13 || !sorted_ids || !sorted_expert_ids || !num_valid || !h || (T > 0 && !x))
         return fail(MOE_ERR_INVALID_ARG, "null pointer");
     if (quant != 0 && (!w13_scale || !h_scale))
-        return fail(MOE_ERR_INVALID_ARG, "fp8 needs w13_scale and h_scale");
+        return fail(MOE_ERR_INVALID_ARG, "fp8 and MXFP4 need w13_scale and h_scale");
     Carver c(nullptr);
     carve_gemm1(c, T, d, f, E, k, B, quant);
     if (ws_bytes < c.bytes() || (c.bytes() > 0 && !ws))
@@ -464,7 +489,7 @@ size_t moe_gemm2_workspace_bytes(int T, int d, int f, int E, int k, int B, int q
 }
 
 int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int ksplit,
-                      const void *h, const float *h_scale, const void *w2, const float *w2_scale,
+                      const void *h, const void *h_scale, const void *w2, const void *w2_scale,
                       const int32_t *sorted_ids, const float *sorted_w,
                       const int32_t *sorted_expert_ids, const int32_t *num_valid, void *out,
                       void *ws, size_t ws_bytes, void *stream) {
@@ -475,7 +500,7 @@ int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int k
         (T > 0 && !out))
         return fail(MOE_ERR_INVALID_ARG, "null pointer");
     if (quant != 0 && (!w2_scale || !h_scale))
-        return fail(MOE_ERR_INVALID_ARG, "fp8 needs w2_scale and h_scale");
+        return fail(MOE_ERR_INVALID_ARG, "fp8 and MXFP4 need w2_scale and h_scale");
     Carver c(nullptr);
     carve_gemm2(c, T, d, k, B);
     if (ws_bytes < c.bytes() || (c.bytes() > 0 && !ws))
@@ -525,7 +550,7 @@ size_t fused_moe_workspace_bytes(int T, int d, int f, int E, int k, int quant, i
 
 int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renorm,
               const float *logits, const int32_t *topk_ids, const float *topk_w, const void *x,
-              const void *w13, const float *w13_scale, const void *w2, const float *w2_scale,
+              const void *w13, const void *w13_scale, const void *w2, const void *w2_scale,
               int B, int stage, int ksplit, void *out, void *ws, size_t ws_bytes, void *stream) {
     g_err[0] = 0;
     int rc = resolve(T, d, f, E, k, quant, &B, &stage);
@@ -535,7 +560,7 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     if (T > 0 && (!x || !out || (!logits && (!topk_ids || !topk_w))))
         return fail(MOE_ERR_INVALID_ARG, "null pointer");
     if (!w13 || !w2) return fail(MOE_ERR_INVALID_ARG, "null weights");
-    if (quant != 0 && (!w13_scale || !w2_scale)) return fail(MOE_ERR_INVALID_ARG, "fp8 needs scales");
+    if (quant != 0 && (!w13_scale || !w2_scale)) return fail(MOE_ERR_INVALID_ARG, "fp8 and MXFP4 need scales");
     Carver c(nullptr);
     carve_fused(c, T, d, f, E, k, quant, B, true);
     if (ws_bytes < c.bytes() || !ws)

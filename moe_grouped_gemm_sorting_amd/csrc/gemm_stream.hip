@@ -12,7 +12,9 @@
 // reads whole 128-byte lines of 16 rows. The same K permutation is used for
 // both operands, so the MFMA sums are the plain dot products
 // (v_mfma_f32_16x16x32_bf16 twice, or one v_mfma_scale_f32_16x16x128_f8f6f4
-// with unit scales, per step).
+// with unit scales, per step). MXFP4 (E2M1, 256 elements per 128-byte step)
+// takes two scaled MFMAs per step whose per-lane E8M0 scales are the lane's
+// two 32-element blocks, so the block scaling happens inside the MFMA.
 // No LDS: weights are used by exactly one workgroup, which is the decode
 // (weight-streaming, HBM-bound) regime. GEMM1 starts each workgroup's K loop
 // at a step given by its column tile: weight rows 8 KiB apart would otherwise
@@ -41,6 +43,9 @@ struct StreamParams {
     const int32_t *seid;
     void *out;               // GEMM1: h ; GEMM2: acc fp32 [T, d]
     float *out_scale;        // GEMM1 quant 1: row amax [P]; quant 2: h_scale [P, f/128]
+    const uint8_t *a_mx;     // quant 3: E8M0 scales of A [rows, K/32]
+    const uint8_t *w_mx;     // quant 3: E8M0 scales of the weights [E, N, K/32]
+    uint8_t *out_mx;         // GEMM1 quant 3: E8M0 scales of h [P, f/32]
     int T, d, f, k, B;
     int kchunk;              // K elements per blockIdx.y
     int rotate;              // start the K loop at a step given by the column tile
@@ -48,10 +53,12 @@ struct StreamParams {
     size_t zero_n;           // its length (a multiple of 4)
 };
 
+// Element formats: 0 bf16, 1/2 e4m3, 3 MXFP4 (E2M1, two per byte)
 template <int QUANT>
 struct Elem {
-    static constexpr int bytes = QUANT == 0 ? 2 : 1;
-    static constexpr int kstep = 128 / bytes;  // K elements per 128-byte step
+    static constexpr int kstep = QUANT == 0 ? 64 : (QUANT == 3 ? 256 : 128);  // K elements per 128-byte step
+    // bytes of n consecutive elements
+    static constexpr size_t off(size_t n) { return QUANT == 0 ? 2 * n : (QUANT == 3 ? n / 2 : n); }
 };
 
 struct Frag {
@@ -97,6 +104,22 @@ __device__ __forceinline__ Frag masked(const Frag &f, bool ok) {
     return r;
 }
 
+// MXFP4: acc += A . B over one 128-byte K step (K = 256): lane piece lo/hi
+// holds the lane's two 32-element blocks, each one scaled E2M1 MFMA
+// (format 4) over K = 128 whose per-lane E8M0 scales are byte 0 / byte 1 of
+// xa (A) and xb (B).
+__device__ __forceinline__ f32x4 mma_step_mx(const Frag &a, const Frag &b, uint32_t xa, uint32_t xb,
+                                             f32x4 acc) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const i32x8 alo = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w, 0, 0, 0, 0};
+    const i32x8 blo = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w, 0, 0, 0, 0};
+    const i32x8 ahi = {(int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w, 0, 0, 0, 0};
+    const i32x8 bhi = {(int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w, 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, blo, acc, 4, 4, 0, (int)xa, 0, (int)xb);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bhi, acc, 4, 4, 1, (int)xa, 1, (int)xb);
+    return acc;
+}
+
 // acc += A . B over one 128-byte K step.
 template <int QUANT>
 __device__ __forceinline__ f32x4 mma_step(const Frag &a, const Frag &b, f32x4 acc) {
@@ -127,6 +150,7 @@ template <int QUANT, int RT, int NT>
 struct StepBuf {
     Frag a[RT], b[NT];
     float sa[RT][4], sw[NT];
+    uint32_t xa[RT], xb[NT];   // MXFP4: the lane's two E8M0 bytes of the step
 };
 
 // The K loop of one wave: a ring of DEPTH fragment buffers, fully unrolled so
@@ -138,17 +162,25 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t
                                              const bool (&arow_ok)[RT],
                                              const uint8_t *const (&wrow)[NT],
                                              const float *const (&sap)[RT][4],
-                                             const float *const (&swp)[NT], int kbeg, int kend,
+                                             const float *const (&swp)[NT],
+                                             const uint8_t *const (&axs)[RT],
+                                             const uint8_t *const (&wxs)[NT], int kbeg, int kend,
                                              int rot) {
-    constexpr int ES = Elem<QUANT>::bytes;
     constexpr int KS = Elem<QUANT>::kstep;
     constexpr int DEPTH = MOE_STREAM_DEPTH;
     StepBuf<QUANT, RT, NT> bf[DEPTH];
     auto load = [&](StepBuf<QUANT, RT, NT> &b, int kk) {
 #pragma unroll
-        for (int rt = 0; rt < RTL; ++rt) b.a[rt] = load_frag(arow[rt] + (size_t)kk * ES);
+        for (int rt = 0; rt < RTL; ++rt) b.a[rt] = load_frag(arow[rt] + Elem<QUANT>::off(kk));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) b.b[nt] = load_frag_stream(wrow[nt] + (size_t)kk * ES);
+        for (int nt = 0; nt < NT; ++nt) b.b[nt] = load_frag_stream(wrow[nt] + Elem<QUANT>::off(kk));
+        if constexpr (QUANT == 3) {
+            // block kk/32 + 2 lg and the next: 2 bytes at an even offset
+#pragma unroll
+            for (int rt = 0; rt < RTL; ++rt) b.xa[rt] = *reinterpret_cast<const uint16_t *>(axs[rt] + kk / 32);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) b.xb[nt] = *reinterpret_cast<const uint16_t *>(wxs[nt] + kk / 32);
+        }
         if constexpr (QUANT == 2) {
             const int kb = kk / 128;
 #pragma unroll
@@ -165,7 +197,9 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t
             const Frag a = masked(b.a[rt], arow_ok[rt]);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                if constexpr (QUANT == 2) {
+                if constexpr (QUANT == 3) {
+                    acc[rt][nt] = mma_step_mx(a, b.b[nt], b.xa[rt], b.xb[nt], acc[rt][nt]);
+                } else if constexpr (QUANT == 2) {
                     const f32x4 part = mma_step<QUANT>(a, b.b[nt], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[rt][nt][i] += part[i] * (b.sa[rt][i] * b.sw[nt]);
@@ -208,9 +242,8 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t
 // (GEMM1: CT gate tiles + CT matching up tiles).
 template <int QUANT, int RT, int CT, bool GEMM1>
 __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
-    constexpr int ES = Elem<QUANT>::bytes;
-    constexpr int KS = Elem<QUANT>::kstep;
     constexpr int NT = GEMM1 ? 2 * CT : CT;
+    static_assert(QUANT != 3 || !GEMM1 || CT == 2, "an MXFP4 h block is one wave's 32 columns");
 
     if (p.zero) {
         // clear the next stage's accumulator, 16 bytes per thread per pass
@@ -248,18 +281,18 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
         if (GEMM1) {
             arow_ok[rt] = a < sentinel;
             const int t = arow_ok[rt] ? a / p.k : 0;
-            arow[rt] = p.a + ((size_t)t * K + lg * (32 / ES)) * ES;
+            arow[rt] = p.a + Elem<QUANT>::off((size_t)t * K) + lg * 32;
         } else {
             arow_ok[rt] = true;
-            arow[rt] = p.a + ((size_t)slot * K + lg * (32 / ES)) * ES;
+            arow[rt] = p.a + Elem<QUANT>::off((size_t)slot * K) + lg * 32;
         }
     }
     const uint8_t *wrow[NT];
-    const uint8_t *wexp = p.w + (size_t)e * Ntot * K * ES;
+    const uint8_t *wexp = p.w + Elem<QUANT>::off((size_t)e * Ntot * K);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int n = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16 + lr;
-        wrow[nt] = wexp + ((size_t)n * K + lg * (32 / ES)) * ES;
+        wrow[nt] = wexp + Elem<QUANT>::off((size_t)n * K) + lg * 32;
     }
 
     f32x4 acc[RT][NT];
@@ -303,11 +336,31 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
     }
     // K steps start at a step given by the column tile: weight rows a power
     // of two apart otherwise meet in the same HBM channels at the same moment
+    // MXFP4 scale rows: the lane's blocks of a step are 2 lg and 2 lg + 1
+    const uint8_t *axs[RT];
+    const uint8_t *wxs[NT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) axs[rt] = nullptr;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) wxs[nt] = nullptr;
+    if constexpr (QUANT == 3) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const size_t r = GEMM1 ? (size_t)(arow_ok[rt] ? a_of_lane[rt] / p.k : 0)
+                                   : (size_t)(slot0 + rt * 16 + lr);
+            axs[rt] = p.a_mx + r * (K / 32) + 2 * lg;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16 + lr;
+            wxs[nt] = p.w_mx + ((size_t)e * Ntot + n) * (K / 32) + 2 * lg;
+        }
+    }
     const int rot = p.rotate ? (int)blockIdx.x : 0;
     if (RT == 2 && live[RT - 1])
-        stream_kloop<QUANT, RT, RT, NT>(acc, arow, arow_ok, wrow, sap, swp, kbeg, kend, rot);
+        stream_kloop<QUANT, RT, RT, NT>(acc, arow, arow_ok, wrow, sap, swp, axs, wxs, kbeg, kend, rot);
     else
-        stream_kloop<QUANT, RT, 1, NT>(acc, arow, arow_ok, wrow, sap, swp, kbeg, kend, rot);
+        stream_kloop<QUANT, RT, 1, NT>(acc, arow, arow_ok, wrow, sap, swp, axs, wxs, kbeg, kend, rot);
 
     // ------------------------------------------------------------ epilogue
     if constexpr (GEMM1) {
@@ -368,6 +421,22 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
                 if constexpr (QUANT == 1) {
                     if (lr == 0) atomic_max_nonneg(p.out_scale + slot, rmax[rt][i]);
                 }
+                if constexpr (QUANT == 3) {
+                    // one MXFP4 block: the wave's 32 columns n0 .. n0+31 of the row;
+                    // even lanes pack their code with the odd neighbour's
+                    const int E = mx_block_exp(rmax[rt][i]);
+                    const float inv = mx_inv_scale(E);
+                    uint8_t *h = reinterpret_cast<uint8_t *>(p.out);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        const uint32_t c = e2m1_code(hv[rt][ct][i] * inv);
+                        const uint32_t hi = (uint32_t)__shfl_xor((int)c, 1, 64);
+                        if ((lr & 1) == 0)
+                            h[(size_t)slot * (f / 2) + (n0 + ct * 16 + lr) / 2] = (uint8_t)(c | (hi << 4));
+                    }
+                    if (lr == 0) p.out_mx[(size_t)slot * (f / 32) + n0 / 32] = (uint8_t)(E + 127);
+                    continue;
+                }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     const int n = n0 + ct * 16 + lr;
@@ -414,14 +483,21 @@ hipError_t run(const StreamParams &p, dim3 grid, hipStream_t s) {
 
 template <bool GEMM1, int QUANT>
 hipError_t dispatch_rt_ct(const StreamParams &p, int RT, int CT, dim3 grid, hipStream_t s) {
-    if (RT == 1) {
-        if (CT == 1) return run<QUANT, 1, 1, GEMM1>(p, grid, s);
-        if (CT == 2) return run<QUANT, 1, 2, GEMM1>(p, grid, s);
-        if (!GEMM1 && CT == 4) return run<QUANT, 1, 4, GEMM1>(p, grid, s);
-    } else if (RT == 2) {
-        if (CT == 1) return run<QUANT, 2, 1, GEMM1>(p, grid, s);
-        if (CT == 2) return run<QUANT, 2, 2, GEMM1>(p, grid, s);
-        if (!GEMM1 && CT == 4) return run<QUANT, 2, 4, GEMM1>(p, grid, s);
+    if constexpr (QUANT == 3 && GEMM1) {
+        if (CT != 2) return hipErrorInvalidValue;
+        if (RT == 1) return run<3, 1, 2, true>(p, grid, s);
+        if (RT == 2) return run<3, 2, 2, true>(p, grid, s);
+        return hipErrorInvalidValue;
+    } else {
+        if (RT == 1) {
+            if (CT == 1) return run<QUANT, 1, 1, GEMM1>(p, grid, s);
+            if (CT == 2) return run<QUANT, 1, 2, GEMM1>(p, grid, s);
+            if (!GEMM1 && CT == 4) return run<QUANT, 1, 4, GEMM1>(p, grid, s);
+        } else if (RT == 2) {
+            if (CT == 1) return run<QUANT, 2, 1, GEMM1>(p, grid, s);
+            if (CT == 2) return run<QUANT, 2, 2, GEMM1>(p, grid, s);
+            if (!GEMM1 && CT == 4) return run<QUANT, 2, 4, GEMM1>(p, grid, s);
+        }
     }
     return hipErrorInvalidValue;
 }
@@ -430,17 +506,22 @@ template <bool GEMM1>
 hipError_t dispatch(const StreamParams &p, int quant, int RT, int CT, dim3 grid, hipStream_t s) {
     if (quant == 0) return dispatch_rt_ct<GEMM1, 0>(p, RT, CT, grid, s);
     if (quant == 1) return dispatch_rt_ct<GEMM1, 1>(p, RT, CT, grid, s);
+    if (quant == 3) return dispatch_rt_ct<GEMM1, 3>(p, RT, CT, grid, s);
     return dispatch_rt_ct<GEMM1, 2>(p, RT, CT, grid, s);
 }
 
 }  // namespace
 
+// K (d for GEMM1, f for GEMM2) in whole 128-byte steps; GEMM1's h columns
+// in whole workgroups (64 per column tile of each wave)
 bool stream_gemm1_supported(const GemmShape &sh) {
-    return (sh.B == 16 || sh.B == 32) && sh.f % 128 == 0 && sh.d % 128 == 0;
+    const int kstep = sh.quant == 3 ? 256 : 128;
+    return (sh.B == 16 || sh.B == 32) && sh.f % 128 == 0 && sh.d % kstep == 0;
 }
 
 bool stream_gemm2_supported(const GemmShape &sh) {
-    return (sh.B == 16 || sh.B == 32) && sh.f % 128 == 0 && sh.d % 128 == 0;
+    const int kstep = sh.quant == 3 ? 256 : 128;
+    return (sh.B == 16 || sh.B == 32) && sh.f % kstep == 0 && sh.d % 128 == 0;
 }
 
 hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
@@ -459,7 +540,12 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
     p.rotate = MOE_STREAM_ROTATE & 1;
     p.zero = g.zero;
     p.zero_n = g.zero_n;
-    if (sh.quant == 2) CT = 2;  // one 128-column quant block per workgroup
+    p.a_mx = g.a_mx;
+    p.w_mx = g.w13_mx;
+    p.out_mx = g.h_mx;
+    // quant 2: one 128-column quant block per workgroup; quant 3: one
+    // 32-column MXFP4 block per wave
+    if (sh.quant == 2 || sh.quant == 3) CT = 2;
     const int RT = sh.B / 16;
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + sh.B - 1) / sh.B;
@@ -478,8 +564,10 @@ hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream
     p.sorted_w = g.sorted_w;
     p.seid = g.sorted_expert_ids;
     p.out = g.acc;
+    p.a_mx = g.h_mx;
+    p.w_mx = g.w2_mx;
     p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
-    const int KS = sh.quant == 0 ? 64 : 128;
+    const int KS = sh.quant == 0 ? 64 : (sh.quant == 3 ? 256 : 128);
     const int steps = sh.f / KS;
     if (ksplit < 1) ksplit = 1;
     if (ksplit > steps) ksplit = steps;

@@ -59,6 +59,10 @@ struct Gemm1Args {
     float *h_scale;         // quant 1: row amax [P] (zeroed by the caller); quant 2: [P, f/128]
     float *zero;            // optional: fp32 buffer [zero_n] the kernel clears on the way
     size_t zero_n;
+    // quant 3 (MXFP4): a / w13 / h are E2M1 codes two per byte, with E8M0
+    // scales a_mx [T, d/32], w13_mx [E, 2f, d/32], h_mx [P, f/32] (out)
+    const uint8_t *a_mx, *w13_mx;
+    uint8_t *h_mx;
 };
 
 struct Gemm2Args {
@@ -73,6 +77,7 @@ struct Gemm2Args {
     const int32_t *sorted_expert_ids, *num_valid;
     float *acc;             // fp32 [T, d], zeroed by the caller
     float *yrows;           // tiled kernel: rows [parts][T*k, d] by K part and assignment instead of acc
+    const uint8_t *h_mx, *w2_mx;   // quant 3: E8M0 scales [P, f/32] and [E, d, f/32]
 };
 
 bool onestage_supported(const GemmShape &sh);

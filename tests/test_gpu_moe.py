@@ -1,6 +1,6 @@
 """GPU parity of the grouped GEMMs and the fused layer against the CPU oracle.
 
-Small shapes compare every output; the five full-size workloads run exactly
+Small shapes compare every output; the full-size workloads run exactly
 as the benchmark launches them and compare sampled token rows (the oracle
 computes any row on its own). Bar: relative error floored at the output RMS
 <= 2e-2 (bf16) or 6e-2 (fp8)."""
@@ -23,6 +23,9 @@ SMALL = [
     workloads.Workload("tok_fp8", T=45, d=256, f=512, E=4, k=2, quant="fp8_token", seed=24),
     workloads.Workload("blk_fp8", T=33, d=384, f=256, E=12, k=3, quant="fp8_block",
                        score="sigmoid", logits="zipf", seed=25),
+    workloads.Workload("tok_mx", T=40, d=256, f=512, E=4, k=2, quant="mxfp4", seed=41),
+    workloads.Workload("mx_sigmoid", T=33, d=512, f=256, E=8, k=3, quant="mxfp4",
+                       score="sigmoid", logits="zipf", seed=42),
     workloads.Workload("one_expert", T=20, d=128, f=128, E=1, k=1, seed=26),
     workloads.Workload("single_token", T=1, d=256, f=256, E=8, k=2, seed=27),
     workloads.Workload("tiled_bf16", T=300, d=512, f=384, E=4, k=2, seed=29),
@@ -37,7 +40,7 @@ SMALL = [
 
 
 def _tiled_ok(wl):
-    return wl.quant != "fp8_block" and wl.d % 256 == 0
+    return wl.quant not in ("fp8_block", "mxfp4") and wl.d % 256 == 0
 
 
 def _run_two_stage(wl, x, ids, w, ws, B, ksplit):
@@ -100,7 +103,7 @@ def test_fused_with_given_routing_and_idle_experts():
 
 
 FULL_SAMPLES = {"tiny": None, "mixtral_decode": None, "mixtral_prefill": 24, "mixtral_fp8": 24,
-                "deepseek_fp8": 6}
+                "deepseek_fp8": 6, "mixtral_mxfp4": None}
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))

@@ -169,8 +169,8 @@ class Workload:
         return 6 * self.d * self.f * self.T * self.k
 
 
-# The five workloads: a tiny layer plus Mixtral-8x7B- and DeepSeek-V3-shaped
-# layers (seed = 1000 + index).
+# The workloads: a tiny layer plus Mixtral-8x7B- and DeepSeek-V3-shaped layers
+# (seed = 1000 + index).
 WORKLOADS = {
     "tiny": Workload("tiny", T=16, d=128, f=256, E=4, k=2, logits="router", seed=1001),
     "mixtral_decode": Workload("mixtral_decode", T=32, d=4096, f=14336, E=8, k=2, seed=1002),
@@ -179,6 +179,9 @@ WORKLOADS = {
                             quant="fp8_token", seed=1004),
     "deepseek_fp8": Workload("deepseek_fp8", T=128, d=7168, f=2048, E=256, k=8,
                              quant="fp8_block", score="sigmoid", logits="zipf", seed=1005),
+    # the per_1x32 (MXFP4) quant type on the Mixtral decode shape
+    "mixtral_mxfp4": Workload("mixtral_mxfp4", T=32, d=4096, f=14336, E=8, k=2,
+                              quant="mxfp4", seed=1006),
 }
 
 
