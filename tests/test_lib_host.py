@@ -88,6 +88,14 @@ def test_validation_before_any_device_call(lib):
                          16, 2, 0, fake, fake, n - 1, S) == 3
     assert lib.fused_moe_workspace_bytes(4, 128, 256, 4, 2, 0, 16, 3) == 0
     assert lib.moe_status_string(3) == b"workspace too small"
+    # MXFP4: d and f must be multiples of 256, the quantiser's columns of 32
+    assert lib.moe_gemm1_swiglu(4, 128, 256, 4, 2, 16, 3, *args) == 2
+    assert lib.moe_gemm1_swiglu(4, 256, 384, 4, 2, 16, 3, *args) == 2
+    assert lib.moe_gemm1_swiglu(4, 256, 256, 4, 2, 16, 3, fake, fake, None, fake, fake, fake, fake,
+                                fake, None, 0, S) == 1          # MXFP4 without scales
+    assert lib.moe_quant_act_mx(None, 2, 48, None, None, S) == 1
+    assert lib.moe_quant_act_mx(None, 2, 64, None, None, S) == 1 and "null" in _err(lib)
+    assert lib.fused_moe_workspace_bytes(4, 256, 256, 4, 2, 3, 64, 2) > 0   # size query only
 
 
 def test_workspace_queries_grow_with_the_problem(lib):
@@ -101,8 +109,11 @@ def test_workspace_queries_grow_with_the_problem(lib):
 def test_select_config_is_host_only_and_valid(lib):
     for shape in [(16, 128, 256, 4, 2, "bf16"), (32, 4096, 14336, 8, 2, "bf16"),
                   (4096, 4096, 14336, 8, 2, "bf16"), (512, 4096, 14336, 8, 2, "fp8_token"),
-                  (128, 7168, 2048, 256, 8, "fp8_block"), (1, 4096, 14336, 8, 2, "bf16")]:
+                  (128, 7168, 2048, 256, 8, "fp8_block"), (1, 4096, 14336, 8, 2, "bf16"),
+                  (32, 4096, 14336, 8, 2, "mxfp4"), (4096, 4096, 14336, 8, 2, "mxfp4")]:
         B, stage, ks = moe.moe_select_config(*shape, cu_count=256)
         assert B in (16, 32, 64, 128, 256) and stage in (1, 2) and ks >= 1
+        if shape[-1] == "mxfp4":
+            assert B in (16, 32)        # MXFP4 runs on the streaming kernels
     with pytest.raises(moe.MoeError):
         moe.moe_select_config(4, 100, 256, 4, 2, "bf16", cu_count=256)
