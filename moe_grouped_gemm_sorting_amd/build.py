@@ -24,10 +24,18 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source flags. The weight-streaming kernels keep their MFMA
+# accumulators in ordinary VGPRs: with accumulation registers the allocator
+# rotated accumulators through copy instructions on every K step of several
+# instantiations (and the extra registers cost a wave of occupancy).
+SOURCE_FLAGS = {
+    "gemm_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -88,4 +88,17 @@ __device__ __forceinline__ void atomic_max_nonneg(float *p, float v) {
     atomicMax(reinterpret_cast<unsigned int *>(p), __float_as_uint(v));
 }
 
+// compile-time integer, and f(IC<0>{}), ..., f(IC<N-1>{})
+template <int I>
+struct IC {
+    static constexpr int value = I;
+};
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(IC<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 }  // namespace moe

@@ -8,13 +8,14 @@
 //
 // Both operands have the reduction dimension contiguous, so every lane loads
 // its MFMA fragments straight from global memory: lane l serves row/column
-// l % 16 and the 32-byte piece (l / 16) of each 128-byte K step, i.e. a wave
-// reads whole 128-byte lines of 16 rows. The same K permutation is used for
-// both operands, so the MFMA sums are the plain dot products
-// (v_mfma_f32_16x16x32_bf16 twice, or one v_mfma_scale_f32_16x16x128_f8f6f4
-// with unit scales, per step). MXFP4 (E2M1, 256 elements per 128-byte step)
-// takes two scaled MFMAs per step whose per-lane E8M0 scales are the lane's
-// two 32-element blocks, so the block scaling happens inside the MFMA.
+// l % 16 and two 16-byte pieces of each 128-byte K step (lane group l / 16
+// picks which), i.e. a wave reads whole 128-byte lines of 16 rows. The same
+// K permutation is used for both operands, so the MFMA sums are the plain
+// dot products (v_mfma_f32_16x16x32_bf16 twice, or one
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales, per step). MXFP4
+// (E2M1, 256 elements per 128-byte step) takes two scaled MFMAs per step
+// whose per-lane E8M0 scales are the lane's two 32-element blocks, so the
+// block scaling happens inside the MFMA; the scales come in 8-step chunks.
 // No LDS: weights are used by exactly one workgroup, which is the decode
 // (weight-streaming, HBM-bound) regime. GEMM1 starts each workgroup's K loop
 // at a step given by its column tile: weight rows 8 KiB apart would otherwise
@@ -46,6 +47,7 @@ struct StreamParams {
     const uint8_t *a_mx;     // quant 3: E8M0 scales of A [rows, K/32]
     const uint8_t *w_mx;     // quant 3: E8M0 scales of the weights [E, N, K/32]
     uint8_t *out_mx;         // GEMM1 quant 3: E8M0 scales of h [P, f/32]
+    int a_rows;              // quant 3: rows of a_mx (GEMM1: T tokens, GEMM2: P slots)
     int T, d, f, k, B;
     int kchunk;              // K elements per blockIdx.y
     int rotate;              // start the K loop at a step given by the column tile
@@ -62,7 +64,19 @@ struct Elem {
 };
 
 struct Frag {
-    u32x4 lo, hi;  // 32 contiguous bytes of one row's 128-byte K step
+    u32x4 lo, hi;  // the lane's two 16-byte pieces of one row's 128-byte K step
+};
+
+// Where lane group lg (lane / 16) finds its two pieces in a 128-byte K step:
+// bytes 32 lg and 32 lg + 16, except for MXFP4, whose pieces sit at 16 lg and
+// 64 + 16 lg. An MXFP4 lane group then owns 32-element blocks lg and 4 + lg
+// of every step, so its E8M0 scales are byte lg of consecutive scale dwords
+// (see mx_chunk_to_lanes). Either way a wave's load covers whole 64-byte
+// halves of 16 rows' lines, and both operands use the same K permutation.
+template <int QUANT>
+struct Piece {
+    static constexpr int first(int lg) { return QUANT == 3 ? 16 * lg : 32 * lg; }
+    static constexpr int second = QUANT == 3 ? 64 : 16;
 };
 
 #ifndef MOE_STREAM_NT
@@ -73,51 +87,36 @@ struct Frag {
 #define MOE_STREAM_ROTATE 1
 #endif
 
+template <int SECOND>
 __device__ __forceinline__ Frag load_frag(const uint8_t *p) {
     Frag f;
     f.lo = *reinterpret_cast<const u32x4 *>(p);
-    f.hi = *reinterpret_cast<const u32x4 *>(p + 16);
+    f.hi = *reinterpret_cast<const u32x4 *>(p + SECOND);
     return f;
 }
 
-// Weight fragments. Nontemporal loads (MOE_STREAM_NT) would keep the weights,
-// read once per call, from evicting activations from the caches, but measured
+// Weight operands are read through a buffer resource over the expert's
+// slice: every weight tile of a wave shares one per-lane offset (row within
+// the tile, piece of the step) and adds a wave-uniform scalar offset (tile
+// row, K step), so the wave keeps no 64-bit pointer per tile and spends no
+// vector ALU on addresses. The slice must stay below 2 GiB.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, size_t bytes) {
+    // word 3 of a raw (unswizzled, stride 0) gfx9 resource: 32-bit data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Nontemporal loads (MOE_STREAM_NT, the slc bit) would keep the weights, read
+// once per call, from evicting activations from the caches, but measured
 // slower; they are off.
-__device__ __forceinline__ Frag load_frag_stream(const uint8_t *p) {
-#if MOE_STREAM_NT
+template <int SECOND>
+__device__ __forceinline__ Frag load_frag_buf(Rsrc r, int voff, int soff) {
+    constexpr int aux = MOE_STREAM_NT ? 2 : 0;
     Frag f;
-    f.lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    f.hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + 16));
+    f.lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, aux));
+    f.hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + SECOND, soff, aux));
     return f;
-#else
-    return load_frag(p);
-#endif
-}
-
-// Padding rows (sentinel slots) enter the MFMA as zeros. The mask is applied
-// where the fragment is consumed: masking right after the load would make
-// the wave wait for that load before issuing the next ones.
-__device__ __forceinline__ Frag masked(const Frag &f, bool ok) {
-    Frag r;
-    r.lo = ok ? f.lo : u32x4{0, 0, 0, 0};
-    r.hi = ok ? f.hi : u32x4{0, 0, 0, 0};
-    return r;
-}
-
-// MXFP4: acc += A . B over one 128-byte K step (K = 256): lane piece lo/hi
-// holds the lane's two 32-element blocks, each one scaled E2M1 MFMA
-// (format 4) over K = 128 whose per-lane E8M0 scales are byte 0 / byte 1 of
-// xa (A) and xb (B).
-__device__ __forceinline__ f32x4 mma_step_mx(const Frag &a, const Frag &b, uint32_t xa, uint32_t xb,
-                                             f32x4 acc) {
-    typedef int i32x8 __attribute__((ext_vector_type(8)));
-    const i32x8 alo = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w, 0, 0, 0, 0};
-    const i32x8 blo = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w, 0, 0, 0, 0};
-    const i32x8 ahi = {(int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w, 0, 0, 0, 0};
-    const i32x8 bhi = {(int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w, 0, 0, 0, 0};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, blo, acc, 4, 4, 0, (int)xa, 0, (int)xb);
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bhi, acc, 4, 4, 1, (int)xa, 1, (int)xb);
-    return acc;
 }
 
 // acc += A . B over one 128-byte K step.
@@ -150,37 +149,28 @@ template <int QUANT, int RT, int NT>
 struct StepBuf {
     Frag a[RT], b[NT];
     float sa[RT][4], sw[NT];
-    uint32_t xa[RT], xb[NT];   // MXFP4: the lane's two E8M0 bytes of the step
 };
 
 // The K loop of one wave: a ring of DEPTH fragment buffers, fully unrolled so
 // every buffer index is a compile-time constant; the loads of step k + DEPTH-1
 // are issued before the MFMAs of step k. Only the first RTL row tiles hold
 // real rows. Block scales (QUANT 2) travel with their fragments.
+// Weight tile nt of step kk is read at (wvoff, wtile[nt] + bytes of kk) of wr.
 template <int QUANT, int RT, int RTL, int NT>
 __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t *const (&arow)[RT],
-                                             const bool (&arow_ok)[RT],
-                                             const uint8_t *const (&wrow)[NT],
+                                             Rsrc wr, int wvoff, const int (&wtile)[NT],
                                              const float *const (&sap)[RT][4],
-                                             const float *const (&swp)[NT],
-                                             const uint8_t *const (&axs)[RT],
-                                             const uint8_t *const (&wxs)[NT], int kbeg, int kend,
+                                             const float *const (&swp)[NT], int kbeg, int kend,
                                              int rot) {
     constexpr int KS = Elem<QUANT>::kstep;
     constexpr int DEPTH = MOE_STREAM_DEPTH;
     StepBuf<QUANT, RT, NT> bf[DEPTH];
     auto load = [&](StepBuf<QUANT, RT, NT> &b, int kk) {
 #pragma unroll
-        for (int rt = 0; rt < RTL; ++rt) b.a[rt] = load_frag(arow[rt] + Elem<QUANT>::off(kk));
+        for (int rt = 0; rt < RTL; ++rt) b.a[rt] = load_frag<16>(arow[rt] + Elem<QUANT>::off(kk));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) b.b[nt] = load_frag_stream(wrow[nt] + Elem<QUANT>::off(kk));
-        if constexpr (QUANT == 3) {
-            // block kk/32 + 2 lg and the next: 2 bytes at an even offset
-#pragma unroll
-            for (int rt = 0; rt < RTL; ++rt) b.xa[rt] = *reinterpret_cast<const uint16_t *>(axs[rt] + kk / 32);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) b.xb[nt] = *reinterpret_cast<const uint16_t *>(wxs[nt] + kk / 32);
-        }
+        for (int nt = 0; nt < NT; ++nt)
+            b.b[nt] = load_frag_buf<16>(wr, wvoff, wtile[nt] + (int)Elem<QUANT>::off(kk));
         if constexpr (QUANT == 2) {
             const int kb = kk / 128;
 #pragma unroll
@@ -194,12 +184,10 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t
     auto compute = [&](const StepBuf<QUANT, RT, NT> &b) {
 #pragma unroll
         for (int rt = 0; rt < RTL; ++rt) {
-            const Frag a = masked(b.a[rt], arow_ok[rt]);
+            const Frag &a = b.a[rt];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                if constexpr (QUANT == 3) {
-                    acc[rt][nt] = mma_step_mx(a, b.b[nt], b.xa[rt], b.xb[nt], acc[rt][nt]);
-                } else if constexpr (QUANT == 2) {
+                if constexpr (QUANT == 2) {
                     const f32x4 part = mma_step<QUANT>(a, b.b[nt], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[rt][nt][i] += part[i] * (b.sa[rt][i] * b.sw[nt]);
@@ -238,6 +226,133 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[RT][NT], const uint8_t
         if (i + s < nsteps) compute(bf[s]);
 }
 
+// MXFP4 scales. A scale row holds one E8M0 byte per 32-element block, 8 per
+// K step; with the MXFP4 piece layout, dword 2j of a chunk of 8 steps holds
+// the scales of lane groups 0..3 for the first MFMA of step j (byte lg) and
+// dword 2j + 1 those for the second. Lane group lg loads dwords 4 lg .. 4 lg + 3
+// of the chunk (16 bytes); this turns them into the lane's own bytes: on
+// return d[m] = [first(2m), second(2m), first(2m+1), second(2m+1)] of lane
+// group lg, and the MFMA picks the byte by op_sel. One 16-byte scale load per
+// tile covers 8 steps.
+__device__ __forceinline__ void mx_chunk_to_lanes(uint32_t (&d)[4]) {
+    // in the lane: t_b = byte b of d0, d1, d2, d3 (what lane group b needs
+    // from this lane group); v_perm byte selectors index {src0 : src1} with
+    // src1 as bytes 0..3
+    const uint32_t u0 = __builtin_amdgcn_perm(d[1], d[0], 0x06020400u);  // d0.b0 d1.b0 d0.b2 d1.b2
+    const uint32_t u1 = __builtin_amdgcn_perm(d[1], d[0], 0x07030501u);  // d0.b1 d1.b1 d0.b3 d1.b3
+    const uint32_t u2 = __builtin_amdgcn_perm(d[3], d[2], 0x06020400u);
+    const uint32_t u3 = __builtin_amdgcn_perm(d[3], d[2], 0x07030501u);
+    const uint32_t t0 = __builtin_amdgcn_perm(u2, u0, 0x05040100u);
+    const uint32_t t1 = __builtin_amdgcn_perm(u3, u1, 0x05040100u);
+    const uint32_t t2 = __builtin_amdgcn_perm(u2, u0, 0x07060302u);
+    const uint32_t t3 = __builtin_amdgcn_perm(u3, u1, 0x07060302u);
+    // across the four 16-lane rows (lane groups): register m of row r takes
+    // register r of row m. permlane32_swap exchanges rows 2-3 of its first
+    // operand with rows 0-1 of its second, permlane16_swap rows 1 and 3 of
+    // the first with rows 0 and 2 of the second.
+    const auto s02 = __builtin_amdgcn_permlane32_swap(t0, t2, false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(t1, t3, false, false);
+    const auto q01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    const auto q23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    d[0] = q01[0];
+    d[1] = q01[1];
+    d[2] = q23[0];
+    d[3] = q23[1];
+}
+
+// The MXFP4 K loop: steps of 128 bytes (K = 256), two scaled E2M1 MFMAs
+// (format 4, K = 128 each) per step and tile pair, block scales applied
+// inside the MFMA. Chunks of 8 steps, each with one scale load per tile
+// issued a step ahead; the data ring is the same as stream_kloop's with
+// DEPTH 2. Chunks start at a chunk given by rot; a last, partial chunk
+// skips its missing steps (prefetches are clamped to the last step, and
+// scale bytes past the end of a row are never used).
+template <int RT, int RTL, int NT>
+__device__ __forceinline__ void stream_kloop_mx(f32x4 (&acc)[RT][NT], const uint8_t *const (&arow)[RT],
+                                                Rsrc wr, int wvoff, const int (&wtile)[NT], Rsrc axr,
+                                                const int (&axvoff)[RT], Rsrc wxr, int wxvoff,
+                                                const int (&wxtile)[NT], int kbeg, int kend, int rot) {
+    constexpr int KS = 256, CH = 8, SECOND = Piece<3>::second;
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const int nsteps = (kend - kbeg) / KS;
+    if (nsteps <= 0) return;
+    const int nch = (nsteps + CH - 1) / CH;
+    rot %= nch;
+    const int xbase = kbeg / 32;
+    Frag fa[2][RT], fb[2][NT];
+    uint32_t ra[RT][4], rb[NT][4];  // chunk in flight
+    uint32_t xa[RT][4], xb[NT][4];  // chunk in use
+    auto chunk = [&](int i) {
+        const int c = i + rot;
+        return c >= nch ? c - nch : c;
+    };
+    auto load_scales = [&](int c) {
+        const int so = xbase + 64 * c;
+#pragma unroll
+        for (int rt = 0; rt < RTL; ++rt) {
+            const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(axr, axvoff[rt], so, 0));
+            ra[rt][0] = v.x; ra[rt][1] = v.y; ra[rt][2] = v.z; ra[rt][3] = v.w;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const u32x4 v =
+                __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wxr, wxvoff, wxtile[nt] + so, 0));
+            rb[nt][0] = v.x; rb[nt][1] = v.y; rb[nt][2] = v.z; rb[nt][3] = v.w;
+        }
+    };
+    auto load_data = [&](int buf, int st) {
+        const int kb = (kbeg + st * KS) / 2;  // bytes
+#pragma unroll
+        for (int rt = 0; rt < RTL; ++rt) fa[buf][rt] = load_frag<SECOND>(arow[rt] + kb);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) fb[buf][nt] = load_frag_buf<SECOND>(wr, wvoff, wtile[nt] + kb);
+    };
+    load_scales(chunk(0));
+    load_data(0, CH * chunk(0));
+    for (int i = 0; i < nch; ++i) {
+        const int c = chunk(i);
+        const int cn = chunk(min(i + 1, nch - 1));
+#pragma unroll
+        for (int rt = 0; rt < RTL; ++rt) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) xa[rt][m] = ra[rt][m];
+            mx_chunk_to_lanes(xa[rt]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) xb[nt][m] = rb[nt][m];
+            mx_chunk_to_lanes(xb[nt]);
+        }
+        static_for<CH>([&](auto sc) {
+            constexpr int st = decltype(sc)::value;
+            constexpr int cur = st & 1, m = st / 2, sel = 2 * (st & 1);
+            if constexpr (st == CH - 1) load_scales(cn);
+            load_data(cur ^ 1, st == CH - 1 ? CH * cn : min(CH * c + st + 1, nsteps - 1));
+            // keep the prefetch above the MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            if (CH * c + st < nsteps) {
+#pragma unroll
+                for (int rt = 0; rt < RTL; ++rt) {
+                    const Frag &a = fa[cur][rt];
+                    const i32x8 alo = {(int)a.lo.x, (int)a.lo.y, (int)a.lo.z, (int)a.lo.w, 0, 0, 0, 0};
+                    const i32x8 ahi = {(int)a.hi.x, (int)a.hi.y, (int)a.hi.z, (int)a.hi.w, 0, 0, 0, 0};
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const Frag &b = fb[cur][nt];
+                        const i32x8 blo = {(int)b.lo.x, (int)b.lo.y, (int)b.lo.z, (int)b.lo.w, 0, 0, 0, 0};
+                        const i32x8 bhi = {(int)b.hi.x, (int)b.hi.y, (int)b.hi.z, (int)b.hi.w, 0, 0, 0, 0};
+                        acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            alo, blo, acc[rt][nt], 4, 4, sel, (int)xa[rt][m], sel, (int)xb[nt][m]);
+                        acc[rt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            ahi, bhi, acc[rt][nt], 4, 4, sel + 1, (int)xa[rt][m], sel + 1, (int)xb[nt][m]);
+                    }
+                }
+            }
+        });
+    }
+}
+
 // RT: 16-row tiles per block (B = 16 * RT). CT: 16-column tiles per wave
 // (GEMM1: CT gate tiles + CT matching up tiles).
 template <int QUANT, int RT, int CT, bool GEMM1>
@@ -257,7 +372,8 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
     const int e = p.seid[blk];
     if (e < 0) return;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int sentinel = p.T * p.k;
     const int K = GEMM1 ? p.d : p.f;
@@ -267,7 +383,10 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
     const int kend = min(K, kbeg + p.kchunk);
     const int slot0 = blk * p.B;
 
-    // rows of this lane's A fragments, and which 16-row tiles hold real rows
+    // rows of this lane's A fragments, and which 16-row tiles hold real rows.
+    // A padding row (sentinel slot) of GEMM1 reads token 0: MFMA output rows
+    // are independent, and the epilogue's results for padding slots are never
+    // consumed, so the row needs no mask.
     const uint8_t *arow[RT];
     bool arow_ok[RT];
     bool live[RT];
@@ -281,19 +400,22 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
         if (GEMM1) {
             arow_ok[rt] = a < sentinel;
             const int t = arow_ok[rt] ? a / p.k : 0;
-            arow[rt] = p.a + Elem<QUANT>::off((size_t)t * K) + lg * 32;
+            arow[rt] = p.a + Elem<QUANT>::off((size_t)t * K) + Piece<QUANT>::first(lg);
         } else {
             arow_ok[rt] = true;
-            arow[rt] = p.a + Elem<QUANT>::off((size_t)slot * K) + lg * 32;
+            arow[rt] = p.a + Elem<QUANT>::off((size_t)slot * K) + Piece<QUANT>::first(lg);
         }
     }
-    const uint8_t *wrow[NT];
-    const uint8_t *wexp = p.w + Elem<QUANT>::off((size_t)e * Ntot * K);
+    // first weight row of each tile (wave-uniform)
+    int wrow0[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int n = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16 + lr;
-        wrow[nt] = wexp + Elem<QUANT>::off((size_t)n * K) + lg * 32;
-    }
+    for (int nt = 0; nt < NT; ++nt) wrow0[nt] = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16;
+    const int kbytes = (int)Elem<QUANT>::off(K);
+    const Rsrc wr = make_rsrc(p.w + Elem<QUANT>::off((size_t)e * Ntot * K), (size_t)Ntot * kbytes);
+    const int wvoff = lr * kbytes + Piece<QUANT>::first(lg);
+    int wtile[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) wtile[nt] = wrow0[nt] * kbytes;
 
     f32x4 acc[RT][NT];
 #pragma unroll
@@ -319,7 +441,7 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
     }
 
     // scale rows of the block-scaled product (sentinel rows read token 0's
-    // scales; their A fragment is zero, so the product stays zero)
+    // scales; their products land in padding rows, which nothing consumes)
     const float *sap[RT][4];
     const float *swp[NT];
     if constexpr (QUANT == 2) {
@@ -336,31 +458,35 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
     }
     // K steps start at a step given by the column tile: weight rows a power
     // of two apart otherwise meet in the same HBM channels at the same moment
-    // MXFP4 scale rows: the lane's blocks of a step are 2 lg and 2 lg + 1
-    const uint8_t *axs[RT];
-    const uint8_t *wxs[NT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) axs[rt] = nullptr;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wxs[nt] = nullptr;
+    const int rot = p.rotate ? (int)blockIdx.x : 0;
     if constexpr (QUANT == 3) {
+        // scale rows: A by token (GEMM1; padding rows read token 0) or slot,
+        // weights by the tile's rows; lane group lg reads bytes 16 lg .. of
+        // each 64-byte chunk
+        int axvoff[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const size_t r = GEMM1 ? (size_t)(arow_ok[rt] ? a_of_lane[rt] / p.k : 0)
-                                   : (size_t)(slot0 + rt * 16 + lr);
-            axs[rt] = p.a_mx + r * (K / 32) + 2 * lg;
+            const int r = GEMM1 ? (arow_ok[rt] ? a_of_lane[rt] / p.k : 0) : slot0 + rt * 16 + lr;
+            axvoff[rt] = r * (K / 32) + 16 * lg;
         }
+        const Rsrc axr = make_rsrc(p.a_mx, (size_t)p.a_rows * (K / 32));
+        const Rsrc wxr = make_rsrc(p.w_mx + (size_t)e * Ntot * (K / 32), (size_t)Ntot * (K / 32));
+        const int wxvoff = lr * (K / 32) + 16 * lg;
+        int wxtile[NT];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int n = (GEMM1 && nt >= CT ? p.f : 0) + n0 + (nt % CT) * 16 + lr;
-            wxs[nt] = p.w_mx + ((size_t)e * Ntot + n) * (K / 32) + 2 * lg;
-        }
+        for (int nt = 0; nt < NT; ++nt) wxtile[nt] = wrow0[nt] * (K / 32);
+        if (RT == 2 && live[RT - 1])
+            stream_kloop_mx<RT, RT, NT>(acc, arow, wr, wvoff, wtile, axr, axvoff, wxr, wxvoff, wxtile, kbeg,
+                                        kend, rot);
+        else
+            stream_kloop_mx<RT, 1, NT>(acc, arow, wr, wvoff, wtile, axr, axvoff, wxr, wxvoff, wxtile, kbeg,
+                                       kend, rot);
+    } else {
+        if (RT == 2 && live[RT - 1])
+            stream_kloop<QUANT, RT, RT, NT>(acc, arow, wr, wvoff, wtile, sap, swp, kbeg, kend, rot);
+        else
+            stream_kloop<QUANT, RT, 1, NT>(acc, arow, wr, wvoff, wtile, sap, swp, kbeg, kend, rot);
     }
-    const int rot = p.rotate ? (int)blockIdx.x : 0;
-    if (RT == 2 && live[RT - 1])
-        stream_kloop<QUANT, RT, RT, NT>(acc, arow, arow_ok, wrow, sap, swp, axs, wxs, kbeg, kend, rot);
-    else
-        stream_kloop<QUANT, RT, 1, NT>(acc, arow, arow_ok, wrow, sap, swp, axs, wxs, kbeg, kend, rot);
 
     // ------------------------------------------------------------ epilogue
     if constexpr (GEMM1) {
@@ -512,16 +638,32 @@ hipError_t dispatch(const StreamParams &p, int quant, int RT, int CT, dim3 grid,
 
 }  // namespace
 
-// K (d for GEMM1, f for GEMM2) in whole 128-byte steps; GEMM1's h columns
-// in whole workgroups (64 per column tile of each wave)
+// Supported shapes: K (d for GEMM1, f for GEMM2) in whole 128-byte steps;
+// GEMM1's h columns in whole workgroups (64 per column tile of each wave);
+// one expert's weights below 2 GiB (buffer offsets).
+static bool expert_slice_fits(const GemmShape &sh, size_t rows, size_t K) {
+    const size_t elems = rows * K;
+    const size_t bytes = sh.quant == 0 ? 2 * elems : (sh.quant == 3 ? elems / 2 : elems);
+    return bytes < ((size_t)1 << 31);
+}
+
+// MXFP4 activation scales (a_rows x K/32 bytes) are read through a buffer
+// resource as well
+static bool mx_scales_fit(const GemmShape &sh, size_t a_rows, size_t K) {
+    return sh.quant != 3 || a_rows * (K / 32) < ((size_t)1 << 31);
+}
+
 bool stream_gemm1_supported(const GemmShape &sh) {
     const int kstep = sh.quant == 3 ? 256 : 128;
-    return (sh.B == 16 || sh.B == 32) && sh.f % 128 == 0 && sh.d % kstep == 0;
+    return (sh.B == 16 || sh.B == 32) && sh.f % 128 == 0 && sh.d % kstep == 0 &&
+           expert_slice_fits(sh, 2 * (size_t)sh.f, sh.d) && mx_scales_fit(sh, sh.T, sh.d);
 }
 
 bool stream_gemm2_supported(const GemmShape &sh) {
     const int kstep = sh.quant == 3 ? 256 : 128;
-    return (sh.B == 16 || sh.B == 32) && sh.f % kstep == 0 && sh.d % 128 == 0;
+    return (sh.B == 16 || sh.B == 32) && sh.f % kstep == 0 && sh.d % 128 == 0 &&
+           expert_slice_fits(sh, sh.d, sh.f) &&
+           mx_scales_fit(sh, (size_t)sh.T * sh.k + (size_t)sh.E * sh.B - sh.k, sh.f);
 }
 
 hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
@@ -541,6 +683,7 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
     p.zero = g.zero;
     p.zero_n = g.zero_n;
     p.a_mx = g.a_mx;
+    p.a_rows = sh.T;
     p.w_mx = g.w13_mx;
     p.out_mx = g.h_mx;
     // quant 2: one 128-column quant block per workgroup; quant 3: one
@@ -565,6 +708,7 @@ hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream
     p.seid = g.sorted_expert_ids;
     p.out = g.acc;
     p.a_mx = g.h_mx;
+    p.a_rows = sh.T * sh.k + sh.E * sh.B - sh.k;
     p.w_mx = g.w2_mx;
     p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
     const int KS = sh.quant == 0 ? 64 : (sh.quant == 3 ? 256 : 128);

@@ -136,19 +136,6 @@ __device__ __forceinline__ f32x16 mma32_fp8(const u32x4 &a0, const u32x4 &a1, co
 // rows). QUANT 0 (bf16) or 1 (e4m3, per-row activation scale and
 // per-channel weight scale applied in the epilogue). The 8 waves form a
 // WM x WN grid, each wave owning (BM / WM) rows x 64 weight rows.
-template <int I>
-struct IC {
-    static constexpr int value = I;
-};
-// f(IC<0>{}), ..., f(IC<N-1>{})
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (I < N) {
-        f(IC<I>{});
-        static_for<N, I + 1>(f);
-    }
-}
-
 template <int QUANT, bool GEMM1, int BM, int TN, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     constexpr int NTHR = 64 * WAVES;
