@@ -156,7 +156,7 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
     // prefill, 560 tiles of 256 x 256: 1110 -> 1015 us). e4m3 at one full
     // round of tiles got slower (121 -> 130 us).
     if (use_tiled(B) && base >= cu)
-        return (quant == 0 && base < 4 * (int64_t)cu && f / KS >= 8) ? 2 : 1;
+        return ((quant == 0 || quant == MOE_QUANT_MXFP4) && base < 4 * (int64_t)cu && f / KS >= 8) ? 2 : 1;
     const int64_t target = use_tiled(B) ? cu : 2 * (int64_t)cu;
     int ks = (int)std::min<int64_t>((target + base - 1) / base, f / KS / 4);
     return std::max(1, ks);
@@ -171,12 +171,15 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
 // e4m3 takes 256-row blocks from about 100 rows per expert on: its 256 x 128
 // tiles then read each expert's weights once, and the MFMAs of padding-only
 // row quarters are skipped.
-int choose_B(int T, int E, int k, int quant) {
+// MXFP4 goes to the tiled kernels like bf16 when d and f are multiples of
+// 512 (its K pairs), else it stays on the streaming kernel.
+int choose_B(int T, int d, int f, int E, int k, int quant) {
     const double rows = (double)T * k / E;
-    if (quant == 0 && rows >= 512) return 256;
+    const bool mx_tiled = quant == MOE_QUANT_MXFP4 && d % 512 == 0 && f % 512 == 0;
+    if ((quant == 0 || mx_tiled) && rows >= 512) return 256;
     if (quant == 1 && rows >= 96) return 256;
-    // e4m3 1x128 and MXFP4 run on the streaming kernel only
-    const bool tiled_ok = quant == 0 || quant == 1;
+    // e4m3 1x128 runs on the streaming kernel only
+    const bool tiled_ok = quant == 0 || quant == 1 || mx_tiled;
     if (tiled_ok && rows >= 96) return 128;
     if (tiled_ok && rows >= 48) return 64;
     if (rows <= 4) return 16;
@@ -185,7 +188,7 @@ int choose_B(int T, int E, int k, int quant) {
 
 Config choose(int T, int d, int f, int E, int k, int quant, int cu) {
     Config c;
-    c.B = choose_B(T, E, k, quant);
+    c.B = choose_B(T, d, f, E, k, quant);
     c.stage = 2;
     c.ksplit = auto_ksplit(T, d, f, E, k, c.B, quant, cu);
     return c;

@@ -82,6 +82,10 @@ struct TiledParams {
     float *zero;
     size_t zero_n;
     float *yrows;   // GEMM2 without K-split: weighted rows [T*k, d] by assignment, stored (no atomics)
+    // quant 3 (MXFP4): E8M0 scales of A [rows, K/32] and of the weights
+    // [E, N, K/32]; GEMM1 writes h's [P, f/32]
+    const uint8_t *a_mx, *w_mx;
+    uint8_t *out_mx;
 };
 
 // Chunk position of (row, chunk) inside the row's 128 bytes (an involution
@@ -131,6 +135,17 @@ __device__ __forceinline__ f32x16 mma32_fp8(const u32x4 &a0, const u32x4 &a1, co
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
 }
 
+// E2M1 x E2M1 over K = 64 (16 bytes per lane: one LDS chunk, which is one
+// 32-element MX block) with the lanes' E8M0 scales in byte OPSEL of xa / xb.
+template <int OPSEL>
+__device__ __forceinline__ f32x16 mma32_fp4(const u32x4 &a, const u32x4 &b, uint32_t xa, uint32_t xb,
+                                            f32x16 acc) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, OPSEL, (int)xa, OPSEL, (int)xb);
+}
+
 // BM: rows per tile (64, 128 or 256); TN: weight rows per tile (256, or 128
 // for 256-row tiles; GEMM1 takes TN/2 gate rows and the TN/2 matching up
 // rows). QUANT 0 (bf16) or 1 (e4m3, per-row activation scale and
@@ -139,8 +154,9 @@ __device__ __forceinline__ f32x16 mma32_fp8(const u32x4 &a0, const u32x4 &a1, co
 template <int QUANT, bool GEMM1, int BM, int TN, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     constexpr int NTHR = 64 * WAVES;
-    constexpr int ES = QUANT == 0 ? 2 : 1;
-    constexpr int KS = ROWB / ES;               // K elements per step
+    constexpr bool MX = QUANT == 3;             // MXFP4: E2M1 two per byte, E8M0 per 32
+    auto eb = [](size_t n) -> size_t { return QUANT == 0 ? 2 * n : (MX ? n / 2 : n); };  // bytes of n elements
+    constexpr int KS = QUANT == 0 ? 64 : (MX ? 256 : 128);  // K elements per 128-byte step
     constexpr int ROWS = BM + TN;               // LDS rows per stage (activations first)
     constexpr int BUF = ROWS * ROWB;            // bytes per stage
     constexpr int NQ = BUF / 1024 / WAVES;      // DMA instructions per wave per step
@@ -148,11 +164,18 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     constexpr int WN = TN / 64, WM = WAVES / WN;
     constexpr int RT = BM / WM / 32;            // 32-row tiles per wave
     constexpr int CT = 2;                       // 32-column tiles per wave
-    constexpr int NBUF = BUF <= 48 * 1024 ? 3 : 2;  // LDS stages (of 160 KB of LDS)
+    // LDS stages (of 160 KB of LDS); MXFP4 keeps two, so that every step
+    // ends with all of its loads complete (its scale loads come every other
+    // step)
+    constexpr int NBUF = (BUF <= 48 * 1024 && !MX) ? 3 : 2;
+    // MXFP4 scales: per pair of K steps, 16 bytes per tile row (8 per step),
+    // in two slots after the stages
+    constexpr int SSLOT = MX ? ROWS * 16 : 0;
     constexpr int HROW = TN + 16;               // bytes per row of the staged h tile (+16 against bank conflicts)
     static_assert(BM % (8 * WAVES) == 0 && TN % 64 == 0 && RT >= 1 && BM <= NTHR, "tile shape");
     static_assert(BM * HROW <= NBUF * BUF, "h staging");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * BUF];
+    static_assert(!MX || ROWS <= NTHR, "one scale row per thread");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * BUF + 2 * SSLOT];
     __shared__ __attribute__((aligned(16))) int row_asg[BM];     // assignment t*k+j, or -1 for padding
     __shared__ __attribute__((aligned(16))) float row_scale[BM];
 
@@ -214,7 +237,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // blocks BM/2 apart, so that when the second half of a tile is padding
     // (whose MFMAs are skipped) every SIMD still has one busy wave
     const int wn = wave % WN, wm = wave / WN;
-    const uint8_t *wexp = p.w + (size_t)e * Ntot * K * ES;
+    const uint8_t *wexp = p.w + eb((size_t)e * Ntot * K);
+    const uint32_t kbytes = (uint32_t)eb(K);
 
     // Instruction i of wave w fills the stage's kilobyte w + 8 i, i.e. 8
     // rows; lane l writes row 8 (w + 8 i) + l / 8 at chunk position l % 8,
@@ -228,6 +252,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     for (int i = 0; i < NQA; ++i) {
         const int row = 8 * (wave + WAVES * i) + (lane >> 3);
         arow_src[i] = GEMM1 ? p.sorted_ids[slot0 + row] : slot0 + row;
+    }
+    // MXFP4 scale rows: wave w copies tile rows 64 w .. 64 w + 63 (all
+    // activation rows or all weight rows, BM being a multiple of 64), lane l
+    // row 64 w + l, 16 bytes (a pair of K steps) at a time
+    const bool xwave = MX && 64 * wave < ROWS;
+    const bool xwave_a = 64 * wave < BM;
+    int xsrc = 0;
+    if constexpr (MX) {
+        const int row = 64 * wave + lane;
+        if (xwave_a) {
+            xsrc = GEMM1 ? p.sorted_ids[slot0 + row] : slot0 + row;
+        } else {
+            const int rb = row - BM;
+            xsrc = GEMM1 ? (rb < TN / 2 ? 0 : p.f - TN / 2) + nt * (TN / 2) + rb : nt * TN + rb;
+        }
     }
     // live 32-row groups of the tile: padding sits at the end of the
     // expert's segment, so they form a prefix (bit g: row 32 g is real)
@@ -259,12 +298,23 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
         const int row = 8 * (wave + WAVES * i) + (lane >> 3);
         const int rb = row - BM;   // 0..TN-1
         const int n = GEMM1 ? (rb < TN / 2 ? 0 : p.f - TN / 2) + nt * (TN / 2) + rb : nt * TN + rb;
-        goff[i] = (uint32_t)n * (uint32_t)(K * ES) + swz(row, lane & 7) * 16;
+        goff[i] = (uint32_t)n * kbytes + swz(row, lane & 7) * 16;
     }
     const uint32_t m0w = lds_addr(lds) + (uint32_t)wave * 1024u;
+    // MXFP4 scale copies: pair q of K steps (steps 2q, 2q + 1 of this K
+    // range) into slot q % 2
+    const uint8_t *xbase = MX ? (xwave_a ? p.a_mx : p.w_mx + (size_t)e * Ntot * (K / 32)) : nullptr;
+    uint32_t xoff = 0;
+    auto issue_scales = [&](int q) {
+        if constexpr (MX) {
+            if (xwave)
+                dma16(xbase, xoff + (uint32_t)(kbeg / 32 + 16 * q),
+                      lds_addr(lds) + (uint32_t)(NBUF * BUF + (q & 1) * SSLOT) + (uint32_t)wave * 1024u);
+        }
+    };
     auto issue_part = [&](int buf, int kk, int i0, int i1) {
-        const uint8_t *ab = p.a + (size_t)kk * ES;
-        const uint8_t *bb = wexp + (size_t)kk * ES;
+        const uint8_t *ab = p.a + eb(kk);
+        const uint8_t *bb = wexp + eb(kk);
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             if (i < i0 || i >= i1) continue;
@@ -279,7 +329,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // and banks (rows a power of two apart otherwise meet in the same ones).
     // Tiles of one column tile keep the same order, so the sort blocks of an
     // expert still share each weight step in L2.
-    const int rot = (p.rotate && nsteps > 0) ? nt % nsteps : 0;
+    const int rot = (p.rotate && nsteps > 0 && !MX) ? nt % nsteps : 0;
     auto kof = [&](int i) {
         int st = min(i, nsteps - 1) + rot;
         if (st >= nsteps) st -= nsteps;
@@ -296,7 +346,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
         const int row = 8 * (wave + WAVES * i) + (lane >> 3);
         int src = arow_src[i];
         if constexpr (GEMM1) src = src < sentinel ? src / p.k : 0;
-        goff[i] = (uint32_t)src * (uint32_t)(K * ES) + swz(row, lane & 7) * 16;
+        goff[i] = (uint32_t)src * kbytes + swz(row, lane & 7) * 16;
+    }
+    if constexpr (MX) {
+        int src = xsrc;
+        if (GEMM1 && xwave_a) src = src < sentinel ? src / p.k : 0;
+        xoff = (uint32_t)src * (uint32_t)(K / 32);
     }
     const bool meta_ok = meta_a < sentinel;
     const int meta_asg = meta_ok ? meta_a : -1;
@@ -339,10 +394,32 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // fragments of sub-step s+1 are read while the MFMAs of sub-step s run.
     // e4m3: CH/4 sub-steps of K = 64 (lane half lh takes chunks 4s + 2lh and
     // 4s + 2lh + 1), all fragments read up front.
-    auto compute = [&](int buf) {
+    // MXFP4: 4 sub-steps of K = 64; lane half lh takes chunk 4 lh + s, i.e.
+    // MX block 4 lh + s of the step, so the lane's four E8M0 scales of the
+    // step are one dword of the scale row (byte s for sub-step s). Step j
+    // reads its scales from slot (j / 2) % 2 at byte 8 (j % 2).
+    auto compute = [&](int buf, int j) {
         if (!wave_live) return;
         const uint8_t *base = lds + buf * BUF;
-        if constexpr (QUANT == 0) {
+        if constexpr (MX) {
+            const uint8_t *sb = lds + NBUF * BUF + ((j >> 1) & 1) * SSLOT + 8 * (j & 1) + 4 * lh;
+            uint32_t xa[RT], xb[CT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const uint32_t *>(sb + arow[rt] * 16);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) xb[ct] = *reinterpret_cast<const uint32_t *>(sb + (BM + brow[ct]) * 16);
+            u32x4 fa[2][RT], fb[2][CT];
+            frags_at(base, 4 * lh, fa[0], fb[0]);
+            static_for<4>([&](auto sc) {
+                constexpr int sub = decltype(sc)::value;
+                if constexpr (sub + 1 < 4) frags_at(base, 4 * lh + sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        acc[rt][ct] = mma32_fp4<sub>(fa[sub & 1][rt], fb[sub & 1][ct], xa[rt], xb[ct], acc[rt][ct]);
+            });
+        } else if constexpr (QUANT == 0) {
             constexpr int NSUB = CH / 2;
             u32x4 fa[2][RT], fb[2][CT];
             frags_at(base, lh, fa[0], fb[0]);
@@ -393,6 +470,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
         if (nsteps <= 0) return;
 #pragma unroll
         for (int b = 0; b < NBUF - 1; ++b) issue_part(b, kof(b), 0, NQAL);
+        issue_scales(0);
         // stage 0 has landed once only the activation rows of the later
         // prologue stages are pending (everything older has completed)
         wait_vmem<NQAL * (NBUF - 2)>();
@@ -401,7 +479,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             const int nb = (b + NBUF - 1) % NBUF, kk = kof(j + NBUF - 1);
             issue_part(nb, kk, 0, NQAL);
             issue_part(nb, kk, NQA, NQ);
-            compute(b);
+            // MXFP4 (two stages, even step count, no rotation): with step
+            // j + 1 even, its pair's scales
+            if (MX && b == 1 && j + 1 < nsteps) issue_scales((j + 1) / 2);
+            compute(b, j);
             wait_vmem<NQL * (NBUF - 2)>();
             __syncthreads();
         };
@@ -454,9 +535,48 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             }
         }
         __syncthreads();
+        uint8_t *h = reinterpret_cast<uint8_t *>(p.out);
+        if constexpr (MX) {
+            // one thread per (row, 32-column MX block): the block's amax
+            // gives its E8M0 scale, the codes go out as 16 bytes
+            constexpr int NBK = TN / 2 / 32;
+            for (int idx = tid; idx < BM * NBK; idx += NTHR) {
+                const int row = idx / NBK, bk = idx % NBK;
+                if (row_asg[row] < 0) continue;
+                float v[32];
+                float m = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 q = *reinterpret_cast<const u32x4 *>(hs + row * HROW + bk * 64 + c * 16);
+                    const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[8 * c + 2 * i] = bf16_bits_to_f32(w4[i] & 0xffffu);
+                        v[8 * c + 2 * i + 1] = bf16_bits_to_f32(w4[i] >> 16);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+                const int E = mx_block_exp(m);
+                const float inv = mx_inv_scale(E);
+                uint32_t cw[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    uint32_t wv = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) wv |= e2m1_code(v[8 * c + i] * inv) << (4 * i);
+                    cw[c] = wv;
+                }
+                const size_t slot = (size_t)slot0 + row;
+                const int col0 = nt * (TN / 2) + bk * 32;
+                *reinterpret_cast<u32x4 *>(h + slot * (p.f / 2) + col0 / 2) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+                p.out_mx[slot * (p.f / 32) + col0 / 32] = (uint8_t)(E + 127);
+            }
+            clear_zero();
+            return;
+        }
         // TN/16 lanes per row, 16 bytes each: the tile's TN-byte row segments
         constexpr int RC = TN / 16;
-        uint8_t *h = reinterpret_cast<uint8_t *>(p.out);
 #pragma unroll
         for (int it = 0; it < BM * RC / NTHR; ++it) {
             const int idx = tid + NTHR * it, row = idx / RC, c = idx % RC;
@@ -520,9 +640,12 @@ hipError_t dispatch_shape(const TiledParams &p, int BM, int TN, dim3 grid, hipSt
         k_gemm_tiled<QUANT, GEMM1, 128, 256, 8><<<grid, 512, 0, s>>>(p);
     else if (BM == 256 && TN == 128)
         k_gemm_tiled<QUANT, GEMM1, 256, 128, 8><<<grid, 512, 0, s>>>(p);
-    else if (QUANT == 0 && BM == 256 && TN == 256)
-        k_gemm_tiled<0, GEMM1, 256, 256, 8><<<grid, 512, 0, s>>>(p);
-    else
+    else if (BM == 256 && TN == 256) {
+        if constexpr (QUANT == 0 || QUANT == 3)
+            k_gemm_tiled<QUANT, GEMM1, 256, 256, 8><<<grid, 512, 0, s>>>(p);
+        else
+            return hipErrorInvalidValue;
+    } else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -531,6 +654,7 @@ template <bool GEMM1>
 hipError_t dispatch(const TiledParams &p, int quant, int BM, int TN, dim3 grid, hipStream_t s) {
     if (quant == 0) return dispatch_shape<0, GEMM1>(p, BM, TN, grid, s);
     if (quant == 1) return dispatch_shape<1, GEMM1>(p, BM, TN, grid, s);
+    if (quant == 3) return dispatch_shape<3, GEMM1>(p, BM, TN, grid, s);
     return hipErrorInvalidValue;
 }
 
@@ -541,16 +665,19 @@ unsigned grid_tiles(int NB, int ntiles) {
 
 }  // namespace
 
+// MXFP4 runs K in pairs of 128-byte steps (512 elements), so d and f must
+// be multiples of 512
 bool tiled_gemm_supported(const GemmShape &sh) {
-    return (sh.B == 64 || sh.B == 128 || sh.B == 256) && (sh.quant == 0 || sh.quant == 1) &&
-           sh.f % 128 == 0 && sh.d % 256 == 0;
+    if (!(sh.B == 64 || sh.B == 128 || sh.B == 256)) return false;
+    if (sh.quant == 3) return sh.f % 512 == 0 && sh.d % 512 == 0;
+    return (sh.quant == 0 || sh.quant == 1) && sh.f % 128 == 0 && sh.d % 256 == 0;
 }
 
 // Tile shape (rows BM, weight rows TN) for sort blocks of B rows; bm / tn
 // > 0 request a shape, which must be one of the instantiated ones and BM must
 // divide B. The library's choice: a 64/128-row block is one 64/128 x 256 tile;
-// a 256-row block runs bf16 as 256 x 256 tiles (a third fewer operand bytes
-// per MFMA than 128 x 256) and e4m3 as 256 x 128 tiles (whose weight columns
+// a 256-row block runs bf16 and MXFP4 as 256 x 256 tiles (a third fewer
+// operand bytes per MFMA than 128 x 256) and e4m3 as 256 x 128 tiles (whose weight columns
 // each cover a whole expert of up to 256 rows, so every weight byte leaves
 // HBM once).
 struct TileShape {
@@ -560,7 +687,7 @@ struct TileShape {
 TileShape tile_shape(int B, int quant, bool gemm1, int bm, int tn) {
     auto valid = [&](int m, int n) {
         if (m <= 0 || m > B || B % m) return false;
-        return (n == 256 && (m == 64 || m == 128 || (m == 256 && quant == 0))) || (n == 128 && m == 256);
+        return (n == 256 && (m == 64 || m == 128 || (m == 256 && quant != 1))) || (n == 128 && m == 256);
     };
     if (valid(bm, tn)) return {bm, tn};
     if (B < 256) return {B, 256};
@@ -593,6 +720,9 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s)
     p.rotate = MOE_TILED_ROTATE & (1 << (2 * sh.quant));
     p.zero = g.zero;
     p.zero_n = g.zero_n;
+    p.a_mx = g.a_mx;
+    p.w_mx = g.w13_mx;
+    p.out_mx = g.h_mx;
     const TileShape ts = tile_shape(sh.B, sh.quant, true, bm, tn);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + ts.bm - 1) / ts.bm;
@@ -600,12 +730,21 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s)
     return dispatch<true>(p, sh.quant, ts.bm, ts.tn, grid, s);
 }
 
-// Parts of K for a requested split: ceil(steps / ceil(steps / ksplit)), each
+// K steps (128 bytes per row) per part of a requested split; MXFP4 parts
+// hold whole pairs of steps.
+static int tiled_steps_per_part(int f, int quant, int ksplit) {
+    const int steps = f / (quant == 0 ? 64 : (quant == 3 ? 256 : 128));
+    ksplit = ksplit < 1 ? 1 : (ksplit > steps ? steps : ksplit);
+    int steps_per = (steps + ksplit - 1) / ksplit;
+    if (quant == 3) steps_per += steps_per & 1;
+    return steps_per;
+}
+
+// Parts of K for a requested split: ceil(steps / steps per part), each
 // non-empty.
 int tiled_gemm2_parts(int f, int quant, int ksplit) {
-    const int steps = f / (quant == 0 ? 64 : 128);
-    ksplit = ksplit < 1 ? 1 : (ksplit > steps ? steps : ksplit);
-    const int steps_per = (steps + ksplit - 1) / ksplit;
+    const int steps = f / (quant == 0 ? 64 : (quant == 3 ? 256 : 128));
+    const int steps_per = tiled_steps_per_part(f, quant, ksplit);
     return (steps + steps_per - 1) / steps_per;
 }
 
@@ -622,12 +761,11 @@ hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hi
     p.num_valid = g.num_valid;
     p.out = g.acc;
     p.yrows = g.yrows;
+    p.a_mx = g.h_mx;
+    p.w_mx = g.w2_mx;
     p.T = sh.T; p.d = sh.d; p.f = sh.f; p.k = sh.k; p.B = sh.B;
-    const int KS = sh.quant == 0 ? 64 : 128;
-    const int steps = sh.f / KS;
-    if (ksplit < 1) ksplit = 1;
-    if (ksplit > steps) ksplit = steps;
-    const int steps_per = (steps + ksplit - 1) / ksplit;
+    const int KS = sh.quant == 0 ? 64 : (sh.quant == 3 ? 256 : 128);
+    const int steps_per = tiled_steps_per_part(sh.f, sh.quant, ksplit);
     p.kchunk = steps_per * KS;
     p.rotate = MOE_TILED_ROTATE & (2 << (2 * sh.quant));
     ksplit = tiled_gemm2_parts(sh.f, sh.quant, ksplit);

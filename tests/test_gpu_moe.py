@@ -26,6 +26,10 @@ SMALL = [
     workloads.Workload("tok_mx", T=40, d=256, f=512, E=4, k=2, quant="mxfp4", seed=41),
     workloads.Workload("mx_sigmoid", T=33, d=512, f=256, E=8, k=3, quant="mxfp4",
                        score="sigmoid", logits="zipf", seed=42),
+    # MXFP4 on the tiled kernels (d, f multiples of 512): 128-row blocks, and
+    # 600 rows per expert in 256-row blocks with a partly padded third block
+    workloads.Workload("tiled_mx", T=300, d=512, f=1024, E=4, k=2, quant="mxfp4", seed=43),
+    workloads.Workload("spill_mx", T=600, d=512, f=512, E=2, k=2, quant="mxfp4", seed=44),
     workloads.Workload("one_expert", T=20, d=128, f=128, E=1, k=1, seed=26),
     workloads.Workload("single_token", T=1, d=256, f=256, E=8, k=2, seed=27),
     workloads.Workload("tiled_bf16", T=300, d=512, f=384, E=4, k=2, seed=29),
@@ -40,7 +44,9 @@ SMALL = [
 
 
 def _tiled_ok(wl):
-    return wl.quant not in ("fp8_block", "mxfp4") and wl.d % 256 == 0
+    if wl.quant == "mxfp4":
+        return wl.d % 512 == 0 and wl.f % 512 == 0
+    return wl.quant != "fp8_block" and wl.d % 256 == 0
 
 
 def _run_two_stage(wl, x, ids, w, ws, B, ksplit):
@@ -103,7 +109,7 @@ def test_fused_with_given_routing_and_idle_experts():
 
 
 FULL_SAMPLES = {"tiny": None, "mixtral_decode": None, "mixtral_prefill": 24, "mixtral_fp8": 24,
-                "deepseek_fp8": 6, "mixtral_mxfp4": None}
+                "deepseek_fp8": 6, "mixtral_mxfp4": None, "mixtral_prefill_mxfp4": 24}
 
 
 @pytest.mark.parametrize("name", list(workloads.WORKLOADS))

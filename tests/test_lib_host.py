@@ -110,10 +110,14 @@ def test_select_config_is_host_only_and_valid(lib):
     for shape in [(16, 128, 256, 4, 2, "bf16"), (32, 4096, 14336, 8, 2, "bf16"),
                   (4096, 4096, 14336, 8, 2, "bf16"), (512, 4096, 14336, 8, 2, "fp8_token"),
                   (128, 7168, 2048, 256, 8, "fp8_block"), (1, 4096, 14336, 8, 2, "bf16"),
-                  (32, 4096, 14336, 8, 2, "mxfp4"), (4096, 4096, 14336, 8, 2, "mxfp4")]:
+                  (32, 4096, 14336, 8, 2, "mxfp4"), (4096, 4096, 14336, 8, 2, "mxfp4"),
+                  (4096, 4096, 14592, 8, 2, "mxfp4")]:
         B, stage, ks = moe.moe_select_config(*shape, cu_count=256)
         assert B in (16, 32, 64, 128, 256) and stage in (1, 2) and ks >= 1
-        if shape[-1] == "mxfp4":
-            assert B in (16, 32)        # MXFP4 runs on the streaming kernels
+    # MXFP4: the streaming kernels at few rows per expert or when d or f is not
+    # a multiple of 512 (the tiled kernels' pairs of K steps), else 256-row tiles
+    assert moe.moe_select_config(32, 4096, 14336, 8, 2, "mxfp4", cu_count=256)[0] == 32
+    assert moe.moe_select_config(4096, 4096, 14336, 8, 2, "mxfp4", cu_count=256)[0] == 256
+    assert moe.moe_select_config(4096, 4096, 14592, 8, 2, "mxfp4", cu_count=256)[0] == 32
     with pytest.raises(moe.MoeError):
         moe.moe_select_config(4, 100, 256, 4, 2, "bf16", cu_count=256)

@@ -182,6 +182,8 @@ WORKLOADS = {
     # the per_1x32 (MXFP4) quant type on the Mixtral decode shape
     "mixtral_mxfp4": Workload("mixtral_mxfp4", T=32, d=4096, f=14336, E=8, k=2,
                               quant="mxfp4", seed=1006),
+    "mixtral_prefill_mxfp4": Workload("mixtral_prefill_mxfp4", T=4096, d=4096, f=14336, E=8, k=2,
+                                      quant="mxfp4", seed=1007),
 }
 
 
