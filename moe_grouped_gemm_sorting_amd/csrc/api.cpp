@@ -154,9 +154,10 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
     // tiles than CUs; bf16 (MFMA-bound) also splits in two under four rounds
     // of tiles, which halves the idle tail of the last round (Mixtral
     // prefill, 560 tiles of 256 x 256: 1110 -> 1015 us). e4m3 at one full
-    // round of tiles got slower (121 -> 130 us).
+    // round of tiles got slower (121 -> 130 us), and so did MXFP4 at the
+    // Mixtral prefill shape (362 -> 384 us).
     if (use_tiled(B) && base >= cu)
-        return ((quant == 0 || quant == MOE_QUANT_MXFP4) && base < 4 * (int64_t)cu && f / KS >= 8) ? 2 : 1;
+        return (quant == 0 && base < 4 * (int64_t)cu && f / KS >= 8) ? 2 : 1;
     const int64_t target = use_tiled(B) ? cu : 2 * (int64_t)cu;
     int ks = (int)std::min<int64_t>((target + base - 1) / base, f / KS / 4);
     return std::max(1, ks);

@@ -396,18 +396,29 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // 4s + 2lh + 1), all fragments read up front.
     // MXFP4: 4 sub-steps of K = 64; lane half lh takes chunk 4 lh + s, i.e.
     // MX block 4 lh + s of the step, so the lane's four E8M0 scales of the
-    // step are one dword of the scale row (byte s for sub-step s). Step j
-    // reads its scales from slot (j / 2) % 2 at byte 8 (j % 2).
+    // step are one dword of the scale row (byte s for sub-step s): dword
+    // 2 (j % 2) + lh of the row's 16 bytes in slot (j / 2) % 2. The even step
+    // of a pair reads the rows' 16 bytes whole (a 16-lane group then covers
+    // all 64 banks once) and the odd step reuses them.
+    u32x4 xs[RT + CT];
     auto compute = [&](int buf, int j) {
         if (!wave_live) return;
         const uint8_t *base = lds + buf * BUF;
         if constexpr (MX) {
-            const uint8_t *sb = lds + NBUF * BUF + ((j >> 1) & 1) * SSLOT + 8 * (j & 1) + 4 * lh;
+            // two stages: buf is the parity of j
+            if (buf == 0) {
+                const uint8_t *sb = lds + NBUF * BUF + ((j >> 1) & 1) * SSLOT;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) xs[rt] = *reinterpret_cast<const u32x4 *>(sb + arow[rt] * 16);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    xs[RT + ct] = *reinterpret_cast<const u32x4 *>(sb + (BM + brow[ct]) * 16);
+            }
             uint32_t xa[RT], xb[CT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const uint32_t *>(sb + arow[rt] * 16);
+            for (int rt = 0; rt < RT; ++rt) xa[rt] = lh ? xs[rt][2 * buf + 1] : xs[rt][2 * buf];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) xb[ct] = *reinterpret_cast<const uint32_t *>(sb + (BM + brow[ct]) * 16);
+            for (int ct = 0; ct < CT; ++ct) xb[ct] = lh ? xs[RT + ct][2 * buf + 1] : xs[RT + ct][2 * buf];
             u32x4 fa[2][RT], fb[2][CT];
             frags_at(base, 4 * lh, fa[0], fb[0]);
             static_for<4>([&](auto sc) {
