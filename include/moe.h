@@ -226,6 +226,24 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
 int moe_select_config(int T, int d, int f, int E, int k, int quant, int cu_count,
                       int *B, int *stage, int *ksplit);
 
+/* Tuned configurations (AITER walk-through, section 4.1: a table of tuned
+ * configurations measured offline and keyed by shape, looked up with a fuzzy
+ * match on the token count). Loads a CSV of rows
+ *     cu,T,d,f,E,k,quant,B,stage,ksplit[,more columns ignored]
+ * (quant: bf16, fp8_token, fp8_block, mxfp4 or 0..3; lines starting with '#'
+ * and a header line are skipped) and replaces the process-wide table.
+ * While a table is loaded, moe_select_config and every B = 0 / stage = 0 /
+ * ksplit <= 0 choice take the row with the same (cu, d, f, E, k, quant)
+ * whose T is the smallest at or above the call's T (else the largest T);
+ * shapes without such a row keep the built-in rule. A K-split from the table
+ * is used only with the row's own B.
+ *   path: a host string; NULL clears the table. rows (may be NULL): the
+ * number of rows loaded. Returns MOE_ERR_INVALID_ARG for an unreadable file
+ * or a malformed row and MOE_ERR_UNSUPPORTED for a row no kernel can run
+ * (moe_last_error names the line); the table in use is then left unchanged.
+ * Host-only; thread-safe against concurrent lookups. */
+int moe_load_config_table(const char *path, int *rows);
+
 const char *moe_status_string(int status);
 const char *moe_last_error(void);
 

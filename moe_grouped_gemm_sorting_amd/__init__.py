@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import warnings
 
 import torch
 
@@ -19,10 +20,14 @@ __all__ = [
     "moe_quant_act_mx",
     "moe_gemm1_workspace_bytes", "moe_gemm1_swiglu", "moe_gemm2_workspace_bytes",
     "moe_gemm2_combine", "fused_moe_workspace_bytes", "fused_moe", "moe_select_config",
+    "moe_load_config_table", "DEFAULT_CONFIG_TABLE",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# Tuned configurations measured on MI355X (written by ``tune.py``). Loaded with
+# the library unless MOE_CONFIG_TABLE names another file ("" loads none).
+DEFAULT_CONFIG_TABLE = os.path.join(_PKG, "configs", "mi355x.csv")
 _lib = None
 
 QUANT = {"bf16": 0, "fp8_token": 1, "fp8_block": 2, "mxfp4": 3}
@@ -65,6 +70,7 @@ def load_library():
         "fused_moe_workspace_bytes": (sz, [i32] * 8),
         "fused_moe": (i32, [i32] * 8 + [P] * 8 + [i32, i32, i32, P, P, sz, P]),
         "moe_select_config": (i32, [i32] * 7 + [P, P, P]),
+        "moe_load_config_table": (i32, [ctypes.c_char_p, P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
@@ -73,6 +79,14 @@ def load_library():
         fn.restype = res
         fn.argtypes = args
     _lib = lib
+    table = os.environ.get("MOE_CONFIG_TABLE")
+    if table:
+        moe_load_config_table(table)
+    elif table is None and os.path.exists(DEFAULT_CONFIG_TABLE):
+        try:
+            moe_load_config_table(DEFAULT_CONFIG_TABLE)
+        except MoeError as e:   # the built-in rule still works
+            warnings.warn(f"tuned-config table not loaded: {e}")
     return lib
 
 
@@ -306,6 +320,14 @@ def fused_moe(x, w13, w2, k: int, logits=None, topk_ids=None, topk_w=None, quant
                          _ptr(topk_w), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
                          _ptr(w2_scale), B, stage, ksplit, _ptr(out), _ptr(ws), nbytes, _stream(x)))
     return out
+
+
+def moe_load_config_table(path=None) -> int:
+    """Load a tuned-configuration CSV (None clears the table); returns its row count."""
+    lib = load_library()
+    rows = ctypes.c_int()
+    _check(lib.moe_load_config_table(None if path is None else os.fsencode(path), ctypes.byref(rows)))
+    return rows.value
 
 
 def moe_select_config(T, d, f, E, k, quant="bf16", cu_count: int = 0):

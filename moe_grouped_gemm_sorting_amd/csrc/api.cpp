@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "moe.h"
 #include "launch.h"
@@ -163,36 +164,85 @@ int auto_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
     return std::max(1, ks);
 }
 
-// Block size: at least the average rows per expert, so that most experts'
-// weights are streamed once; 64/128/256-row blocks go to the LDS-tiled
-// kernels. With many rows per expert, bf16 takes 256-row blocks, whose
-// 256 x 256 tiles need a third fewer operand bytes per MFMA than 128 x 256
-// tiles (measured at Mixtral prefill: GEMM1 -8%; GEMM2 -9% together with
-// the two-part split of K).
-// e4m3 takes 256-row blocks from about 100 rows per expert on: its 256 x 128
-// tiles then read each expert's weights once, and the MFMAs of padding-only
-// row quarters are skipped.
-// MXFP4 goes to the tiled kernels like bf16 when d and f are multiples of
-// 512 (its K pairs), else it stays on the streaming kernel.
+// Block size (measured on MI355X at the Mixtral shape with the sweep that
+// writes the tuned-config table; the table overrides this rule where it has
+// rows). 64/128/256-row blocks go to the LDS-tiled kernels.
+// - bf16 takes 256-row blocks from 512 rows per expert on: their 256 x 256
+//   tiles need a third fewer operand bytes per MFMA than 128 x 256 (Mixtral
+//   prefill: GEMM1 -8 %; GEMM2 -9 % with the two-part split of K). From
+//   about 12 rows per expert a 64-row tiled block beats the streaming kernel
+//   (T = 128: 530 against 816 us), which re-reads an expert's weights for
+//   each of its blocks once random routing gives it more than 32 rows.
+// - e4m3 per-token takes the tiled kernel at every size where it runs: at a
+//   few rows per expert its 64 x 256 tiles stream the weights as full
+//   128-byte lines and beat the streaming kernel by about a quarter
+//   (T = 32: 275 against 376 us); 256-row blocks from about 100 rows per
+//   expert read each expert's weights once.
+// - MXFP4 goes to the tiled kernels like bf16 from about 24 rows per expert
+//   when d and f are multiples of 512 (its K pairs), else it stays on the
+//   streaming kernel; e4m3 1x128 runs on the streaming kernel only.
 int choose_B(int T, int d, int f, int E, int k, int quant) {
     const double rows = (double)T * k / E;
+    // shapes the tiled kernels take (d a multiple of 256; MXFP4 whole K pairs)
+    const bool bf16_tiled = quant == 0 && d % 256 == 0;
     const bool mx_tiled = quant == MOE_QUANT_MXFP4 && d % 512 == 0 && f % 512 == 0;
-    if ((quant == 0 || mx_tiled) && rows >= 512) return 256;
-    if (quant == 1 && rows >= 96) return 256;
-    // e4m3 1x128 runs on the streaming kernel only
-    const bool tiled_ok = quant == 0 || quant == 1 || mx_tiled;
-    if (tiled_ok && rows >= 96) return 128;
-    if (tiled_ok && rows >= 48) return 64;
+    const bool fp8_tiled = quant == 1 && d % 256 == 0;
+    if ((bf16_tiled || mx_tiled) && rows >= 512) return 256;
+    if (fp8_tiled && rows >= 96) return 256;
+    if ((bf16_tiled || mx_tiled) && rows >= 96) return 128;
+    if (fp8_tiled) return 64;
+    if (bf16_tiled && rows >= 12) return 64;
+    if (mx_tiled && rows >= 24) return 64;
     if (rows <= 4) return 16;
     return 32;
 }
 
+// ------------------------------------------------------ tuned-config table
+// Rows measured offline (cu, T, d, f, E, k, quant) -> (B, stage, ksplit), in
+// the spirit of the tuned-configuration CSV of the AITER walk-through
+// (section 4.1), whose lookup matches the token count fuzzily (padded M).
+// Here: among rows with the call's (cu, d, f, E, k, quant), the one with the
+// smallest T at or above the call's T, else the one with the largest T.
+struct TableRow {
+    int cu, T, d, f, E, k, quant, B, stage, ksplit;
+};
+std::mutex g_table_mu;
+std::vector<TableRow> g_table;
+
+bool table_lookup(int T, int d, int f, int E, int k, int quant, int cu, Config *out) {
+    std::lock_guard<std::mutex> lock(g_table_mu);
+    const TableRow *best = nullptr;
+    for (const TableRow &r : g_table) {
+        if (r.cu != cu || r.d != d || r.f != f || r.E != E || r.k != k || r.quant != quant) continue;
+        if (!best) {
+            best = &r;
+            continue;
+        }
+        const bool r_up = r.T >= T, b_up = best->T >= T;
+        if ((r_up && (!b_up || r.T < best->T)) || (!r_up && !b_up && r.T > best->T)) best = &r;
+    }
+    if (!best) return false;
+    out->B = best->B;
+    out->stage = best->stage;
+    out->ksplit = best->ksplit;
+    return true;
+}
+
 Config choose(int T, int d, int f, int E, int k, int quant, int cu) {
     Config c;
+    if (table_lookup(T, d, f, E, k, quant, cu, &c)) return c;
     c.B = choose_B(T, d, f, E, k, quant);
     c.stage = 2;
     c.ksplit = auto_ksplit(T, d, f, E, k, c.B, quant, cu);
     return c;
+}
+
+// K-split when the caller leaves it to the library: the table's, if its row
+// has the block size in use, else the rule above
+int pick_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
+    Config c;
+    if (table_lookup(T, d, f, E, k, quant, cu, &c) && c.B == B) return c.ksplit;
+    return auto_ksplit(T, d, f, E, k, B, quant, cu);
 }
 
 // -------------------------------------------------------------- stage 1/2
@@ -317,7 +367,7 @@ int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, c
     g.sorted_expert_ids = seid;
     g.num_valid = num_valid;
     g.acc = acc;
-    if (ksplit <= 0) ksplit = auto_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
+    if (ksplit <= 0) ksplit = pick_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
     g.ksplit = ksplit;
     const bool tiled = use_tiled(B);
     if (tiled ? !tiled_gemm_supported(g.sh) : !stream_gemm2_supported(g.sh))
@@ -516,6 +566,78 @@ int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int k
                      sorted_w, sorted_expert_ids, num_valid, out, acc, (hipStream_t)stream);
 }
 
+int moe_load_config_table(const char *path, int *rows) {
+    g_err[0] = 0;
+    if (rows) *rows = 0;
+    if (!path) {
+        std::lock_guard<std::mutex> lock(g_table_mu);
+        g_table.clear();
+        return MOE_OK;
+    }
+    FILE *fp = fopen(path, "r");
+    if (!fp) return fail(MOE_ERR_INVALID_ARG, "cannot open %s", path);
+    std::vector<TableRow> table;
+    char line[512];
+    int lineno = 0, rc = MOE_OK;
+    while (fgets(line, sizeof line, fp)) {
+        ++lineno;
+        char *p = line;
+        while (*p == ' ' || *p == '\t') ++p;
+        if (*p == '#' || *p == '\n' || *p == '\r' || *p == 0) continue;
+        if (*p < '0' || *p > '9') {
+            if (table.empty()) continue;   // a header line
+            rc = fail(MOE_ERR_INVALID_ARG, "%s:%d: not a row", path, lineno);
+            break;
+        }
+        // cu,T,d,f,E,k,quant,B,stage,ksplit[,anything]
+        char qname[32] = {0};
+        TableRow r{};
+        int n = sscanf(p, "%d,%d,%d,%d,%d,%d,%31[^,],%d,%d,%d", &r.cu, &r.T, &r.d, &r.f, &r.E, &r.k,
+                       qname, &r.B, &r.stage, &r.ksplit);
+        if (n != 10) {
+            rc = fail(MOE_ERR_INVALID_ARG, "%s:%d: expected cu,T,d,f,E,k,quant,B,stage,ksplit", path, lineno);
+            break;
+        }
+        if (!strcmp(qname, "bf16") || !strcmp(qname, "0")) r.quant = 0;
+        else if (!strcmp(qname, "fp8_token") || !strcmp(qname, "1")) r.quant = 1;
+        else if (!strcmp(qname, "fp8_block") || !strcmp(qname, "2")) r.quant = 2;
+        else if (!strcmp(qname, "mxfp4") || !strcmp(qname, "3")) r.quant = MOE_QUANT_MXFP4;
+        else {
+            rc = fail(MOE_ERR_INVALID_ARG, "%s:%d: unknown quant '%s'", path, lineno, qname);
+            break;
+        }
+        if (r.cu < 1 || r.T < 1 || (r.stage != 1 && r.stage != 2) || r.ksplit < 1) {
+            rc = fail(MOE_ERR_INVALID_ARG, "%s:%d: bad cu / T / stage / ksplit", path, lineno);
+            break;
+        }
+        const GemmShape sh{r.T, r.d, r.f, r.E, r.k, r.B, r.quant};
+        const int cs = check_shape(r.T, r.d, r.f, r.E, r.k, r.B, r.quant);
+        if (cs != MOE_OK) {
+            char why[512];
+            snprintf(why, sizeof why, "%s", g_err);
+            rc = fail(cs, "%s:%d: %s", path, lineno, why);
+            break;
+        }
+        bool ok = true;
+        if (r.stage == 1) ok = onestage_supported(sh);
+        if (r.stage == 2)
+            ok = use_tiled(r.B) ? tiled_gemm_supported(sh)
+                                : stream_gemm1_supported(sh) && stream_gemm2_supported(sh);
+        if (!ok) {
+            rc = fail(MOE_ERR_UNSUPPORTED, "%s:%d: no kernels for B=%d stage=%d at this shape", path,
+                      lineno, r.B, r.stage);
+            break;
+        }
+        table.push_back(r);
+    }
+    fclose(fp);
+    if (rc != MOE_OK) return rc;
+    std::lock_guard<std::mutex> lock(g_table_mu);
+    g_table.swap(table);
+    if (rows) *rows = (int)g_table.size();
+    return MOE_OK;
+}
+
 int moe_select_config(int T, int d, int f, int E, int k, int quant, int cu_count, int *B,
                       int *stage, int *ksplit) {
     g_err[0] = 0;
@@ -608,7 +730,7 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     }
     // GEMM1 also clears GEMM2's accumulator (same stream, so it is done first)
     // unless GEMM2 stores whole rows
-    if (ksplit <= 0) ksplit = auto_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
+    if (ksplit <= 0) ksplit = pick_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
     const bool clear = !stored_rows(B, ksplit);
     rc = run_gemm1(T, d, f, E, k, B, quant, x, w13, w13_scale, w.sorted_ids, w.seid, w.num_valid,
                    w.h, w.h_scale, w.g1, s, clear ? w.acc : nullptr, clear ? (size_t)T * d : 0);

@@ -106,7 +106,16 @@ def test_workspace_queries_grow_with_the_problem(lib):
     assert lib.moe_gemm1_workspace_bytes(32, 4096, 14336, 8, 2, 32, 0) == 0
 
 
-def test_select_config_is_host_only_and_valid(lib):
+@pytest.fixture
+def no_table(lib):
+    """The built-in choice: no tuned table while the test runs (the default one is reloaded)."""
+    moe.moe_load_config_table(None)
+    yield
+    if os.path.exists(moe.DEFAULT_CONFIG_TABLE):
+        moe.moe_load_config_table(moe.DEFAULT_CONFIG_TABLE)
+
+
+def test_select_config_is_host_only_and_valid(lib, no_table):
     for shape in [(16, 128, 256, 4, 2, "bf16"), (32, 4096, 14336, 8, 2, "bf16"),
                   (4096, 4096, 14336, 8, 2, "bf16"), (512, 4096, 14336, 8, 2, "fp8_token"),
                   (128, 7168, 2048, 256, 8, "fp8_block"), (1, 4096, 14336, 8, 2, "bf16"),
@@ -121,3 +130,56 @@ def test_select_config_is_host_only_and_valid(lib):
     assert moe.moe_select_config(4096, 4096, 14592, 8, 2, "mxfp4", cu_count=256)[0] == 32
     with pytest.raises(moe.MoeError):
         moe.moe_select_config(4, 100, 256, 4, 2, "bf16", cu_count=256)
+
+
+def test_config_table_fuzzy_match_on_T(lib, no_table, tmp_path):
+    """Rows of the same (cu, d, f, E, k, quant): the smallest T at or above the call's T, else the
+    largest; other shapes and CU counts keep the built-in rule."""
+    path = tmp_path / "t.csv"
+    path.write_text("# a comment\ncu,T,d,f,E,k,quant,B,stage,ksplit,us\n"
+                    "256,8,4096,14336,8,2,bf16,16,1,1,1.0\n"
+                    "256,64,4096,14336,8,2,bf16,32,2,3,2.0\n"
+                    "256,1024,4096,14336,8,2,0,128,2,1,3.0\n"
+                    "256,512,4096,14336,8,2,mxfp4,64,2,2\n")
+    assert moe.moe_load_config_table(str(path)) == 4
+    sel = lambda T, q="bf16", cu=256: moe.moe_select_config(T, 4096, 14336, 8, 2, q, cu_count=cu)
+    assert sel(1) == (16, 1, 1) and sel(8) == (16, 1, 1)
+    assert sel(9) == (32, 2, 3) and sel(64) == (32, 2, 3)
+    assert sel(65) == (128, 2, 1) and sel(1024) == (128, 2, 1)
+    assert sel(5000) == (128, 2, 1)                 # above every row: the largest T
+    assert sel(3, "mxfp4") == (64, 2, 2)
+    # another CU count or another shape: the built-in rule
+    moe.moe_load_config_table(None)
+    b304 = sel(64, cu=304)
+    b_k4 = moe.moe_select_config(64, 4096, 14336, 8, 4, cu_count=256)
+    moe.moe_load_config_table(str(path))
+    assert sel(64, cu=304) == b304
+    assert moe.moe_select_config(64, 4096, 14336, 8, 4, cu_count=256) == b_k4
+
+
+def test_config_table_rejects_bad_rows_and_keeps_the_old_table(lib, no_table, tmp_path):
+    good = tmp_path / "good.csv"
+    good.write_text("256,32,4096,14336,8,2,bf16,16,2,4\n")
+    assert moe.moe_load_config_table(str(good)) == 1
+    for bad, status in [("256,32,4096,14336,8,2,bf16,48,2,4\n", "MOE_ERR_INVALID_ARG"),     # B
+                        ("256,32,4096,14336,8,2,fp16,16,2,4\n", "MOE_ERR_INVALID_ARG"),     # quant
+                        ("256,32,4096,14336,8,2,bf16,16,3,4\n", "MOE_ERR_INVALID_ARG"),     # stage
+                        ("256,32,4096,14336,8,2,bf16,16\n", "MOE_ERR_INVALID_ARG"),         # short row
+                        ("256,32,4096,14336,8,2,fp8_token,16,1,1\n", "MOE_ERR_UNSUPPORTED"),  # 1-stage fp8
+                        ("256,32,4096,14336,8,2,fp8_block,64,2,1\n", "MOE_ERR_UNSUPPORTED"),  # tiled 1x128
+                        ("256,32,4096,14592,8,2,mxfp4,64,2,1\n", "MOE_ERR_UNSUPPORTED")]:   # f % 512
+        path = tmp_path / "bad.csv"
+        path.write_text("256,64,4096,14336,8,2,bf16,32,2,2\n" + bad)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_load_config_table(str(path))
+        assert status in str(ei.value) and "bad.csv:2" in str(ei.value)
+        assert moe.moe_select_config(32, 4096, 14336, 8, 2, cu_count=256) == (16, 2, 4)
+    with pytest.raises(moe.MoeError):
+        moe.moe_load_config_table(str(tmp_path / "missing.csv"))
+
+
+def test_packaged_config_table_loads(lib):
+    """The committed table (if present) parses and names only runnable configurations."""
+    if not os.path.exists(moe.DEFAULT_CONFIG_TABLE):
+        pytest.skip("no packaged table")
+    assert moe.moe_load_config_table(moe.DEFAULT_CONFIG_TABLE) > 0
