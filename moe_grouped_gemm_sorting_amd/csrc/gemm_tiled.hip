@@ -104,12 +104,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // One wave-wide LDS DMA: lane l copies the 16 bytes at base + off into LDS
 // bytes [m0 + 16 l, m0 + 16 l + 16). m0 must be wave-uniform. The s_nop
 // covers the wait state an M0 write needs before an LDS DMA reads it.
+// M0 is listed as clobbered although the compiler reserves it: nothing else
+// in these kernels reads M0 (no other LDS DMA, message or relative-move
+// instruction; checked in the generated assembly), so the warning is
+// silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(off), "s"(base), "s"(m0)
                  : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Wait until at most N of this wave's vector memory operations are pending
 // (they complete in issue order).
@@ -164,10 +171,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     constexpr int WN = TN / 64, WM = WAVES / WN;
     constexpr int RT = BM / WM / 32;            // 32-row tiles per wave
     constexpr int CT = 2;                       // 32-column tiles per wave
-    // LDS stages (of 160 KB of LDS); MXFP4 keeps two, so that every step
-    // ends with all of its loads complete (its scale loads come every other
-    // step)
-    constexpr int NBUF = (BUF <= 48 * 1024 && !MX) ? 3 : 2;
+    // LDS stages (of 160 KB of LDS)
+    constexpr int NBUF = BUF <= 48 * 1024 ? 3 : 2;
     // MXFP4 scales: per pair of K steps, 16 bytes per tile row (8 per step),
     // in two slots after the stages
     constexpr int SSLOT = MX ? ROWS * 16 : 0;
@@ -401,12 +406,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // of a pair reads the rows' 16 bytes whole (a 16-lane group then covers
     // all 64 banks once) and the odd step reuses them.
     u32x4 xs[RT + CT];
-    auto compute = [&](int buf, int j) {
+    auto compute = [&](int buf, int j, int par) {
         if (!wave_live) return;
         const uint8_t *base = lds + buf * BUF;
         if constexpr (MX) {
-            // two stages: buf is the parity of j
-            if (buf == 0) {
+            // par: the parity of j (a compile-time constant after unrolling)
+            if (par == 0) {
                 const uint8_t *sb = lds + NBUF * BUF + ((j >> 1) & 1) * SSLOT;
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) xs[rt] = *reinterpret_cast<const u32x4 *>(sb + arow[rt] * 16);
@@ -416,9 +421,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             }
             uint32_t xa[RT], xb[CT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) xa[rt] = lh ? xs[rt][2 * buf + 1] : xs[rt][2 * buf];
+            for (int rt = 0; rt < RT; ++rt) xa[rt] = lh ? xs[rt][2 * par + 1] : xs[rt][2 * par];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) xb[ct] = lh ? xs[RT + ct][2 * buf + 1] : xs[RT + ct][2 * buf];
+            for (int ct = 0; ct < CT; ++ct) xb[ct] = lh ? xs[RT + ct][2 * par + 1] : xs[RT + ct][2 * par];
             u32x4 fa[2][RT], fb[2][CT];
             frags_at(base, 4 * lh, fa[0], fb[0]);
             static_for<4>([&](auto sc) {
@@ -467,9 +472,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // (j+S-1) % S (read during step j-1, which every wave has finished:
     // barrier), multiply stage j % S, wait for this wave's loads of step j+1,
     // barrier (so all of step j+1 has landed and stage j % S is free).
-    // Unrolled by S so that the stage offsets are constants; loads past the
-    // end are clamped to the last step, which keeps the wait counts exact and
-    // lands in a stage nobody reads.
+    // Unrolled by S (MXFP4 with three stages: by 6, so that the stage and the
+    // parity of the step are both constants) so that the stage offsets and
+    // wait counts are constants; loads past the end are clamped to the last
+    // step, which keeps the wait counts exact and lands in a stage nobody
+    // reads. MXFP4 scale pairs go out with the loads of their first (even)
+    // step, so a step's wait allows one more outstanding load after an
+    // issue of scales (waves that copy scale rows only).
     // Activation load i of every wave covers rows [64 i, 64 i + 64) of the
     // tile, so only the first NQAL = ceil(real rows / 64) of them carry real
     // rows; the others are not issued. Their LDS rows keep stale bytes, which
@@ -478,33 +487,41 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     auto kloop = [&](auto nqal_c) {
         constexpr int NQAL = decltype(nqal_c)::value;
         constexpr int NQL = NQAL + (NQ - NQA);   // loads per wave per step
+        constexpr int UNR = (MX && NBUF % 2) ? 2 * NBUF : NBUF;
         if (nsteps <= 0) return;
+        // scales of the first pair before the activation rows, which the
+        // first wait leaves outstanding
+        issue_scales(0);
 #pragma unroll
         for (int b = 0; b < NBUF - 1; ++b) issue_part(b, kof(b), 0, NQAL);
-        issue_scales(0);
         // stage 0 has landed once only the activation rows of the later
         // prologue stages are pending (everything older has completed)
         wait_vmem<NQAL * (NBUF - 2)>();
         __syncthreads();
-        auto step = [&](int j, int b) {
-            const int nb = (b + NBUF - 1) % NBUF, kk = kof(j + NBUF - 1);
+        // b: position in the unrolled group (the group starts at an even step)
+        auto step = [&](int j, auto bc) {
+            constexpr int b = decltype(bc)::value;
+            constexpr int nb = (b + NBUF - 1) % NBUF;
+            // MXFP4 (even step count, no rotation): the issued step is even
+            constexpr bool SC = MX && (b + NBUF - 1) % 2 == 0;
+            const int jj = j + NBUF - 1, kk = kof(jj);
             issue_part(nb, kk, 0, NQAL);
             issue_part(nb, kk, NQA, NQ);
-            // MXFP4 (two stages, even step count, no rotation): with step
-            // j + 1 even, its pair's scales
-            if (MX && b == 1 && j + 1 < nsteps) issue_scales((j + 1) / 2);
-            compute(b, j);
-            wait_vmem<NQL * (NBUF - 2)>();
+            const bool sc = SC && jj < nsteps;
+            if (sc) issue_scales(jj / 2);
+            compute(b % NBUF, j, b % 2);
+            if (NBUF > 2 && sc && xwave)
+                wait_vmem<(NQL + 1) * (NBUF - 2)>();
+            else
+                wait_vmem<NQL * (NBUF - 2)>();
             __syncthreads();
         };
         int j = 0;
-        for (; j + NBUF <= nsteps; j += NBUF) {
-#pragma unroll
-            for (int b = 0; b < NBUF; ++b) step(j + b, b);
-        }
-#pragma unroll
-        for (int b = 0; b < NBUF - 1; ++b)
-            if (j + b < nsteps) step(j + b, b);
+        for (; j + UNR <= nsteps; j += UNR)
+            static_for<UNR>([&](auto bc) { step(j + decltype(bc)::value, bc); });
+        static_for<UNR - 1>([&](auto bc) {
+            if (j + decltype(bc)::value < nsteps) step(j + decltype(bc)::value, bc);
+        });
     };
     const int nqal = min(NQA, (__popcll(live32) + 1) / 2);
     static_for<NQA>([&](auto ic) {
