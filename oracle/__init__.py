@@ -19,6 +19,9 @@ passage it follows:
 * :func:`e4m3_encode` / :func:`e4m3_decode` / :func:`quant_rows` -- OCP FP8
   E4M3FN and the amax/448 scale rule used by the fp8 layers (quant types
   per_Token and per_1x128 named in the AITER article, sections 1.1 and 3.2).
+* :func:`moe_backward` -- the gradients of the bf16 layer (the training
+  step named as the next milestone: rocketrecap.com/entries/19116, 10:07),
+  from the chain rule of :func:`moe`.
 * :func:`fp4_encode` / :func:`fp4_decode` / :func:`mx_quant_rows` -- MXFP4,
   the quant type per_1x32 (same article, sections 1.1, 2.2 and 3.2;
   rocketrecap.com/entries/19188 glossary "MXFP4"), with the element format,
@@ -89,6 +92,9 @@ def _load():
         lib.oracle_mx_quant_group.restype = ctypes.c_uint8
         lib.oracle_mx_quant_rows.argtypes = [P, i32, i32, P, P]
         lib.oracle_mx_quant_rows.restype = i32
+        lib.oracle_moe_backward.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P,
+                                            P, P, P, P, i32]
+        lib.oracle_moe_backward.restype = i32
         _lib = lib
     return _lib
 
@@ -283,3 +289,48 @@ def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
     if rc != 0:
         raise ValueError(f"oracle_moe failed ({rc})")
     return y, out
+
+
+def moe_backward(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
+                 dy_bf16: np.ndarray, h_exact: bool = False, threads: int = 0):
+    """Gradients of the bf16 layer for the output gradient dy (bf16 bits [T, d]).
+
+    w13 / w2 as in :func:`moe` (bf16 bits; None for unused experts).
+    Returns (dx fp32 [T, d], dw13 list of fp32 [2f, d] or None, dw2 list of
+    fp32 [d, f] or None, dtopk_w fp32 [T, k])."""
+    lib = _load()
+    x = _c(x_bf16, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    w = _c(topk_w, np.float32)
+    dy = _c(dy_bf16, np.uint16)
+    T, d = x.shape
+    k = ids.shape[1]
+    E = len(w13)
+    f = next(a for a in w13 if a is not None).shape[0] // 2
+    keep = []
+
+    def table(arrs, dtype):
+        t = (ctypes.c_void_p * E)()
+        for e, a in enumerate(arrs):
+            if a is None:
+                t[e] = None
+            else:
+                a = _c(a, dtype)
+                keep.append(a)
+                t[e] = a.ctypes.data
+        return t
+
+    t13, t2 = table(w13, np.uint16), table(w2, np.uint16)
+    dw13 = [None if a is None else np.empty((2 * f, d), np.float32) for a in w13]
+    dw2 = [None if a is None else np.empty((d, f), np.float32) for a in w2]
+    g13, g2 = (ctypes.c_void_p * E)(), (ctypes.c_void_p * E)()
+    for e in range(E):   # outputs are written in place: point at the arrays themselves
+        g13[e] = None if dw13[e] is None else dw13[e].ctypes.data
+        g2[e] = None if dw2[e] is None else dw2[e].ctypes.data
+    dx = np.empty((T, d), np.float32)
+    dtw = np.empty((T, k), np.float32)
+    rc = lib.oracle_moe_backward(T, d, f, E, k, int(h_exact), _ptr(x), _ptr(ids), _ptr(w), t13, t2,
+                                 _ptr(dy), _ptr(dx), g13, g2, _ptr(dtw), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_moe_backward failed ({rc})")
+    return dx, dw13, dw2, dtw

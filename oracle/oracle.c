@@ -38,6 +38,15 @@
  *    floor(log2(amax)) - 2 (2 = exponent of the largest E2M1 value; -127
  *    for an all-zero block), elements are round-to-nearest-even of v / 2^E,
  *    saturating at +-6.
+ *  - oracle_moe_backward: the gradients of the bf16 layer (the training
+ *    step the pages name as the next milestone: rocketrecap.com/entries/
+ *    19116, 10:07; entries/19188, custom VJP). Written from the chain rule of
+ *    the forward above, one token at a time in fp32: dz = w dy,
+ *    dh = Wd^T dz, dg = dh * u * silu'(g), du = dh * silu(g),
+ *    dx = Wg^T dg + Wu^T du, dWd += dz h^T, dWg += dg x^T, dWu += du x^T,
+ *    dw = <dy, Wd h>. The bf16 rounding of h passes the gradient unchanged
+ *    (a cast's derivative is taken as 1, as automatic differentiation of a
+ *    dtype conversion does).
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no BLAS, no
  * fast-math). Every exported function returns 0 on success and a negative
@@ -492,6 +501,142 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
         free(h);
     }
     return bad ? -2 : 0;
+}
+
+static float silu_grad(float z)
+{
+    const float sg = 1.0f / (1.0f + expf(-z));
+    return sg * (1.0f + z * (1.0f - sg));
+}
+
+/* Backward of the bf16 layer (quant 0) for every token.
+ * In: x [T, d] bf16, topk_ids / topk_w [T, k], weights per expert as in
+ * oracle_moe (bf16 bits; unused experts may be NULL), dy [T, d] bf16 bits,
+ * h_exact as in oracle_moe.
+ * Out (overwritten): dx [T, d] fp32; dw13[e] [2f, d] and dw2[e] [d, f] fp32
+ * for every expert whose pointer is non-NULL (zero for experts no token
+ * selects); dtopk_w [T, k] fp32.
+ * Per-token work runs in parallel; the weight gradients are then summed per
+ * expert over tokens in ascending order, so the result does not depend on
+ * the thread count. */
+int oracle_moe_backward(int T, int d, int f, int E, int k, int h_exact, const uint16_t *x,
+                        const int32_t *topk_ids, const float *topk_w,
+                        const void *const *w13, const void *const *w2, const uint16_t *dy,
+                        float *dx, float *const *dw13, float *const *dw2, float *dtopk_w,
+                        int nthreads)
+{
+    if (!x || !topk_ids || !topk_w || !w13 || !w2 || !dy || !dx || !dw13 || !dw2 || !dtopk_w)
+        return -1;
+    if (T < 0 || d < 1 || f < 1 || E < 1 || k < 1 || k > E)
+        return -1;
+    for (size_t a = 0; a < (size_t)T * k; ++a) {
+        int e = topk_ids[a];
+        if (e < 0 || e >= E || !w13[e] || !w2[e])
+            return -1;
+    }
+    const size_t n_asg = (size_t)T * k;
+    /* per assignment: dz [d], h [f], dg [f], du [f] */
+    float *dz = (float *)malloc(sizeof(float) * (n_asg * d + 3 * n_asg * f + 1));
+    if (!dz)
+        return -2;
+    float *hh = dz + n_asg * d, *dg = hh + n_asg * f, *du = dg + n_asg * f;
+    int bad = 0;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+#endif
+    for (int t = 0; t < T; ++t) {
+        float *xt = (float *)malloc(sizeof(float) * (size_t)(2 * d + 3 * f));
+        if (!xt) {
+            bad |= 1;
+            continue;
+        }
+        float *dyt = xt + d, *g = dyt + d, *u = g + f, *dh = u + f;
+        for (int c = 0; c < d; ++c) {
+            xt[c] = bf16_bits_to_f32(x[(size_t)t * d + c]);
+            dyt[c] = bf16_bits_to_f32(dy[(size_t)t * d + c]);
+            dx[(size_t)t * d + c] = 0.0f;
+        }
+        for (int j = 0; j < k; ++j) {
+            const size_t a = (size_t)t * k + j;
+            const int e = topk_ids[a];
+            const float w = topk_w[a];
+            expert_view v = {d, f, 0, w13[e], w2[e], NULL, NULL};
+            float *h = hh + a * f, *dga = dg + a * f, *dua = du + a * f, *dza = dz + a * d;
+            for (int n = 0; n < f; ++n) {
+                float gs = 0.0f, us = 0.0f;
+                for (int c = 0; c < d; ++c) {
+                    gs += xt[c] * weight13(&v, n, c);
+                    us += xt[c] * weight13(&v, f + n, c);
+                }
+                g[n] = gs;
+                u[n] = us;
+                const float hn = silu(gs) * us;
+                h[n] = h_exact ? hn : round_to_bf16(hn);
+            }
+            /* dw = <dy, Wd h>; dz = w dy; dh = Wd^T dz */
+            float dw = 0.0f;
+            for (int m = 0; m < d; ++m) {
+                float z = 0.0f;
+                for (int n = 0; n < f; ++n)
+                    z += h[n] * weight2(&v, m, n);
+                dw += dyt[m] * z;
+                dza[m] = w * dyt[m];
+            }
+            dtopk_w[a] = dw;
+            for (int n = 0; n < f; ++n) {
+                float s = 0.0f;
+                for (int m = 0; m < d; ++m)
+                    s += dza[m] * weight2(&v, m, n);
+                dh[n] = s;
+            }
+            for (int n = 0; n < f; ++n) {
+                dga[n] = dh[n] * u[n] * silu_grad(g[n]);
+                dua[n] = dh[n] * silu(g[n]);
+            }
+            for (int c = 0; c < d; ++c) {
+                float s = 0.0f;
+                for (int n = 0; n < f; ++n)
+                    s += dga[n] * weight13(&v, n, c) + dua[n] * weight13(&v, f + n, c);
+                dx[(size_t)t * d + c] += s;
+            }
+        }
+        free(xt);
+    }
+    if (bad) {
+        free(dz);
+        return -2;
+    }
+    /* weight gradients: per expert, tokens in ascending order */
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int e = 0; e < E; ++e) {
+        if (dw2[e])
+            memset(dw2[e], 0, sizeof(float) * (size_t)d * f);
+        if (dw13[e])
+            memset(dw13[e], 0, sizeof(float) * (size_t)2 * f * d);
+        for (size_t a = 0; a < n_asg; ++a) {
+            if (topk_ids[a] != e)
+                continue;
+            const size_t t = a / k;
+            const float *h = hh + a * f, *dga = dg + a * f, *dua = du + a * f, *dza = dz + a * d;
+            if (dw2[e])
+                for (int m = 0; m < d; ++m)
+                    for (int n = 0; n < f; ++n)
+                        dw2[e][(size_t)m * f + n] += dza[m] * h[n];
+            if (dw13[e])
+                for (int n = 0; n < f; ++n)
+                    for (int c = 0; c < d; ++c) {
+                        const float xc = bf16_bits_to_f32(x[t * d + c]);
+                        dw13[e][(size_t)n * d + c] += dga[n] * xc;
+                        dw13[e][(size_t)(f + n) * d + c] += dua[n] * xc;
+                    }
+        }
+    }
+    free(dz);
+    return 0;
 }
 
 /* Dynamic MXFP4 quantisation of a bf16 matrix [rows, cols] (cols % 32 == 0):
