@@ -226,6 +226,27 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
 int moe_select_config(int T, int d, int f, int E, int k, int quant, int cu_count,
                       int *B, int *stage, int *ksplit);
 
+/* Backward of the bf16 layer (the training step named as the next milestone:
+ * rocketrecap.com/entries/19116, talk summary at 10:07; entries/19188, the
+ * custom VJP of the JAX bridge). For a given routing (topk_ids / topk_w, as
+ * the forward used them) and the output gradient dy, computes
+ *   dx [T, d] bf16, dw13 [E, 2f, d] fp32, dw2 [E, d, f] fp32 (all experts;
+ *   zero for experts no token selects) and dtopk_w [T, k] fp32 (the gradient
+ *   of each assignment's routing weight: <dy[t], Wd h>),
+ * from the chain rule of the forward: dz = w dy, dh = Wd^T dz,
+ * dg = dh u silu'(g), du = dh silu(g), dx = Wg^T dg + Wu^T du,
+ * dWd = sum dz h^T, dWg = sum dg x^T, dWu = sum du x^T. h is the forward's
+ * bf16 h; its rounding passes the gradient unchanged. The gate / up sums are
+ * recomputed (a second GEMM1), the weights are transposed into the workspace
+ * per call, and the weight gradients reduce over each expert's rows of the
+ * sorted assignment list. bf16 only; B = 16, 32 or 0 (library's choice).
+ * Layouts and ownership as in fused_moe; every output is overwritten. */
+size_t moe_backward_workspace_bytes(int T, int d, int f, int E, int k, int B);
+int moe_backward(int T, int d, int f, int E, int k, int B, const void *x,
+                 const int32_t *topk_ids, const float *topk_w, const void *w13,
+                 const void *w2, const void *dy, void *dx, float *dw13, float *dw2,
+                 float *dtopk_w, void *ws, size_t ws_bytes, void *stream);
+
 /* Tuned configurations (AITER walk-through, section 4.1: a table of tuned
  * configurations measured offline and keyed by shape, looked up with a fuzzy
  * match on the token count). Loads a CSV of rows

@@ -20,7 +20,7 @@ __all__ = [
     "moe_quant_act_mx",
     "moe_gemm1_workspace_bytes", "moe_gemm1_swiglu", "moe_gemm2_workspace_bytes",
     "moe_gemm2_combine", "fused_moe_workspace_bytes", "fused_moe", "moe_select_config",
-    "moe_load_config_table", "DEFAULT_CONFIG_TABLE",
+    "moe_load_config_table", "DEFAULT_CONFIG_TABLE", "moe_backward_workspace_bytes", "moe_backward",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,8 @@ def load_library():
         "fused_moe": (i32, [i32] * 8 + [P] * 8 + [i32, i32, i32, P, P, sz, P]),
         "moe_select_config": (i32, [i32] * 7 + [P, P, P]),
         "moe_load_config_table": (i32, [ctypes.c_char_p, P]),
+        "moe_backward_workspace_bytes": (sz, [i32] * 6),
+        "moe_backward": (i32, [i32] * 6 + [P] * 10 + [P, sz, P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_last_error": (ctypes.c_char_p, []),
     }
@@ -337,3 +339,37 @@ def moe_select_config(T, d, f, E, k, quant="bf16", cu_count: int = 0):
     _check(lib.moe_select_config(T, d, f, E, k, QUANT[quant], cu_count, ctypes.byref(B),
                                  ctypes.byref(stage), ctypes.byref(ks)))
     return B.value, stage.value, ks.value
+
+
+def moe_backward_workspace_bytes(T, d, f, E, k, B=0) -> int:
+    return int(load_library().moe_backward_workspace_bytes(T, d, f, E, k, B))
+
+
+def moe_backward(x, w13, w2, dy, topk_ids, topk_w, B: int = 0, workspace=None):
+    """Gradients of the bf16 layer for the output gradient dy and the routing
+    the forward used. Returns (dx bf16 [T, d], dw13 fp32 [E, 2f, d],
+    dw2 fp32 [E, d, f], dtopk_w fp32 [T, k])."""
+    lib = load_library()
+    dev = x.device
+    _need(x, "x", (torch.bfloat16,), dev)
+    _need(dy, "dy", (torch.bfloat16,), dev)
+    _need(w13, "w13", (torch.bfloat16,), dev)
+    _need(w2, "w2", (torch.bfloat16,), dev)
+    _need(topk_ids, "topk_ids", (torch.int32,), dev)
+    _need(topk_w, "topk_w", (torch.float32,), dev)
+    T, d = x.shape
+    E, f2, _ = w13.shape
+    f = f2 // 2
+    k = topk_ids.shape[1]
+    dx = torch.empty(T, d, device=dev, dtype=torch.bfloat16)
+    dw13 = torch.empty(E, 2 * f, d, device=dev, dtype=torch.float32)
+    dw2 = torch.empty(E, d, f, device=dev, dtype=torch.float32)
+    dtw = torch.empty(T, k, device=dev, dtype=torch.float32)
+    nbytes = moe_backward_workspace_bytes(T, d, f, E, k, B)
+    if nbytes == 0:
+        _check(lib.moe_backward(T, d, f, E, k, B, *([None] * 10), None, 0, None))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.moe_backward(T, d, f, E, k, B, _ptr(x), _ptr(topk_ids), _ptr(topk_w), _ptr(w13),
+                            _ptr(w2), _ptr(dy), _ptr(dx), _ptr(dw13), _ptr(dw2), _ptr(dtw),
+                            _ptr(ws), nbytes, _stream(x)))
+    return dx, dw13, dw2, dtw

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["api.cpp", "route_sort.hip", "quant.hip", "gemm_stream.hip", "gemm_tiled.hip", "moe_1stage.hip"]
+SOURCES = ["api.cpp", "route_sort.hip", "quant.hip", "gemm_stream.hip", "gemm_tiled.hip", "moe_1stage.hip",
+           "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -566,6 +566,126 @@ int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int k
                      sorted_w, sorted_expert_ids, num_valid, out, acc, (hipStream_t)stream);
 }
 
+// ------------------------------------------------------------- backward
+namespace {
+struct BwdWs {
+    int32_t *sorted_ids = nullptr, *seid = nullptr, *counts = nullptr, *offsets = nullptr,
+            *num_valid = nullptr;
+    float *sorted_w = nullptr, *gu = nullptr, *acc = nullptr, *dgu32 = nullptr;
+    uint16_t *w13t = nullptr, *w2t = nullptr, *h = nullptr, *dgu = nullptr;
+};
+
+BwdWs carve_backward(Carver &c, int T, int d, int f, int E, int k, int B) {
+    BwdWs w;
+    const size_t P = (size_t)max_padded(T, k, E, B), NB = (size_t)max_blocks(T, k, E, B);
+    w.sorted_ids = c.take<int32_t>(P);
+    w.sorted_w = c.take<float>(P);
+    w.seid = c.take<int32_t>(NB);
+    w.counts = c.take<int32_t>(E);
+    w.offsets = c.take<int32_t>((size_t)E + 1);
+    w.num_valid = c.take<int32_t>(1);
+    w.w13t = c.take<uint16_t>((size_t)E * 2 * f * d);
+    w.w2t = c.take<uint16_t>((size_t)E * f * d);
+    w.gu = c.take<float>(P * 2 * f);
+    w.h = c.take<uint16_t>(P * f);
+    w.dgu = c.take<uint16_t>(P * 2 * f);
+    w.dgu32 = c.take<float>(P * 2 * f);
+    w.acc = c.take<float>((size_t)T * d);
+    return w;
+}
+
+int backward_B(int T, int E, int k) { return (double)T * k / E <= 4 ? 16 : 32; }
+
+int check_backward(int T, int d, int f, int E, int k, int B) {
+    int rc = check_shape(T, d, f, E, k, B == 0 ? 32 : B, 0);
+    if (rc) return rc;
+    if (B != 0 && B != 16 && B != 32)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward runs sort blocks of 16 or 32 rows (got B=%d)", B);
+    if ((int64_t)E * 2 * f * d >= (int64_t(1) << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "the backward's weight copies need E*2f*d below 2^31");
+    return MOE_OK;
+}
+}  // namespace
+
+size_t moe_backward_workspace_bytes(int T, int d, int f, int E, int k, int B) {
+    if (check_backward(T, d, f, E, k, B) != MOE_OK) return 0;
+    if (B == 0) B = backward_B(T, E, k);
+    Carver c(nullptr);
+    carve_backward(c, T, d, f, E, k, B);
+    return c.bytes();
+}
+
+int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const int32_t *topk_ids,
+                 const float *topk_w, const void *w13, const void *w2, const void *dy, void *dx,
+                 float *dw13, float *dw2, float *dtopk_w, void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    int rc = check_backward(T, d, f, E, k, B);
+    if (rc) return rc;
+    if (B == 0) B = backward_B(T, E, k);
+    if (!w13 || !w2 || !dw13 || !dw2 || (T > 0 && (!x || !topk_ids || !topk_w || !dy || !dx || !dtopk_w)))
+        return fail(MOE_ERR_INVALID_ARG, "null pointer");
+    Carver c(nullptr);
+    carve_backward(c, T, d, f, E, k, B);
+    if (ws_bytes < c.bytes() || !ws)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, c.bytes());
+    hipStream_t s = (hipStream_t)stream;
+    if (T == 0) {   // no assignment: zero weight gradients
+        HIP_TRY(launch_fill_f32(dw13, (size_t)E * 2 * f * d, 0.0f, s), "fill launch");
+        HIP_TRY(launch_fill_f32(dw2, (size_t)E * d * f, 0.0f, s), "fill launch");
+        return MOE_OK;
+    }
+    Carver cw(ws);
+    BwdWs w = carve_backward(cw, T, d, f, E, k, B);
+    const GemmShape sh{T, d, f, E, k, B, 0};
+    HIP_TRY(launch_sort(topk_ids, topk_w, T, k, E, B, w.sorted_ids, w.sorted_w, w.seid, w.counts,
+                        w.offsets, w.num_valid, s),
+            "sort launch");
+    HIP_TRY(launch_transpose_bf16(static_cast<const uint16_t *>(w13), E, 2 * f, d, w.w13t, s),
+            "transpose launch");
+    HIP_TRY(launch_transpose_bf16(static_cast<const uint16_t *>(w2), E, d, f, w.w2t, s),
+            "transpose launch");
+    // forward GEMM1 again, keeping the gate / up sums
+    Gemm1Args g{};
+    g.sh = sh;
+    g.a = x;
+    g.w13 = w13;
+    g.sorted_ids = w.sorted_ids;
+    g.sorted_expert_ids = w.seid;
+    g.num_valid = w.num_valid;
+    g.h = w.h;
+    g.gu_out = w.gu;
+    HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
+    HIP_TRY(launch_fill_f32(dtopk_w, (size_t)T * k, 0.0f, s), "fill launch");
+    HIP_TRY(launch_fill_f32(w.acc, (size_t)T * d, 0.0f, s), "fill launch");
+    // dg, du and the routing-weight gradients from v = Wd^T dy
+    HIP_TRY(launch_stream_bwd_dh(sh, static_cast<const uint16_t *>(dy), w.w2t, w.sorted_ids,
+                                 w.sorted_w, w.seid, w.gu, w.h, w.dgu, w.dgu32, dtopk_w, s),
+            "backward GEMM launch");
+    // dx = Wg^T dg + Wu^T du summed over each token's assignments (unit weights)
+    Gemm2Args g2{};
+    g2.sh = GemmShape{T, d, 2 * f, E, k, B, 0};
+    g2.h = w.dgu;
+    g2.w2 = w.w13t;
+    g2.sorted_ids = w.sorted_ids;
+    g2.sorted_w = nullptr;
+    g2.sorted_expert_ids = w.seid;
+    g2.num_valid = w.num_valid;
+    g2.acc = w.acc;
+    const int ks = auto_ksplit(T, d, 2 * f, E, k, B, 0, cu_count_cached());
+    HIP_TRY(launch_stream_gemm2(g2, MOE_G2_CT, ks, s), "backward GEMM launch");
+    HIP_TRY(launch_finalize(w.acc, static_cast<uint16_t *>(dx), (size_t)T * d, s), "finalize launch");
+    // weight gradients: dWd = sum dz h^T (dz = w dy), dW13 = sum [dg du] x^T
+    HIP_TRY(launch_wgrad(WgradOperand{static_cast<const uint16_t *>(dy), nullptr, 1, 1},
+                         WgradOperand{w.h, nullptr, 0, 0}, d, f, T, k, E, w.sorted_ids, w.sorted_w,
+                         w.offsets, dw2, s),
+            "weight-gradient launch");
+    HIP_TRY(launch_wgrad(WgradOperand{nullptr, w.dgu32, 0, 0},
+                         WgradOperand{static_cast<const uint16_t *>(x), nullptr, 1, 0}, 2 * f, d, T, k,
+                         E, w.sorted_ids, w.sorted_w, w.offsets, dw13, s),
+            "weight-gradient launch");
+    return MOE_OK;
+}
+
 int moe_load_config_table(const char *path, int *rows) {
     g_err[0] = 0;
     if (rows) *rows = 0;

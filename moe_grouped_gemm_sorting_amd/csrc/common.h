@@ -63,6 +63,16 @@ __device__ __forceinline__ float silu(float z) {
     return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
+// logistic sigmoid and the derivative of silu: silu'(z) = s (1 + z (1 - s))
+__device__ __forceinline__ float sigmoid(float z) {
+    constexpr float kLog2e = 1.44269504088896341f;
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+__device__ __forceinline__ float silu_grad(float z) {
+    const float s = sigmoid(z);
+    return s * (1.0f + z * (1.0f - s));
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

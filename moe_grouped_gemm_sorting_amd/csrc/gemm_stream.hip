@@ -48,6 +48,20 @@ struct StreamParams {
     const uint8_t *w_mx;     // quant 3: E8M0 scales of the weights [E, N, K/32]
     uint8_t *out_mx;         // GEMM1 quant 3: E8M0 scales of h [P, f/32]
     int a_rows;              // quant 3: rows of a_mx (GEMM1: T tokens, GEMM2: P slots)
+    // backward (bf16 GEMM1 only): gu_out receives the raw gate / up sums
+    // [P, 2f] fp32 next to h. With bwd set the kernel computes v = Wd^T dy
+    // (A = dy rows by token, weights Wd^T [E, f, d] split into "gate" rows
+    // 0..f/2 and "up" rows f/2..f) and its epilogue turns v into the SwiGLU
+    // input gradients dg, du [P, 2f] bf16 (from gu and the slot's routing
+    // weight) and adds <v, h> into the routing-weight gradient of the
+    // assignment (fp32 atomics); bwd_f is the layer's f.
+    float *gu_out;
+    int bwd, bwd_f;
+    const float *bwd_gu;
+    const uint16_t *bwd_h;
+    uint16_t *bwd_dgu;
+    float *bwd_dgu32;        // the same gradients in fp32 (for the weight gradients)
+    float *bwd_dtw;
     int T, d, f, k, B;
     int kchunk;              // K elements per blockIdx.y
     int rotate;              // start the K loop at a step given by the column tile
@@ -493,6 +507,43 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
     }
 
     // ------------------------------------------------------------ epilogue
+    if constexpr (GEMM1 && QUANT == 0) {
+        if (p.bwd) {
+            const int fb = p.bwd_f;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = lg * 4 + i;
+                    const int a = __shfl(a_of_lane[rt], r, 64);
+                    const int slot = slot0 + rt * 16 + r;
+                    const bool ok = a < sentinel;   // the same for the row's 16 lanes
+                    const float w = ok ? p.sorted_w[slot] : 0.0f;
+                    float dwp = 0.0f;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct) {
+                            if (!ok) continue;
+                            const int col = half * p.f + n0 + ct * 16 + lr;
+                            const float v = acc[rt][half * CT + ct][i];
+                            const size_t gi = (size_t)slot * 2 * fb + col;
+                            const float g = p.bwd_gu[gi], u = p.bwd_gu[gi + fb];
+                            dwp += v * bf16_bits_to_f32(p.bwd_h[(size_t)slot * fb + col]);
+                            const float dh = w * v;
+                            const float dg = dh * u * silu_grad(g), du = dh * silu(g);
+                            p.bwd_dgu[gi] = f32_to_bf16_bits(dg);
+                            p.bwd_dgu[gi + fb] = f32_to_bf16_bits(du);
+                            p.bwd_dgu32[gi] = dg;
+                            p.bwd_dgu32[gi + fb] = du;
+                        }
+#pragma unroll
+                    for (int o = 8; o > 0; o >>= 1) dwp += __shfl_xor(dwp, o, 64);
+                    if (ok && lr == 0) atomic_add_f32(p.bwd_dtw + a, dwp);
+                }
+            return;
+        }
+    }
     if constexpr (GEMM1) {
         const int f = p.f;
         __shared__ float amax_lds[4][RT * 16];
@@ -514,6 +565,12 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
                         const int n = n0 + ct * 16 + lr;
                         g = g * sx * p.w_scale[(size_t)e * Ntot + n];
                         u = u * sx * p.w_scale[(size_t)e * Ntot + f + n];
+                    }
+                    if (QUANT == 0 && p.gu_out) {
+                        const int slot = slot0 + rt * 16 + r;
+                        const int n = n0 + ct * 16 + lr;
+                        p.gu_out[(size_t)slot * 2 * f + n] = g;
+                        p.gu_out[(size_t)slot * 2 * f + f + n] = u;
                     }
                     const float h = bf16_bits_to_f32(f32_to_bf16_bits(silu(g) * u));
                     hv[rt][ct][i] = h;
@@ -590,7 +647,7 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
                 const int slot = slot0 + rt * 16 + r;
                 const int a = __shfl(a_of_lane[rt], r, 64);
                 if (a >= sentinel) continue;
-                float wgt = p.sorted_w[slot];
+                float wgt = p.sorted_w ? p.sorted_w[slot] : 1.0f;
                 if constexpr (QUANT == 1) wgt *= p.a_scale[slot];
                 float *dst = accg + (size_t)(a / p.k) * p.d;
 #pragma unroll
@@ -690,6 +747,7 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
     p.a_rows = sh.T;
     p.w_mx = g.w13_mx;
     p.out_mx = g.h_mx;
+    p.gu_out = g.gu_out;
     // quant 2: one 128-column quant block per workgroup; quant 3: one
     // 32-column MXFP4 block per wave
     if (sh.quant == 2 || sh.quant == 3) CT = 2;
@@ -698,6 +756,36 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
     const int NB = (P + sh.B - 1) / sh.B;
     const dim3 grid(sh.f / (64 * CT), 1, NB);
     return dispatch<true>(p, sh.quant, RT, CT, grid, s);
+}
+
+// Backward of the down projection and SwiGLU (bf16): v = Wd^T dy per slot,
+// then dg, du and the routing-weight gradient (see StreamParams). B = 16 or 32.
+hipError_t launch_stream_bwd_dh(const GemmShape &sh, const uint16_t *dy, const uint16_t *w2t,
+                                const int32_t *sorted_ids, const float *sorted_w,
+                                const int32_t *sorted_expert_ids, const float *gu,
+                                const uint16_t *h, uint16_t *dgu, float *dgu32, float *dtw,
+                                hipStream_t s) {
+    StreamParams p{};
+    p.a = reinterpret_cast<const uint8_t *>(dy);
+    p.w = reinterpret_cast<const uint8_t *>(w2t);
+    p.sorted_ids = sorted_ids;
+    p.sorted_w = sorted_w;
+    p.seid = sorted_expert_ids;
+    p.T = sh.T; p.d = sh.d; p.f = sh.f / 2; p.k = sh.k; p.B = sh.B;
+    p.kchunk = sh.d;
+    p.rotate = MOE_STREAM_ROTATE & 1;
+    p.bwd = 1;
+    p.bwd_f = sh.f;
+    p.bwd_gu = gu;
+    p.bwd_h = h;
+    p.bwd_dgu = dgu;
+    p.bwd_dgu32 = dgu32;
+    p.bwd_dtw = dtw;
+    const int CT = 1, RT = sh.B / 16;
+    const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
+    const int NB = (P + sh.B - 1) / sh.B;
+    const dim3 grid(p.f / (64 * CT), 1, NB);
+    return dispatch<true>(p, 0, RT, CT, grid, s);
 }
 
 hipError_t launch_stream_gemm2(const Gemm2Args &g, int CT, int ksplit, hipStream_t s) {

@@ -63,6 +63,7 @@ struct Gemm1Args {
     // scales a_mx [T, d/32], w13_mx [E, 2f, d/32], h_mx [P, f/32] (out)
     const uint8_t *a_mx, *w13_mx;
     uint8_t *h_mx;
+    float *gu_out;          // optional (bf16 streaming kernel): raw gate / up sums [P, 2f] fp32
 };
 
 struct Gemm2Args {
@@ -77,8 +78,32 @@ struct Gemm2Args {
     const int32_t *sorted_expert_ids, *num_valid;
     float *acc;             // fp32 [T, d], zeroed by the caller
     float *yrows;           // tiled kernel: rows [parts][T*k, d] by K part and assignment instead of acc
+                            // (sorted_w NULL: unit weights, streaming kernel)
     const uint8_t *h_mx, *w2_mx;   // quant 3: E8M0 scales [P, f/32] and [E, d, f/32]
 };
+
+// ---- backward of the bf16 layer (streaming kernel, B = 16 or 32)
+hipError_t launch_stream_bwd_dh(const GemmShape &sh, const uint16_t *dy, const uint16_t *w2t,
+                                const int32_t *sorted_ids, const float *sorted_w,
+                                const int32_t *sorted_expert_ids, const float *gu,
+                                const uint16_t *h, uint16_t *dgu, float *dgu32, float *dtw,
+                                hipStream_t s);
+// out[e] = in[e]^T for E matrices [R, C] bf16 (R, C multiples of 64)
+hipError_t launch_transpose_bf16(const uint16_t *in, int E, int R, int C, uint16_t *out, hipStream_t s);
+// Weight gradient per expert: C[e] [M, N] fp32 = sum over the expert's slots
+// of P[slot]^T Q[slot]; a row of P / Q (length M / N) is taken by token
+// (by_token: row = sorted_ids[slot] / k) or by slot, P rows optionally
+// scaled by the slot's routing weight; padding slots add nothing. M, N
+// multiples of 64.
+struct WgradOperand {
+    const uint16_t *base;   // bf16 rows, or
+    const float *base32;    // fp32 rows (P only; used when non-NULL)
+    int by_token;
+    int scale_by_w;         // P only
+};
+hipError_t launch_wgrad(WgradOperand P, WgradOperand Q, int M, int N, int T, int k, int E,
+                        const int32_t *sorted_ids, const float *sorted_w, const int32_t *offsets,
+                        float *C, hipStream_t s);
 
 bool onestage_supported(const GemmShape &sh);
 hipError_t launch_moe_1stage(const GemmShape &sh, const void *x, const void *w13, const void *w2,
