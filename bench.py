@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--stage", type=int, default=0)
     ap.add_argument("--ksplit", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer's backward (moe_backward, bf16 workloads) instead of the "
+                         "forward; prints its own JSON line")
     ap.add_argument("--cpu-sample", type=int, default=32, help="tokens the CPU oracle runs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU sample until this much time has run")
@@ -120,6 +123,57 @@ def record_traffic(workload, fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
+def bench_backward(args, wl, x, logits, ws, dev):
+    """K steps of moe_backward on resident inputs (the forward's routing, a
+    random output gradient). Roofline: HBM, counting each touched expert's
+    weights read once, every expert's fp32 weight gradients written once, and
+    x, dy, dx."""
+    import torch
+
+    import moe_grouped_gemm_sorting_amd as moe
+
+    if wl.quant != "bf16":
+        print("the backward is built for bf16 layers", file=sys.stderr)
+        sys.exit(2)
+    ids, w = moe.moe_topk(logits, wl.k, wl.score)
+    g = torch.Generator(device=dev).manual_seed(wl.seed + 7)
+    dy = torch.randn(wl.T, wl.d, generator=g, device=dev).bfloat16()
+    B = args.B
+    nbytes = moe.moe_backward_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, B)
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def step():
+        moe.moe_backward(x, ws["w13"], ws["w2"], dy, ids, w, B=B, workspace=workspace)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    touched = int(torch.unique(ids).numel())
+    d, f, E, T = wl.d, wl.f, wl.E, wl.T
+    wbytes = touched * 3 * f * d * 2 + E * 3 * f * d * 4 + 3 * T * d * 2
+    flops = T * wl.k * 2 * (3 * d * f) * 3 + T * wl.k * 2 * 2 * f * d   # fwd GEMM1 + dh + dx + 2 wgrads
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] moe_backward: {ms * 1e3:.1f} us/step, {T / (ms / 1e3):,.0f} tokens/s, "
+        f"{gbs:.0f} GB/s against the algorithmic bytes")
+    result = {
+        "metric": "fused-MoE backward tokens/s (bf16; dx, dW13, dW2, routing-weight gradients)",
+        "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "d": d, "f": f, "E": E, "k": wl.k,
+                   "B": B or (16 if T * wl.k / E <= 4 else 32), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "the whole backward",
+                     "algorithmic_bytes": wbytes, "flops": flops, "touched_experts": touched},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -143,6 +197,9 @@ def main():
     x, logits = wl.activations(dev)
     ws = wl.weights(dev)
     torch.cuda.synchronize()
+    if args.backward:
+        bench_backward(args, wl, x, logits, ws, dev)
+        return
 
     B, stage, ksplit = moe.moe_select_config(wl.T, wl.d, wl.f, wl.E, wl.k, wl.quant)
     B = args.B or B
