@@ -100,11 +100,11 @@ def test_validation_before_any_device_call(lib):
     assert lib.moe_backward_workspace_bytes(4, 128, 256, 4, 2, 64) == 0
     assert lib.moe_backward_workspace_bytes(4, 100, 256, 4, 2, 16) == 0
     n = lib.moe_backward_workspace_bytes(4, 128, 256, 4, 2, 0)
-    assert n > 0 and n == lib.moe_backward_workspace_bytes(4, 128, 256, 4, 2, 32)
+    assert n > 0 and n == lib.moe_backward_workspace_bytes(4, 128, 256, 4, 2, 16)   # 2 rows per expert
     bw = [None] * 10
     assert lib.moe_backward(4, 128, 256, 4, 2, 64, *bw, None, 0, S) == 2
     assert lib.moe_backward(4, 128, 256, 4, 2, 32, *bw, None, 0, S) == 1 and "null" in _err(lib)
-    assert lib.moe_backward(4, 128, 256, 4, 2, 32, *([fake] * 10), fake, n - 1, S) == 3
+    assert lib.moe_backward(4, 128, 256, 4, 2, 0, *([fake] * 10), fake, n - 1, S) == 3
 
 
 def test_workspace_queries_grow_with_the_problem(lib):
