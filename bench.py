@@ -123,6 +123,15 @@ def record_traffic(workload, fetch_dir, write_dir):
     print(json.dumps(rec))
 
 
+def backward_block(T, d, f, E, k):
+    """The library's default sort block for the backward (streaming kernels
+    for few rows per expert, tiled kernels from 64 rows per expert on)."""
+    rows = T * k / E
+    if rows >= 64 and d % 256 == 0 and f % 256 == 0:
+        return 256 if rows >= 256 else (128 if rows >= 128 else 64)
+    return 16 if rows <= 4 else 32
+
+
 def bench_backward(args, wl, x, logits, ws, dev):
     """K steps of moe_backward on resident inputs (the forward's routing, a
     random output gradient). Roofline: HBM, counting each touched expert's
@@ -156,7 +165,8 @@ def bench_backward(args, wl, x, logits, ws, dev):
     touched = int(torch.unique(ids).numel())
     d, f, E, T = wl.d, wl.f, wl.E, wl.T
     wbytes = touched * 3 * f * d * 2 + E * 3 * f * d * 4 + 3 * T * d * 2
-    flops = T * wl.k * 2 * (3 * d * f) * 3 + T * wl.k * 2 * 2 * f * d   # fwd GEMM1 + dh + dx + 2 wgrads
+    # per assignment: GEMM1 recompute 4df, dh 2df, dx 4df, dW13 4df, dW2 2df
+    flops = 16 * T * wl.k * d * f
     gbs = wbytes / (ms * 1e-3) / 1e9
     log(f"[bench] moe_backward: {ms * 1e3:.1f} us/step, {T / (ms / 1e3):,.0f} tokens/s, "
         f"{gbs:.0f} GB/s against the algorithmic bytes")
@@ -166,7 +176,7 @@ def bench_backward(args, wl, x, logits, ws, dev):
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "T": T, "d": d, "f": f, "E": E, "k": wl.k,
-                   "B": B or (16 if T * wl.k / E <= 4 else 32), "parallelism": "single GPU"},
+                   "B": B or backward_block(T, d, f, E, wl.k), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "the whole backward",
                      "algorithmic_bytes": wbytes, "flops": flops, "touched_experts": touched},

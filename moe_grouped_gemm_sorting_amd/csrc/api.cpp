@@ -571,8 +571,12 @@ namespace {
 struct BwdWs {
     int32_t *sorted_ids = nullptr, *seid = nullptr, *counts = nullptr, *offsets = nullptr,
             *num_valid = nullptr;
-    float *sorted_w = nullptr, *gu = nullptr, *acc = nullptr, *dgu32 = nullptr;
+    float *sorted_w = nullptr, *gu = nullptr, *acc = nullptr;
     uint16_t *w13t = nullptr, *w2t = nullptr, *h = nullptr, *dgu = nullptr;
+    uint16_t *dgu_lo = nullptr;   // low bf16 parts of dg / du [P, 2f]
+    uint16_t *xs = nullptr;       // x in slot order [P, d]
+    uint16_t *dz_hi = nullptr, *dz_lo = nullptr;   // w dy in slot order, two bf16 parts [P, d]
+    float *v = nullptr;           // tiled path: Wd^T dy per slot [P, f]
 };
 
 BwdWs carve_backward(Carver &c, int T, int d, int f, int E, int k, int B) {
@@ -589,18 +593,43 @@ BwdWs carve_backward(Carver &c, int T, int d, int f, int E, int k, int B) {
     w.gu = c.take<float>(P * 2 * f);
     w.h = c.take<uint16_t>(P * f);
     w.dgu = c.take<uint16_t>(P * 2 * f);
-    w.dgu32 = c.take<float>(P * 2 * f);
+    w.dgu_lo = c.take<uint16_t>(P * 2 * f);
     w.acc = c.take<float>((size_t)T * d);
+    w.xs = c.take<uint16_t>(P * d);
+    w.dz_hi = c.take<uint16_t>(P * d);
+    w.dz_lo = c.take<uint16_t>(P * d);
+    if (B >= 64) w.v = c.take<float>(P * f);
     return w;
 }
 
-int backward_B(int T, int E, int k) { return (double)T * k / E <= 4 ? 16 : 32; }
+// The backward's GEMMs on the tiled kernels (sort blocks of 64, 128 or 256
+// rows): the forward sums, v = Wd^T dy with Wd^T [E, f, d] taken as two
+// halves of f/2 rows, and dx with K = 2f.
+bool backward_tiled_ok(int T, int d, int f, int E, int k, int B) {
+    return f % 256 == 0 && tiled_gemm_supported(GemmShape{T, d, f, E, k, B, 0}) &&
+           tiled_gemm_supported(GemmShape{T, d, f / 2, E, k, B, 0}) &&
+           tiled_gemm_supported(GemmShape{T, d, 2 * f, E, k, B, 0});
+}
+
+// Streaming kernels (16 / 32-row blocks) while experts average few rows,
+// tiled kernels (a block about the size of an expert's rows, at most 256)
+// from 64 rows per expert on.
+int backward_B(int T, int d, int f, int E, int k) {
+    const double rows = (double)T * k / E;
+    if (rows >= 64) {
+        const int B = rows >= 256 ? 256 : (rows >= 128 ? 128 : 64);
+        if (backward_tiled_ok(T, d, f, E, k, B)) return B;
+    }
+    return rows <= 4 ? 16 : 32;
+}
 
 int check_backward(int T, int d, int f, int E, int k, int B) {
     int rc = check_shape(T, d, f, E, k, B == 0 ? 32 : B, 0);
     if (rc) return rc;
-    if (B != 0 && B != 16 && B != 32)
-        return fail(MOE_ERR_UNSUPPORTED, "the backward runs sort blocks of 16 or 32 rows (got B=%d)", B);
+    if (B != 0 && B != 16 && B != 32 && B != 64 && B != 128 && B != 256)
+        return fail(MOE_ERR_UNSUPPORTED, "the backward runs sort blocks of 16, 32, 64, 128 or 256 rows (got B=%d)", B);
+    if (B >= 64 && !backward_tiled_ok(T, d, f, E, k, B))
+        return fail(MOE_ERR_UNSUPPORTED, "the backward's tiled GEMMs need d %% 256 == 0 and f %% 256 == 0 (B=%d)", B);
     if ((int64_t)E * 2 * f * d >= (int64_t(1) << 31))
         return fail(MOE_ERR_UNSUPPORTED, "the backward's weight copies need E*2f*d below 2^31");
     return MOE_OK;
@@ -609,7 +638,7 @@ int check_backward(int T, int d, int f, int E, int k, int B) {
 
 size_t moe_backward_workspace_bytes(int T, int d, int f, int E, int k, int B) {
     if (check_backward(T, d, f, E, k, B) != MOE_OK) return 0;
-    if (B == 0) B = backward_B(T, E, k);
+    if (B == 0) B = backward_B(T, d, f, E, k);
     Carver c(nullptr);
     carve_backward(c, T, d, f, E, k, B);
     return c.bytes();
@@ -621,7 +650,7 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
     g_err[0] = 0;
     int rc = check_backward(T, d, f, E, k, B);
     if (rc) return rc;
-    if (B == 0) B = backward_B(T, E, k);
+    if (B == 0) B = backward_B(T, d, f, E, k);
     if (!w13 || !w2 || !dw13 || !dw2 || (T > 0 && (!x || !topk_ids || !topk_w || !dy || !dx || !dtopk_w)))
         return fail(MOE_ERR_INVALID_ARG, "null pointer");
     Carver c(nullptr);
@@ -644,6 +673,8 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
             "transpose launch");
     HIP_TRY(launch_transpose_bf16(static_cast<const uint16_t *>(w2), E, d, f, w.w2t, s),
             "transpose launch");
+    HIP_TRY(launch_fill_f32(dtopk_w, (size_t)T * k, 0.0f, s), "fill launch");
+    HIP_TRY(launch_fill_f32(w.acc, (size_t)T * d, 0.0f, s), "fill launch");
     // forward GEMM1 again, keeping the gate / up sums
     Gemm1Args g{};
     g.sh = sh;
@@ -654,13 +685,6 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
     g.num_valid = w.num_valid;
     g.h = w.h;
     g.gu_out = w.gu;
-    HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
-    HIP_TRY(launch_fill_f32(dtopk_w, (size_t)T * k, 0.0f, s), "fill launch");
-    HIP_TRY(launch_fill_f32(w.acc, (size_t)T * d, 0.0f, s), "fill launch");
-    // dg, du and the routing-weight gradients from v = Wd^T dy
-    HIP_TRY(launch_stream_bwd_dh(sh, static_cast<const uint16_t *>(dy), w.w2t, w.sorted_ids,
-                                 w.sorted_w, w.seid, w.gu, w.h, w.dgu, w.dgu32, dtopk_w, s),
-            "backward GEMM launch");
     // dx = Wg^T dg + Wu^T du summed over each token's assignments (unit weights)
     Gemm2Args g2{};
     g2.sh = GemmShape{T, d, 2 * f, E, k, B, 0};
@@ -671,17 +695,42 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
     g2.sorted_expert_ids = w.seid;
     g2.num_valid = w.num_valid;
     g2.acc = w.acc;
-    const int ks = auto_ksplit(T, d, 2 * f, E, k, B, 0, cu_count_cached());
-    HIP_TRY(launch_stream_gemm2(g2, MOE_G2_CT, ks, s), "backward GEMM launch");
+    if (B >= 64) {
+        HIP_TRY(launch_tiled_gemm1(g, 0, 0, s), "GEMM1 launch");
+        // v = Wd^T dy per slot: Wd^T [E, f, d] as GEMM1 weights of f/2 gate and f/2 up rows
+        Gemm1Args gv{};
+        gv.sh = GemmShape{T, d, f / 2, E, k, B, 0};
+        gv.a = dy;
+        gv.w13 = w.w2t;
+        gv.sorted_ids = w.sorted_ids;
+        gv.sorted_expert_ids = w.seid;
+        gv.num_valid = w.num_valid;
+        gv.gu_out = w.v;
+        HIP_TRY(launch_tiled_gemm1(gv, 0, 0, s), "backward GEMM launch");
+        HIP_TRY(launch_bwd_swiglu(w.gu, w.v, w.sorted_ids, w.sorted_w, (int)max_padded(T, k, E, B), T, k, f,
+                                  w.h, w.dgu, w.dgu_lo, dtopk_w, s),
+                "backward SwiGLU launch");
+        HIP_TRY(launch_tiled_gemm2(g2, 0, 0, 1, s), "backward GEMM launch");
+    } else {
+        HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
+        // dg, du and the routing-weight gradients from v = Wd^T dy
+        HIP_TRY(launch_stream_bwd_dh(sh, static_cast<const uint16_t *>(dy), w.w2t, w.sorted_ids,
+                                     w.sorted_w, w.seid, w.gu, w.h, w.dgu, w.dgu_lo, dtopk_w, s),
+                "backward GEMM launch");
+        const int ks = auto_ksplit(T, d, 2 * f, E, k, B, 0, cu_count_cached());
+        HIP_TRY(launch_stream_gemm2(g2, MOE_G2_CT, ks, s), "backward GEMM launch");
+    }
     HIP_TRY(launch_finalize(w.acc, static_cast<uint16_t *>(dx), (size_t)T * d, s), "finalize launch");
-    // weight gradients: dWd = sum dz h^T (dz = w dy), dW13 = sum [dg du] x^T
-    HIP_TRY(launch_wgrad(WgradOperand{static_cast<const uint16_t *>(dy), nullptr, 1, 1},
-                         WgradOperand{w.h, nullptr, 0, 0}, d, f, T, k, E, w.sorted_ids, w.sorted_w,
-                         w.offsets, dw2, s),
+    // weight gradients: dWd = sum dz h^T (dz = w dy), dW13 = sum [dg du] x^T, with x and dz
+    // gathered into slot order first
+    const int P = max_padded(T, k, E, B);
+    HIP_TRY(launch_gather_bwd(w.sorted_ids, w.sorted_w, P, T, k, d, static_cast<const uint16_t *>(x),
+                              static_cast<const uint16_t *>(dy), w.xs, w.dz_hi, w.dz_lo, s),
+            "gather launch");
+    const bool short_seg = (int64_t)T * k <= 256;
+    HIP_TRY(launch_wgrad(w.dz_hi, w.dz_lo, w.h, d, f, E, w.offsets, w.counts, short_seg, dw2, s),
             "weight-gradient launch");
-    HIP_TRY(launch_wgrad(WgradOperand{nullptr, w.dgu32, 0, 0},
-                         WgradOperand{static_cast<const uint16_t *>(x), nullptr, 1, 0}, 2 * f, d, T, k,
-                         E, w.sorted_ids, w.sorted_w, w.offsets, dw13, s),
+    HIP_TRY(launch_wgrad(w.dgu, w.dgu_lo, w.xs, 2 * f, d, E, w.offsets, w.counts, short_seg, dw13, s),
             "weight-gradient launch");
     return MOE_OK;
 }

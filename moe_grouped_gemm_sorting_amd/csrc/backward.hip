@@ -1,8 +1,9 @@
 // backward.hip -- kernels of the bf16 layer's backward pass that the forward
 // GEMMs do not cover: per-expert transposes of the weights (so that the
-// backward GEMMs again reduce over a contiguous dimension) and the weight
-// gradients, which reduce over the rows of each expert's segment of the
-// sorted assignment list.
+// backward GEMMs again reduce over a contiguous dimension), the SwiGLU
+// backward of the tiled path, the gather of the weight gradients' operands
+// into slot order, and the weight gradients, which reduce over the rows of
+// each expert's segment of the sorted assignment list.
 //
 // The backward is the training step the pages name as the next milestone
 // (rocketrecap.com/entries/19116, 10:07; rocketrecap.com/entries/19188,
@@ -31,103 +32,297 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t *__restri
     for (int c = ty; c < 64; c += 4) dst[(size_t)(c0 + c) * R + r0 + tx] = tile[tx][c];
 }
 
-// C[e] [M, N] = sum over slots of the expert's segment of P[slot]^T Q[slot].
-// Workgroup: a 64 x 64 tile of C; 4 waves of 32 x 32 (one 32x32x16 bf16 MFMA
-// accumulator each). The segment is walked 32 rows at a time: each thread
-// loads 8 values of one row of P and of Q and stores them transposed into
-// LDS ([column][row], rows contiguous), so that an MFMA operand (8
-// consecutive K = rows of one column) is one 16-byte LDS read. P is an fp32
-// value in general (a routing weight times dy, or the fp32 dg / du), so it
-// enters as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), and two MFMAs:
-// about 16 mantissa bits, against 8 for a plain bf16 operand. Q (x or h) is
-// exactly bf16.
-constexpr int WG_ROWS = 32;
-constexpr int LDSW = WG_ROWS + 8;   // padded row of the transposed tiles (bf16)
+// SwiGLU backward for the tiled path, from the recomputed gate / up sums
+// gu [P, 2f] and v = Wd^T dy [P, f] (fp32, slot order) of a real slot with
+// routing weight w: h = bf16(silu(g) u) (the forward's h), dh = w v,
+// dg = dh u silu'(g), du = dh silu(g), each stored as two bf16 parts
+// (dgu = bf16(x), dgu_lo = bf16(x - dgu), [P, 2f]), and the routing-weight
+// gradient dtw[a] += sum over the row of v h (one atomic per workgroup).
+// Workgroup: 2048 columns of one slot, 8 per thread; padding slots are
+// skipped (nothing reads their rows).
+__global__ __launch_bounds__(256) void k_bwd_swiglu(const float *__restrict__ gu, const float *__restrict__ v,
+                                                    const int32_t *__restrict__ sorted_ids,
+                                                    const float *__restrict__ sorted_w, int T, int k, int f,
+                                                    uint16_t *__restrict__ h, uint16_t *__restrict__ dgu,
+                                                    uint16_t *__restrict__ dgu_lo, float *__restrict__ dtw) {
+    __shared__ float red[4];
+    const int slot = blockIdx.x;
+    const int a = sorted_ids[slot];
+    if (a >= T * k) return;
+    const float w = sorted_w[slot];
+    const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+    float part = 0.0f;
+    if (c < f) {
+        const size_t f2 = 2 * (size_t)f;
+        const float *gp = gu + (size_t)slot * f2 + c;
+        const float *vp = v + (size_t)slot * f + c;
+        float g[8], u[8], vv[8];
+#pragma unroll
+        for (int j = 0; j < 8; j += 4) {
+            const float4 g4 = *reinterpret_cast<const float4 *>(gp + j);
+            const float4 u4 = *reinterpret_cast<const float4 *>(gp + f + j);
+            const float4 v4 = *reinterpret_cast<const float4 *>(vp + j);
+            g[j] = g4.x; g[j + 1] = g4.y; g[j + 2] = g4.z; g[j + 3] = g4.w;
+            u[j] = u4.x; u[j + 1] = u4.y; u[j + 2] = u4.z; u[j + 3] = u4.w;
+            vv[j] = v4.x; vv[j + 1] = v4.y; vv[j + 2] = v4.z; vv[j + 3] = v4.w;
+        }
+        uint32_t hw[4], gh[4], gl[4], uh[4], ul[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            uint32_t hb[2], dgh[2], dgl[2], duh[2], dul[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float gg = g[j + i], uu = u[j + i], vi = vv[j + i];
+                const uint16_t hbits = f32_to_bf16_bits(silu(gg) * uu);
+                part += vi * bf16_bits_to_f32(hbits);
+                const float dh = w * vi;
+                const float dg = dh * uu * silu_grad(gg), du = dh * silu(gg);
+                const uint16_t dgb = f32_to_bf16_bits(dg), dub = f32_to_bf16_bits(du);
+                hb[i] = hbits;
+                dgh[i] = dgb;
+                dgl[i] = f32_to_bf16_bits(dg - bf16_bits_to_f32(dgb));
+                duh[i] = dub;
+                dul[i] = f32_to_bf16_bits(du - bf16_bits_to_f32(dub));
+            }
+            hw[j / 2] = hb[0] | (hb[1] << 16);
+            gh[j / 2] = dgh[0] | (dgh[1] << 16);
+            gl[j / 2] = dgl[0] | (dgl[1] << 16);
+            uh[j / 2] = duh[0] | (duh[1] << 16);
+            ul[j / 2] = dul[0] | (dul[1] << 16);
+        }
+        const size_t o = (size_t)slot * f2 + c;
+        *reinterpret_cast<uint4 *>(h + (size_t)slot * f + c) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *reinterpret_cast<uint4 *>(dgu + o) = make_uint4(gh[0], gh[1], gh[2], gh[3]);
+        *reinterpret_cast<uint4 *>(dgu + o + f) = make_uint4(uh[0], uh[1], uh[2], uh[3]);
+        *reinterpret_cast<uint4 *>(dgu_lo + o) = make_uint4(gl[0], gl[1], gl[2], gl[3]);
+        *reinterpret_cast<uint4 *>(dgu_lo + o + f) = make_uint4(ul[0], ul[1], ul[2], ul[3]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) atomic_add_f32(dtw + a, red[0] + red[1] + red[2] + red[3]);
+}
 
-__global__ __launch_bounds__(256) void k_wgrad(WgradOperand P, WgradOperand Q, int M, int N, int T,
-                                               int k, const int32_t *__restrict__ sorted_ids,
-                                               const float *__restrict__ sorted_w,
+// The weight gradients' operands in slot order: xs[slot] = x[t] and the
+// fp32 value w[slot] dy[t] as two bf16 parts, dz_hi = bf16(z) and dz_lo =
+// bf16(z - dz_hi), for the assignment a = t k + j in the slot; zeros for
+// padding slots. One thread per (slot, 8 columns).
+__global__ __launch_bounds__(256) void k_gather_bwd(const int32_t *__restrict__ sorted_ids,
+                                                    const float *__restrict__ sorted_w, int P, int T,
+                                                    int k, int d, const uint16_t *__restrict__ x,
+                                                    const uint16_t *__restrict__ dy,
+                                                    uint16_t *__restrict__ xs, uint16_t *__restrict__ dz_hi,
+                                                    uint16_t *__restrict__ dz_lo) {
+    const int g8 = d / 8;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)P * g8) return;
+    const int slot = (int)(i / g8), c = (int)(i % g8) * 8;
+    const int a = sorted_ids[slot];
+    uint4 xv = make_uint4(0, 0, 0, 0);
+    uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
+    if (a < T * k) {
+        const size_t src = (size_t)(a / k) * d + c;
+        xv = *reinterpret_cast<const uint4 *>(x + src);
+        const uint4 dv = *reinterpret_cast<const uint4 *>(dy + src);
+        const float w = sorted_w[slot];
+        const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float z0 = w * bf16_bits_to_f32(dw[j] & 0xffffu);
+            const float z1 = w * bf16_bits_to_f32(dw[j] >> 16);
+            const uint16_t h0 = f32_to_bf16_bits(z0), h1 = f32_to_bf16_bits(z1);
+            hi[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+            lo[j] = (uint32_t)f32_to_bf16_bits(z0 - bf16_bits_to_f32(h0)) |
+                    ((uint32_t)f32_to_bf16_bits(z1 - bf16_bits_to_f32(h1)) << 16);
+        }
+    }
+    const size_t o = (size_t)slot * d + c;
+    *reinterpret_cast<uint4 *>(xs + o) = xv;
+    *reinterpret_cast<uint4 *>(dz_hi + o) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4 *>(dz_lo + o) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
+// C[e] [M, N] = sum over the slots of expert e's segment of P[slot]^T Q[slot]
+// (P = P_hi + P_lo and Q bf16, [slots, M] and [slots, N], in slot order;
+// rows past the expert's count are padding and contribute zeros).
+// Workgroup: a 128 x 128 tile of C, 4 waves of 64 x 64 (2 x 2 accumulators
+// of v_mfma_f32_32x32x16_bf16). The segment is walked 32 rows at a time.
+// Thread t loads rows 4 (t % 8) .. + 3 and columns 4 (t / 8) .. + 3 of a
+// chunk of each operand (8-byte row pieces) and stores them transposed
+// into LDS, [column][row] with 4 rows per 8-byte store, so that an MFMA
+// operand (8 consecutive K = rows of one column) is one 16-byte LDS read.
+// LDS rows are 80 bytes apart: the 16-byte operand reads of 16 lanes then
+// cover all 64 banks once, and the 8-byte stores of 32 lanes (row offset
+// fastest) are conflict-free. Slot-ordered operands make every load address
+// affine in the row, so with NST = 2 LDS stages the loads run 3 chunks ahead
+// in registers (the chunk stored at step c was loaded at step c - 2) and a
+// chunk's store overlaps the previous chunk's MFMAs. NST = 1 (half the LDS,
+// for short segments) loads, stores and multiplies one chunk at a time.
+// P is an fp32 value (a routing weight times dy, or dg / du), which its
+// producer stores as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi); it
+// enters as two MFMAs: about 16 mantissa bits, against 8 for a plain bf16
+// operand (split once there rather than once per column tile of C here). Q
+// (x or h) is exactly bf16.
+// Workgroup barrier for LDS hand-over only: this wave's LDS operations
+// complete, then s_barrier. A __syncthreads() also waits for every
+// outstanding global load (its release fence), which would drain the
+// register prefetch ring at every chunk.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+constexpr int WG_ROWS = 32;
+constexpr int WG_PITCH = WG_ROWS + 8;   // bf16 per LDS row: 80 bytes
+constexpr int WG_RD = 3;                // chunks in flight in registers
+
+struct WgChunk {
+    uint32_t v[3][4][2];   // [P_hi, P_lo, Q][row][column pair]
+    int nreal;             // real rows among the thread's 4 (a prefix)
+};
+
+template <int NST>
+__global__ __launch_bounds__(256) void k_wgrad(const uint16_t *__restrict__ p_hi,
+                                               const uint16_t *__restrict__ p_lo,
+                                               const uint16_t *__restrict__ q, int M, int N,
                                                const int32_t *__restrict__ offsets,
+                                               const int32_t *__restrict__ counts,
                                                float *__restrict__ C) {
-    __shared__ __attribute__((aligned(16))) uint16_t pt[64][LDSW];
-    __shared__ __attribute__((aligned(16))) uint16_t pl[64][LDSW];
-    __shared__ __attribute__((aligned(16))) uint16_t qt[64][LDSW];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[NST][3][128][WG_PITCH];  // [stage][hi, lo, q]
     const int e = blockIdx.z;
-    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int sentinel = T * k;
-    const int beg = offsets[e], end = offsets[e + 1];
+    const int beg = offsets[e];
+    const int real_end = beg + counts[e];
+    // chunks over the real rows (an empty expert has none)
+    const int nch = (real_end - beg + WG_ROWS - 1) / WG_ROWS;
+    // loader: rows lr0 .. lr0 + 3 of a chunk, tile columns lc0 .. lc0 + 3
+    const int lr0 = 4 * (tid & 7), lc0 = 4 * (tid >> 3);
+    const bool pm_ok = m0 + lc0 < M, qn_ok = n0 + lc0 < N;   // M, N multiples of 4
 
-    f32x16 acc;
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-    // loader: thread -> row lr (0..31) of the chunk and 8 columns cs
-    const int lr = tid >> 3, cs = (tid & 7) * 8;
-    auto row_of = [&](const WgradOperand &o, int slot, int a) -> long {
-        return o.by_token ? (long)(a / k) : (long)slot;
+    // Every load is issued (no divergent branch, whose join would make the
+    // compiler wait for it at once): rows past real_end read the last real
+    // row and columns past M / N read column 0; the store zeroes them.
+    const size_t pcol = pm_ok ? (size_t)(m0 + lc0) : 0, qcol = qn_ok ? (size_t)(n0 + lc0) : 0;
+    auto load = [&](WgChunk &ch, int c) {
+        const int r0 = beg + c * WG_ROWS + lr0;
+        ch.nreal = max(0, min(4, real_end - r0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const size_t r = (size_t)min(r0 + i, real_end - 1);
+            const uint2 h = *reinterpret_cast<const uint2 *>(p_hi + r * M + pcol);
+            const uint2 l = *reinterpret_cast<const uint2 *>(p_lo + r * M + pcol);
+            const uint2 u = *reinterpret_cast<const uint2 *>(q + r * N + qcol);
+            ch.v[0][i][0] = h.x; ch.v[0][i][1] = h.y;
+            ch.v[1][i][0] = l.x; ch.v[1][i][1] = l.y;
+            ch.v[2][i][0] = u.x; ch.v[2][i][1] = u.y;
+        }
     };
-    for (int r0 = beg; r0 < end; r0 += WG_ROWS) {
-        const int slot = r0 + lr;
-        const int a = slot < end ? sorted_ids[slot] : sentinel;
-        const bool ok = a < sentinel;
-        const float w = ok ? sorted_w[slot] : 0.0f;
-        float pvals[8];
-        uint4 qv = make_uint4(0, 0, 0, 0);
+    // column j of the thread's 4: rows lr0 .. lr0 + 3 as one 8-byte store
+    // per operand (v_perm picks 16-bit halves; selector bytes 0-3 index the
+    // second operand)
+    auto store = [&](const WgChunk &ch, int st) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pvals[i] = 0.0f;
-        if (ok) {
-            const long pr = row_of(P, slot, a) * M + m0 + cs;
-            if (P.base32) {
-                const float4 u0 = *reinterpret_cast<const float4 *>(P.base32 + pr);
-                const float4 u1 = *reinterpret_cast<const float4 *>(P.base32 + pr + 4);
-                pvals[0] = u0.x; pvals[1] = u0.y; pvals[2] = u0.z; pvals[3] = u0.w;
-                pvals[4] = u1.x; pvals[5] = u1.y; pvals[6] = u1.z; pvals[7] = u1.w;
-            } else {
-                const uint4 pv = *reinterpret_cast<const uint4 *>(P.base + pr);
-                const uint32_t pw[4] = {pv.x, pv.y, pv.z, pv.w};
+        for (int o = 0; o < 3; ++o) {
+            const bool ok = o < 2 ? pm_ok : qn_ok;
+            uint32_t vv[4][2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pvals[2 * i] = bf16_bits_to_f32(pw[i] & 0xffffu);
-                    pvals[2 * i + 1] = bf16_bits_to_f32(pw[i] >> 16);
-                }
+            for (int i = 0; i < 4; ++i) {
+                vv[i][0] = (ok && i < ch.nreal) ? ch.v[o][i][0] : 0u;
+                vv[i][1] = (ok && i < ch.nreal) ? ch.v[o][i][1] : 0u;
             }
-            if (P.scale_by_w)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) pvals[i] *= w;
-            qv = *reinterpret_cast<const uint4 *>(Q.base + row_of(Q, slot, a) * N + n0 + cs);
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                const uint32_t r01 = __builtin_amdgcn_perm(vv[1][j >> 1], vv[0][j >> 1], sel);
+                const uint32_t r23 = __builtin_amdgcn_perm(vv[3][j >> 1], vv[2][j >> 1], sel);
+                *reinterpret_cast<uint2 *>(&lds[st][o][lc0 + j][lr0]) = make_uint2(r01, r23);
+            }
         }
-        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint16_t hi = f32_to_bf16_bits(pvals[i]);
-            pt[cs + i][lr] = hi;
-            pl[cs + i][lr] = f32_to_bf16_bits(pvals[i] - bf16_bits_to_f32(hi));
-            qt[cs + i][lr] = (uint16_t)((i & 1) ? qw[i >> 1] >> 16 : qw[i >> 1] & 0xffffu);
-        }
-        __syncthreads();
-        // two K = 16 sub-steps over the 32 rows; lane half takes rows 8 (lane / 32) ..
+    };
+    // two K = 16 sub-steps over the chunk's 32 rows; lane half lane / 32
+    // takes rows 8 (lane / 32) .. of each
+    auto compute = [&](int st) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int kr = 16 * sub + 8 * (lane >> 5);
-            const u32x4 av = *reinterpret_cast<const u32x4 *>(&pt[32 * wm + (lane & 31)][kr]);
-            const u32x4 al = *reinterpret_cast<const u32x4 *>(&pl[32 * wm + (lane & 31)][kr]);
-            const u32x4 bv = *reinterpret_cast<const u32x4 *>(&qt[32 * wn + (lane & 31)][kr]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
-                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al),
-                                                          __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+            u32x4 ah[2], al[2], bq[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int col = 64 * wm + 32 * a + (lane & 31);
+                ah[a] = *reinterpret_cast<const u32x4 *>(&lds[st][0][col][kr]);
+                al[a] = *reinterpret_cast<const u32x4 *>(&lds[st][1][col][kr]);
+            }
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                bq[b] = *reinterpret_cast<const u32x4 *>(&lds[st][2][64 * wn + 32 * b + (lane & 31)][kr]);
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[a]),
+                                                                        __builtin_bit_cast(bf16x8, bq[b]),
+                                                                        acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al[a]),
+                                                                        __builtin_bit_cast(bf16x8, bq[b]),
+                                                                        acc[a][b], 0, 0, 0);
+                }
         }
-        __syncthreads();
+    };
+    if (nch > 0) {
+        // chunk c lives in ring[c % RD]; the loop is unrolled by RD so the
+        // ring index is a constant, and runs over a multiple of RD chunks so
+        // that it is straight-line code (the compiler's wait counts then stay
+        // exact). Chunks past the last real one have no real rows: they load
+        // the last real row, store zeros and add nothing.
+        constexpr int RD = NST == 2 ? WG_RD : 1;
+        const int nch_pad = (nch + RD - 1) / RD * RD;
+        WgChunk ring[RD];
+#pragma unroll
+        for (int i = 0; i < RD; ++i) load(ring[i], i);
+        store(ring[0], 0);
+        lds_barrier();
+        for (int c0 = 0; c0 < nch_pad; c0 += RD) {
+            static_for<RD>([&](auto ic) {
+                constexpr int r = decltype(ic)::value;
+                const int c = c0 + r;
+                if constexpr (NST == 2) {
+                    compute(c & 1);
+                    store(ring[(r + 1) % RD], (c + 1) & 1);   // stage last read at chunk c - 1
+                    load(ring[r], c + RD);                     // ring[r] (chunk c) is in LDS
+                    lds_barrier();
+                } else {
+                    compute(0);
+                    load(ring[0], c + 1);
+                    lds_barrier();                             // every wave is done with the stage
+                    store(ring[0], 0);
+                    lds_barrier();
+                }
+            });
+        }
     }
     // 32x32 accumulator: lane holds column (lane & 31), rows 8 (v / 4) + 4 (lane / 32) + (v & 3)
     float *dst = C + (size_t)e * M * N;
-    const int n = n0 + 32 * wn + (lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int m = m0 + 32 * wm + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        dst[(size_t)m * N + n] = acc[v];
+    for (int b = 0; b < 2; ++b) {
+        const int n = n0 + 64 * wn + 32 * b + (lane & 31);
+        if (n >= N) continue;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + 64 * wm + 32 * a + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (m < M) dst[(size_t)m * N + n] = acc[a][b][v];
+            }
     }
 }
 
@@ -139,12 +334,37 @@ hipError_t launch_transpose_bf16(const uint16_t *in, int E, int R, int C, uint16
     return hipGetLastError();
 }
 
-hipError_t launch_wgrad(WgradOperand P, WgradOperand Q, int M, int N, int T, int k, int E,
-                        const int32_t *sorted_ids, const float *sorted_w, const int32_t *offsets,
-                        float *C, hipStream_t s) {
+hipError_t launch_bwd_swiglu(const float *gu, const float *v, const int32_t *sorted_ids,
+                             const float *sorted_w, int P, int T, int k, int f, uint16_t *h, uint16_t *dgu,
+                             uint16_t *dgu_lo, float *dtw, hipStream_t s) {
+    if (P == 0) return hipSuccess;
+    if (f % 8) return hipErrorInvalidValue;
+    k_bwd_swiglu<<<dim3(P, (f + 2047) / 2048), 256, 0, s>>>(gu, v, sorted_ids, sorted_w, T, k, f, h, dgu,
+                                                             dgu_lo, dtw);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_bwd(const int32_t *sorted_ids, const float *sorted_w, int P, int T, int k,
+                             int d, const uint16_t *x, const uint16_t *dy, uint16_t *xs, uint16_t *dz_hi,
+                             uint16_t *dz_lo, hipStream_t s) {
+    if (P == 0) return hipSuccess;
+    if (d % 8) return hipErrorInvalidValue;
+    const size_t n = (size_t)P * (d / 8);
+    k_gather_bwd<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(sorted_ids, sorted_w, P, T, k, d, x, dy, xs,
+                                                              dz_hi, dz_lo);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const uint16_t *p_hi, const uint16_t *p_lo, const uint16_t *q, int M, int N, int E,
+                        const int32_t *offsets, const int32_t *counts, bool short_segments, float *C,
+                        hipStream_t s) {
     if (E == 0) return hipSuccess;
-    if (M % 64 || N % 64) return hipErrorInvalidValue;
-    k_wgrad<<<dim3(N / 64, M / 64, E), 256, 0, s>>>(P, Q, M, N, T, k, sorted_ids, sorted_w, offsets, C);
+    if (M % 4 || N % 4) return hipErrorInvalidValue;
+    const dim3 grid((N + 127) / 128, (M + 127) / 128, E);
+    if (short_segments)
+        k_wgrad<1><<<grid, 256, 0, s>>>(p_hi, p_lo, q, M, N, offsets, counts, C);
+    else
+        k_wgrad<2><<<grid, 256, 0, s>>>(p_hi, p_lo, q, M, N, offsets, counts, C);
     return hipGetLastError();
 }
 

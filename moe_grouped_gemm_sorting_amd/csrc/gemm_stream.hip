@@ -60,7 +60,7 @@ struct StreamParams {
     const float *bwd_gu;
     const uint16_t *bwd_h;
     uint16_t *bwd_dgu;
-    float *bwd_dgu32;        // the same gradients in fp32 (for the weight gradients)
+    uint16_t *bwd_dgu_lo;    // bf16(g - bf16(g)) of each gradient: with bwd_dgu, about 16 bits
     float *bwd_dtw;
     int T, d, f, k, B;
     int kchunk;              // K elements per blockIdx.y
@@ -532,10 +532,11 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
                             dwp += v * bf16_bits_to_f32(p.bwd_h[(size_t)slot * fb + col]);
                             const float dh = w * v;
                             const float dg = dh * u * silu_grad(g), du = dh * silu(g);
-                            p.bwd_dgu[gi] = f32_to_bf16_bits(dg);
-                            p.bwd_dgu[gi + fb] = f32_to_bf16_bits(du);
-                            p.bwd_dgu32[gi] = dg;
-                            p.bwd_dgu32[gi + fb] = du;
+                            const uint16_t gh = f32_to_bf16_bits(dg), uh = f32_to_bf16_bits(du);
+                            p.bwd_dgu[gi] = gh;
+                            p.bwd_dgu[gi + fb] = uh;
+                            p.bwd_dgu_lo[gi] = f32_to_bf16_bits(dg - bf16_bits_to_f32(gh));
+                            p.bwd_dgu_lo[gi + fb] = f32_to_bf16_bits(du - bf16_bits_to_f32(uh));
                         }
 #pragma unroll
                     for (int o = 8; o > 0; o >>= 1) dwp += __shfl_xor(dwp, o, 64);
@@ -763,7 +764,7 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
 hipError_t launch_stream_bwd_dh(const GemmShape &sh, const uint16_t *dy, const uint16_t *w2t,
                                 const int32_t *sorted_ids, const float *sorted_w,
                                 const int32_t *sorted_expert_ids, const float *gu,
-                                const uint16_t *h, uint16_t *dgu, float *dgu32, float *dtw,
+                                const uint16_t *h, uint16_t *dgu, uint16_t *dgu_lo, float *dtw,
                                 hipStream_t s) {
     StreamParams p{};
     p.a = reinterpret_cast<const uint8_t *>(dy);
@@ -779,7 +780,7 @@ hipError_t launch_stream_bwd_dh(const GemmShape &sh, const uint16_t *dy, const u
     p.bwd_gu = gu;
     p.bwd_h = h;
     p.bwd_dgu = dgu;
-    p.bwd_dgu32 = dgu32;
+    p.bwd_dgu_lo = dgu_lo;
     p.bwd_dtw = dtw;
     const int CT = 1, RT = sh.B / 16;
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;

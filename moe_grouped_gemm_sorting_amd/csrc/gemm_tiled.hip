@@ -102,6 +102,11 @@ struct TiledParams {
     // [E, N, K/32]; GEMM1 writes h's [P, f/32]
     const uint8_t *a_mx, *w_mx;
     uint8_t *out_mx;
+    // GEMM1, bf16 only: when set, the raw gate / up sums of the real rows go
+    // to raw_out [P, 2f] fp32 (gate at column n, up at f + n) and no h is
+    // written (the backward's recompute of the forward sums, and its
+    // v = Wd^T dy with Wd^T split into two halves)
+    float *raw_out;
 };
 
 // Chunk position of (row, chunk) inside the row's 128 bytes (an involution
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     if (tid < BM) {
         meta_a = p.sorted_ids[slot0 + tid];
         if constexpr (!GEMM1) {
-            meta_w = p.sorted_w[slot0 + tid];
+            meta_w = p.sorted_w ? p.sorted_w[slot0 + tid] : 1.0f;
             if constexpr (QUANT == 1) meta_s = p.a_scale[slot0 + tid];
         }
     }
@@ -564,6 +569,24 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // ---- epilogue -----------------------------------------------------------
     // 32x32 accumulator layout: lane holds column (lane & 31) and rows
     // 8 * (v / 4) + 4 * (lane >> 5) + (v & 3), v = 0..15.
+    if constexpr (GEMM1 && QUANT == 0) {
+        if (p.raw_out) {
+            const size_t f2 = 2 * (size_t)p.f;
+            const int col = nt * (TN / 2) + wn * 32 + lr;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = wm * (BM / WM) + rt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                    if (row_asg[row] < 0) continue;
+                    float *dst = p.raw_out + (size_t)(slot0 + row) * f2 + col;
+                    dst[0] = acc[rt][0][v];
+                    dst[p.f] = acc[rt][1][v];
+                }
+            clear_zero();
+            return;
+        }
+    }
     if constexpr (GEMM1) {
         uint8_t *hs = lds;   // [BM][HROW] bf16 h tile
         const int hcol = wn * 32 + lr;
@@ -779,6 +802,7 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s)
     p.a_mx = g.a_mx;
     p.w_mx = g.w13_mx;
     p.out_mx = g.h_mx;
+    p.raw_out = sh.quant == 0 ? g.gu_out : nullptr;
     const TileShape ts = tile_shape(sh.B, sh.quant, true, bm, tn);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + ts.bm - 1) / ts.bm;

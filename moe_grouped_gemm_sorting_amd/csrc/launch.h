@@ -63,7 +63,8 @@ struct Gemm1Args {
     // scales a_mx [T, d/32], w13_mx [E, 2f, d/32], h_mx [P, f/32] (out)
     const uint8_t *a_mx, *w13_mx;
     uint8_t *h_mx;
-    float *gu_out;          // optional (bf16 streaming kernel): raw gate / up sums [P, 2f] fp32
+    float *gu_out;          // optional (bf16): raw gate / up sums [P, 2f] fp32; the streaming
+                            // kernel also writes h, the tiled kernel writes only these
 };
 
 struct Gemm2Args {
@@ -86,24 +87,28 @@ struct Gemm2Args {
 hipError_t launch_stream_bwd_dh(const GemmShape &sh, const uint16_t *dy, const uint16_t *w2t,
                                 const int32_t *sorted_ids, const float *sorted_w,
                                 const int32_t *sorted_expert_ids, const float *gu,
-                                const uint16_t *h, uint16_t *dgu, float *dgu32, float *dtw,
+                                const uint16_t *h, uint16_t *dgu, uint16_t *dgu_lo, float *dtw,
                                 hipStream_t s);
 // out[e] = in[e]^T for E matrices [R, C] bf16 (R, C multiples of 64)
 hipError_t launch_transpose_bf16(const uint16_t *in, int E, int R, int C, uint16_t *out, hipStream_t s);
-// Weight gradient per expert: C[e] [M, N] fp32 = sum over the expert's slots
-// of P[slot]^T Q[slot]; a row of P / Q (length M / N) is taken by token
-// (by_token: row = sorted_ids[slot] / k) or by slot, P rows optionally
-// scaled by the slot's routing weight; padding slots add nothing. M, N
-// multiples of 64.
-struct WgradOperand {
-    const uint16_t *base;   // bf16 rows, or
-    const float *base32;    // fp32 rows (P only; used when non-NULL)
-    int by_token;
-    int scale_by_w;         // P only
-};
-hipError_t launch_wgrad(WgradOperand P, WgradOperand Q, int M, int N, int T, int k, int E,
-                        const int32_t *sorted_ids, const float *sorted_w, const int32_t *offsets,
-                        float *C, hipStream_t s);
+// Backward, tiled path: from the recomputed sums gu [P, 2f] and v = Wd^T dy
+// [P, f] (fp32, slot order): h [P, f], dg / du as two bf16 parts (dgu,
+// dgu_lo [P, 2f]) and dtw[a] += <v, h> (dtw zeroed by the caller).
+hipError_t launch_bwd_swiglu(const float *gu, const float *v, const int32_t *sorted_ids,
+                             const float *sorted_w, int P, int T, int k, int f, uint16_t *h, uint16_t *dgu,
+                             uint16_t *dgu_lo, float *dtw, hipStream_t s);
+// Backward: xs[slot] = x[t] and w[slot] dy[t] as two bf16 parts dz_hi + dz_lo
+// (zeros for padding slots; P slots).
+hipError_t launch_gather_bwd(const int32_t *sorted_ids, const float *sorted_w, int P, int T, int k,
+                             int d, const uint16_t *x, const uint16_t *dy, uint16_t *xs, uint16_t *dz_hi,
+                             uint16_t *dz_lo, hipStream_t s);
+// Weight gradient per expert: C[e] [M, N] fp32 = sum over expert e's slots
+// of (P_hi + P_lo)[slot]^T Q[slot] (bf16 rows in slot order; rows past the
+// expert's count add nothing). M, N multiples of 4. short_segments: a variant with one LDS stage, for
+// segments of a few chunks.
+hipError_t launch_wgrad(const uint16_t *p_hi, const uint16_t *p_lo, const uint16_t *q, int M, int N, int E,
+                        const int32_t *offsets, const int32_t *counts, bool short_segments, float *C,
+                        hipStream_t s);
 
 bool onestage_supported(const GemmShape &sh);
 hipError_t launch_moe_1stage(const GemmShape &sh, const void *x, const void *w13, const void *w2,

@@ -32,9 +32,16 @@ def _check(name, got, ref):
     assert err <= 2e-2, (name, err)
 
 
-@pytest.mark.parametrize("wl", SHAPES, ids=lambda w: w.name)
-@pytest.mark.parametrize("B", [0, 16, 32])
-def test_backward_matches_the_oracle(wl, B):
+# The tiled path (sort blocks of 64, 128, 256 rows; d and f multiples of 256)
+TILED_SHAPES = [
+    # 128 rows per expert: the default block is 128
+    workloads.Workload("bwd_tiled", T=256, d=256, f=512, E=4, k=2, seed=55),
+    # Zipf-skewed routing, ragged segments, a block size larger than most segments
+    workloads.Workload("bwd_tiled_skew", T=300, d=512, f=256, E=6, k=2, logits="zipf", seed=56),
+]
+
+
+def _run_and_check(wl, B):
     x, logits = wl.activations(DEV)
     ws = wl.weights(DEV)
     ids, w = oracle.route(logits.cpu().numpy(), wl.k, wl.score)
@@ -57,7 +64,20 @@ def test_backward_matches_the_oracle(wl, B):
             assert not dw13[e].any() and not dw2[e].any()
 
 
-def test_backward_rejects_tiled_block_sizes():
+@pytest.mark.parametrize("wl", SHAPES, ids=lambda w: w.name)
+@pytest.mark.parametrize("B", [0, 16, 32])
+def test_backward_matches_the_oracle(wl, B):
+    _run_and_check(wl, B)
+
+
+@pytest.mark.parametrize("wl", TILED_SHAPES, ids=lambda w: w.name)
+@pytest.mark.parametrize("B", [0, 64, 128, 256])
+def test_backward_tiled_matches_the_oracle(wl, B):
+    _run_and_check(wl, B)
+
+
+def test_backward_rejects_tiled_blocks_on_unsupported_shapes():
+    # d = 128 is not a multiple of 256: no tiled backward
     wl = workloads.get("tiny")
     x, logits = wl.activations(DEV)
     ws = wl.weights(DEV)

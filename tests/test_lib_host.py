@@ -96,8 +96,10 @@ def test_validation_before_any_device_call(lib):
     assert lib.moe_quant_act_mx(None, 2, 48, None, None, S) == 1
     assert lib.moe_quant_act_mx(None, 2, 64, None, None, S) == 1 and "null" in _err(lib)
     assert lib.fused_moe_workspace_bytes(4, 256, 256, 4, 2, 3, 64, 2) > 0   # size query only
-    # backward: bf16 streaming blocks only; null pointers; small workspace
+    # backward: tiled blocks need d, f multiples of 256; null pointers; small workspace
     assert lib.moe_backward_workspace_bytes(4, 128, 256, 4, 2, 64) == 0
+    assert lib.moe_backward_workspace_bytes(4, 256, 256, 4, 2, 64) > 0
+    assert lib.moe_backward_workspace_bytes(4, 256, 256, 4, 2, 48) == 0
     assert lib.moe_backward_workspace_bytes(4, 100, 256, 4, 2, 16) == 0
     n = lib.moe_backward_workspace_bytes(4, 128, 256, 4, 2, 0)
     assert n > 0 and n == lib.moe_backward_workspace_bytes(4, 128, 256, 4, 2, 16)   # 2 rows per expert
