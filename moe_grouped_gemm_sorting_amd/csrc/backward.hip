@@ -146,24 +146,25 @@ __global__ __launch_bounds__(256) void k_gather_bwd(const int32_t *__restrict__ 
 // C[e] [M, N] = sum over the slots of expert e's segment of P[slot]^T Q[slot]
 // (P = P_hi + P_lo and Q bf16, [slots, M] and [slots, N], in slot order;
 // rows past the expert's count are padding and contribute zeros).
-// Workgroup: a 128 x 128 tile of C, 4 waves of 64 x 64 (2 x 2 accumulators
+// Workgroup: a 128 x 256 tile of C, 4 waves of 64 x 128 (2 x 4 accumulators
 // of v_mfma_f32_32x32x16_bf16). The segment is walked 32 rows at a time.
-// Thread t loads rows 4 (t % 8) .. + 3 and columns 4 (t / 8) .. + 3 of a
-// chunk of each operand (8-byte row pieces) and stores them transposed
-// into LDS, [column][row] with 4 rows per 8-byte store, so that an MFMA
-// operand (8 consecutive K = rows of one column) is one 16-byte LDS read.
-// LDS rows are 80 bytes apart: the 16-byte operand reads of 16 lanes then
-// cover all 64 banks once, and the 8-byte stores of 32 lanes (row offset
-// fastest) are conflict-free. Slot-ordered operands make every load address
-// affine in the row, so with NST = 2 LDS stages the loads run 3 chunks ahead
-// in registers (the chunk stored at step c was loaded at step c - 2) and a
-// chunk's store overlaps the previous chunk's MFMAs. NST = 1 (half the LDS,
-// for short segments) loads, stores and multiplies one chunk at a time.
+// Thread t loads rows 4 (t % 8) .. + 3 of a chunk, P columns 4 (t / 8) ..
+// + 3 and Q columns 8 (t / 8) .. + 7 (8- and 16-byte row pieces), and stores
+// them transposed into LDS, [column][row] with 4 rows per 8-byte store, so
+// that an MFMA operand (8 consecutive K = rows of one column) is one 16-byte
+// LDS read. LDS rows are 80 bytes apart: the 16-byte operand reads of 16
+// lanes then cover all 64 banks once, and the 8-byte P stores of 32 lanes
+// (row offset fastest) are conflict-free (Q stores: 2-way). Slot-ordered
+// operands make every load address affine in the row, so with NST = 2 LDS
+// stages the loads run a chunk ahead in registers and a chunk's store
+// overlaps the previous chunk's MFMAs. NST = 1 (half the LDS, for short
+// segments) loads, stores and multiplies one chunk at a time.
 // P is an fp32 value (a routing weight times dy, or dg / du), which its
 // producer stores as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi); it
 // enters as two MFMAs: about 16 mantissa bits, against 8 for a plain bf16
 // operand (split once there rather than once per column tile of C here). Q
 // (x or h) is exactly bf16.
+
 // Workgroup barrier for LDS hand-over only: this wave's LDS operations
 // complete, then s_barrier. A __syncthreads() also waits for every
 // outstanding global load (its release fence), which would drain the
@@ -174,11 +175,20 @@ __device__ __forceinline__ void lds_barrier() {
 
 constexpr int WG_ROWS = 32;
 constexpr int WG_PITCH = WG_ROWS + 8;   // bf16 per LDS row: 80 bytes
-constexpr int WG_RD = 3;                // chunks in flight in registers
+#ifndef MOE_WG_QCOLS
+#define MOE_WG_QCOLS 256
+#endif
+// Q columns (C columns) per workgroup: 256, or 128 (measured 1.75x slower at
+// the prefill shape: more LDS fragment reads and global loads per MFMA)
+constexpr int WG_QC = MOE_WG_QCOLS;
+constexpr int WG_QW = WG_QC / 32;       // ... per loading thread
+constexpr int WG_NB = WG_QC / 64;       // 32-column accumulator tiles per wave
+constexpr int WG_RD = WG_QC == 128 ? 3 : 2;   // chunks in flight in registers
 
 struct WgChunk {
-    uint32_t v[3][4][2];   // [P_hi, P_lo, Q][row][column pair]
-    int nreal;             // real rows among the thread's 4 (a prefix)
+    uint32_t p[2][4][2];          // [P_hi, P_lo][row][column pair]
+    uint32_t q[4][WG_QW / 2];     // [row][column pair]
+    int nreal;                    // real rows among the thread's 4 (a prefix)
 };
 
 template <int NST>
@@ -188,31 +198,33 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t *__restrict__ p_hi
                                                const int32_t *__restrict__ offsets,
                                                const int32_t *__restrict__ counts,
                                                float *__restrict__ C) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[NST][3][128][WG_PITCH];  // [stage][hi, lo, q]
+    __shared__ __attribute__((aligned(16))) uint16_t lp[NST][2][128][WG_PITCH];   // [stage][hi, lo]
+    __shared__ __attribute__((aligned(16))) uint16_t lq[NST][WG_QC][WG_PITCH];
     const int e = blockIdx.z;
-    const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 128;
+    const int m0 = blockIdx.y * 128, n0 = blockIdx.x * WG_QC;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int beg = offsets[e];
     const int real_end = beg + counts[e];
     // chunks over the real rows (an empty expert has none)
     const int nch = (real_end - beg + WG_ROWS - 1) / WG_ROWS;
-    // loader: rows lr0 .. lr0 + 3 of a chunk, tile columns lc0 .. lc0 + 3
-    const int lr0 = 4 * (tid & 7), lc0 = 4 * (tid >> 3);
-    const bool pm_ok = m0 + lc0 < M, qn_ok = n0 + lc0 < N;   // M, N multiples of 4
+    // loader: rows lr0 .. lr0 + 3 of a chunk, P columns lc0 .. lc0 + 3 and
+    // Q columns lq0 .. lq0 + WG_QW - 1 of the tile
+    const int lr0 = 4 * (tid & 7), lc0 = 4 * (tid >> 3), lq0 = WG_QW * (tid >> 3);
+    const bool pm_ok = m0 + lc0 < M, qn_ok = n0 + lq0 < N;   // M, N multiples of 4 / WG_QW
 
-    f32x16 acc[2][2];
+    f32x16 acc[2][WG_NB];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < WG_NB; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
     // Every load is issued (no divergent branch, whose join would make the
     // compiler wait for it at once): rows past real_end read the last real
     // row and columns past M / N read column 0; the store zeroes them.
-    const size_t pcol = pm_ok ? (size_t)(m0 + lc0) : 0, qcol = qn_ok ? (size_t)(n0 + lc0) : 0;
+    const size_t pcol = pm_ok ? (size_t)(m0 + lc0) : 0, qcol = qn_ok ? (size_t)(n0 + lq0) : 0;
     auto load = [&](WgChunk &ch, int c) {
         const int r0 = beg + c * WG_ROWS + lr0;
         ch.nreal = max(0, min(4, real_end - r0));
@@ -221,32 +233,47 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t *__restrict__ p_hi
             const size_t r = (size_t)min(r0 + i, real_end - 1);
             const uint2 h = *reinterpret_cast<const uint2 *>(p_hi + r * M + pcol);
             const uint2 l = *reinterpret_cast<const uint2 *>(p_lo + r * M + pcol);
-            const uint2 u = *reinterpret_cast<const uint2 *>(q + r * N + qcol);
-            ch.v[0][i][0] = h.x; ch.v[0][i][1] = h.y;
-            ch.v[1][i][0] = l.x; ch.v[1][i][1] = l.y;
-            ch.v[2][i][0] = u.x; ch.v[2][i][1] = u.y;
+            ch.p[0][i][0] = h.x; ch.p[0][i][1] = h.y;
+            ch.p[1][i][0] = l.x; ch.p[1][i][1] = l.y;
+            if constexpr (WG_QW == 4) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(q + r * N + qcol);
+                ch.q[i][0] = u.x; ch.q[i][1] = u.y;
+            } else {
+                const uint4 u = *reinterpret_cast<const uint4 *>(q + r * N + qcol);
+                ch.q[i][0] = u.x; ch.q[i][1] = u.y; ch.q[i][2] = u.z; ch.q[i][3] = u.w;
+            }
         }
     };
-    // column j of the thread's 4: rows lr0 .. lr0 + 3 as one 8-byte store
+    // column j of the thread's: rows lr0 .. lr0 + 3 as one 8-byte store
     // per operand (v_perm picks 16-bit halves; selector bytes 0-3 index the
     // second operand)
     auto store = [&](const WgChunk &ch, int st) {
 #pragma unroll
-        for (int o = 0; o < 3; ++o) {
-            const bool ok = o < 2 ? pm_ok : qn_ok;
-            uint32_t vv[4][2];
+        for (int o = 0; o < 2; ++o) {
+            uint32_t vv[4][WG_QW / 2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vv[i][0] = (ok && i < ch.nreal) ? ch.v[o][i][0] : 0u;
-                vv[i][1] = (ok && i < ch.nreal) ? ch.v[o][i][1] : 0u;
-            }
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int w = 0; w < 2; ++w) vv[i][w] = (pm_ok && i < ch.nreal) ? ch.p[o][i][w] : 0u;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
                 const uint32_t r01 = __builtin_amdgcn_perm(vv[1][j >> 1], vv[0][j >> 1], sel);
                 const uint32_t r23 = __builtin_amdgcn_perm(vv[3][j >> 1], vv[2][j >> 1], sel);
-                *reinterpret_cast<uint2 *>(&lds[st][o][lc0 + j][lr0]) = make_uint2(r01, r23);
+                *reinterpret_cast<uint2 *>(&lp[st][o][lc0 + j][lr0]) = make_uint2(r01, r23);
             }
+        }
+        uint32_t vq[4][WG_QW / 2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int w = 0; w < WG_QW / 2; ++w) vq[i][w] = (qn_ok && i < ch.nreal) ? ch.q[i][w] : 0u;
+#pragma unroll
+        for (int j = 0; j < WG_QW; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t r01 = __builtin_amdgcn_perm(vq[1][j >> 1], vq[0][j >> 1], sel);
+            const uint32_t r23 = __builtin_amdgcn_perm(vq[3][j >> 1], vq[2][j >> 1], sel);
+            *reinterpret_cast<uint2 *>(&lq[st][lq0 + j][lr0]) = make_uint2(r01, r23);
         }
     };
     // two K = 16 sub-steps over the chunk's 32 rows; lane half lane / 32
@@ -255,20 +282,20 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t *__restrict__ p_hi
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int kr = 16 * sub + 8 * (lane >> 5);
-            u32x4 ah[2], al[2], bq[2];
+            u32x4 ah[2], al[2], bq[WG_NB];
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
                 const int col = 64 * wm + 32 * a + (lane & 31);
-                ah[a] = *reinterpret_cast<const u32x4 *>(&lds[st][0][col][kr]);
-                al[a] = *reinterpret_cast<const u32x4 *>(&lds[st][1][col][kr]);
+                ah[a] = *reinterpret_cast<const u32x4 *>(&lp[st][0][col][kr]);
+                al[a] = *reinterpret_cast<const u32x4 *>(&lp[st][1][col][kr]);
             }
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-                bq[b] = *reinterpret_cast<const u32x4 *>(&lds[st][2][64 * wn + 32 * b + (lane & 31)][kr]);
+            for (int b = 0; b < WG_NB; ++b)
+                bq[b] = *reinterpret_cast<const u32x4 *>(&lq[st][(WG_QC / 2) * wn + 32 * b + (lane & 31)][kr]);
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int b = 0; b < WG_NB; ++b) {
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[a]),
                                                                         __builtin_bit_cast(bf16x8, bq[b]),
                                                                         acc[a][b], 0, 0, 0);
@@ -313,8 +340,8 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t *__restrict__ p_hi
     // 32x32 accumulator: lane holds column (lane & 31), rows 8 (v / 4) + 4 (lane / 32) + (v & 3)
     float *dst = C + (size_t)e * M * N;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int n = n0 + 64 * wn + 32 * b + (lane & 31);
+    for (int b = 0; b < WG_NB; ++b) {
+        const int n = n0 + (WG_QC / 2) * wn + 32 * b + (lane & 31);
         if (n >= N) continue;
 #pragma unroll
         for (int a = 0; a < 2; ++a)
@@ -359,8 +386,8 @@ hipError_t launch_wgrad(const uint16_t *p_hi, const uint16_t *p_lo, const uint16
                         const int32_t *offsets, const int32_t *counts, bool short_segments, float *C,
                         hipStream_t s) {
     if (E == 0) return hipSuccess;
-    if (M % 4 || N % 4) return hipErrorInvalidValue;
-    const dim3 grid((N + 127) / 128, (M + 127) / 128, E);
+    if (M % 4 || N % WG_QW) return hipErrorInvalidValue;
+    const dim3 grid((N + WG_QC - 1) / WG_QC, (M + 127) / 128, E);
     if (short_segments)
         k_wgrad<1><<<grid, 256, 0, s>>>(p_hi, p_lo, q, M, N, offsets, counts, C);
     else
