@@ -334,3 +334,83 @@ def moe_backward(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w
     if rc != 0:
         raise ValueError(f"oracle_moe_backward failed ({rc})")
     return dx, dw13, dw2, dtw
+
+
+def moe_backward_sampled(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
+                         dy_bf16: np.ndarray, dx_tokens=(), dw13_at=(), dw2_at=(), dtw_at=(),
+                         chunk: int = 2048):
+    """Selected entries of the gradients :func:`moe_backward` defines, each
+    computed on its own in float64 from the chain rule (for full-size layers,
+    where the whole backward is out of reach on a CPU):
+
+      g = Wg x, u = Wu x, h = bf16(silu(g) u)   (per assignment a = t k + j),
+      v = Wd^T dy[t], dh = w v, dg = dh u silu'(g), du = dh silu(g),
+      dx[t] = sum_j Wg^T dg + Wu^T du,  dtopk_w[a] = <v, h>,
+      dW2[e][m, n] = sum over a of expert e of w dy[t, m] h[n],
+      dW13[e][n, c] = sum over a of expert e of (dg or du)[n] x[t, c].
+
+    dx_tokens: tokens whose dx rows to return; dtw_at: flat assignments;
+    dw13_at / dw2_at: (e, row, column) triples. w13 / w2: per-expert bf16
+    bits [2f, d] / [d, f]. Returns (dx [len, d], dw13 [len], dw2 [len],
+    dtw [len]) as float64."""
+    x = bf16_bits_to_f32(np.asarray(x_bf16)).astype(np.float64)
+    dy = bf16_bits_to_f32(np.asarray(dy_bf16)).astype(np.float64)
+    ids = np.asarray(topk_ids)
+    wts = np.asarray(topk_w, dtype=np.float64)
+    T, d = x.shape
+    k = ids.shape[1]
+    f = next(a for a in w13 if a is not None).shape[0] // 2
+
+    def f64(b):
+        return bf16_bits_to_f32(np.asarray(b)).astype(np.float64)
+
+    def silu(z):
+        return z / (1.0 + np.exp(-z))
+
+    def silu_grad(z):
+        s = 1.0 / (1.0 + np.exp(-z))
+        return s * (1.0 + z * (1.0 - s))
+
+    def bf16_round(v):
+        return f64(f32_to_bf16_bits(v.astype(np.float32)))
+
+    def columns(a, ns):
+        """g, u, h, v, dg, du of assignment a at the columns ns of f."""
+        t, e, w = a // k, int(ids.flat[a]), float(wts.flat[a])
+        ns = np.asarray(ns)
+        g = f64(w13[e][ns]) @ x[t]
+        u = f64(w13[e][f + ns]) @ x[t]
+        h = bf16_round(silu(g) * u)
+        v = dy[t] @ f64(w2[e][:, ns])
+        dh = w * v
+        return g, u, h, v, dh * u * silu_grad(g), dh * silu(g)
+
+    def all_columns(a):
+        parts = [columns(a, np.arange(s, min(f, s + chunk))) for s in range(0, f, chunk)]
+        return [np.concatenate([p[i] for p in parts]) for i in range(6)]
+
+    dx = np.zeros((len(dx_tokens), d))
+    for i, t in enumerate(dx_tokens):
+        for j in range(k):
+            a = t * k + j
+            e = int(ids.flat[a])
+            _, _, _, _, dg, du = all_columns(a)
+            for s in range(0, f, chunk):
+                sl = slice(s, min(f, s + chunk))
+                dx[i] += dg[sl] @ f64(w13[e][sl]) + du[sl] @ f64(w13[e][f + sl.start:f + sl.stop])
+    dtw = np.zeros(len(dtw_at))
+    for i, a in enumerate(dtw_at):
+        _, _, h, v, _, _ = all_columns(a)
+        dtw[i] = v @ h
+    dw2 = np.zeros(len(dw2_at))
+    for i, (e, m, n) in enumerate(dw2_at):
+        for a in np.flatnonzero(ids.ravel() == e):
+            _, _, h, _, _, _ = columns(a, [n])
+            dw2[i] += wts.flat[a] * dy[a // k, m] * h[0]
+    dw13 = np.zeros(len(dw13_at))
+    for i, (e, r, c) in enumerate(dw13_at):
+        n = r % f
+        for a in np.flatnonzero(ids.ravel() == e):
+            _, _, _, _, dg, du = columns(a, [n])
+            dw13[i] += (dg[0] if r < f else du[0]) * x[a // k, c]
+    return dx, dw13, dw2, dtw

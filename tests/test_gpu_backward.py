@@ -85,3 +85,37 @@ def test_backward_rejects_tiled_blocks_on_unsupported_shapes():
     with pytest.raises(moe.MoeError):
         moe.moe_backward(x, ws["w13"], ws["w2"], x, torch.from_numpy(ids).to(DEV),
                          torch.from_numpy(w).to(DEV), B=64)
+
+
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill"])
+def test_backward_full_size_sampled(name):
+    """The Mixtral-shaped layers at full size (the decode shape on the
+    streaming path, the prefill shape on the tiled path, each with the
+    library's block size) against the oracle's per-entry backward on sampled
+    entries: two dx rows, four routing-weight gradients, twelve entries each
+    of dW13 (gate and up rows) and dW2 in experts that tokens select."""
+    wl = workloads.get(name)
+    log(f"full-size backward: {name} (generating inputs)")
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    ids, w = oracle.route(logits.cpu().numpy(), wl.k, wl.score)
+    g = torch.Generator(device=DEV).manual_seed(wl.seed + 7)
+    dy = torch.randn(wl.T, wl.d, generator=g, device=DEV).bfloat16()
+    dx, dw13, dw2, dtw = moe.moe_backward(x, ws["w13"], ws["w2"], dy, torch.from_numpy(ids).to(DEV),
+                                          torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    used = np.unique(ids)
+    tokens = [0, wl.T - 1]
+    asg = rng.choice(wl.T * wl.k, 4, replace=False).tolist()
+    at13 = [(int(rng.choice(used)), int(rng.integers(2 * wl.f)), int(rng.integers(wl.d))) for _ in range(12)]
+    at2 = [(int(rng.choice(used)), int(rng.integers(wl.d)), int(rng.integers(wl.f))) for _ in range(12)]
+    w13 = [bits(ws["w13"][e]) for e in range(wl.E)]
+    w2 = [bits(ws["w2"][e]) for e in range(wl.E)]
+    log("  oracle on the sampled entries")
+    s_dx, s13, s2, stw = oracle.moe_backward_sampled(bits(x), ids, w, w13, w2, bits(dy), dx_tokens=tokens,
+                                                     dw13_at=at13, dw2_at=at2, dtw_at=asg)
+    _check("dx", bf16_to_f64(bits(dx))[tokens], s_dx)
+    _check("dw13", np.array([dw13[e, r, c].item() for e, r, c in at13]), s13)
+    _check("dw2", np.array([dw2[e, m, n].item() for e, m, n in at2]), s2)
+    _check("dtopk_w", dtw.cpu().numpy().ravel()[asg], stw)

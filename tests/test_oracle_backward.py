@@ -94,3 +94,28 @@ def test_backward_does_not_depend_on_the_thread_count():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[3], b[3])
     for e in range(4):
         assert np.array_equal(a[1][e], b[1][e]) and np.array_equal(a[2][e], b[2][e])
+
+
+def test_sampled_backward_matches_the_whole_backward():
+    """moe_backward_sampled (per-entry, float64) against moe_backward (whole
+    layer, fp32) on a small routed layer: same chain rule, same bf16 h."""
+    rng = np.random.default_rng(11)
+    T, d, f, E, k = 12, 64, 96, 4, 2
+    x = oracle.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32)).reshape(T, d)
+    dy = oracle.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32)).reshape(T, d)
+    w13 = [oracle.f32_to_bf16_bits((rng.standard_normal((2 * f, d)) * d ** -0.5).astype(np.float32))
+           .reshape(2 * f, d) for _ in range(E)]
+    w2 = [oracle.f32_to_bf16_bits((rng.standard_normal((d, f)) * f ** -0.5).astype(np.float32))
+          .reshape(d, f) for _ in range(E)]
+    ids, w = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    rdx, r13, r2, rtw = oracle.moe_backward(x, ids, w, w13, w2, dy)
+    used = sorted(set(ids.ravel().tolist()))
+    at13 = [(e, r, c) for e in used for r, c in ((0, 0), (f - 1, d - 1), (f, 3), (2 * f - 1, 17))]
+    at2 = [(e, m, n) for e in used for m, n in ((0, 0), (d - 1, f - 1), (5, 40))]
+    s_dx, s13, s2, stw = oracle.moe_backward_sampled(x, ids, w, w13, w2, dy, dx_tokens=[0, 5, T - 1],
+                                                     dw13_at=at13, dw2_at=at2,
+                                                     dtw_at=list(range(T * k)), chunk=40)
+    np.testing.assert_allclose(s_dx, rdx[[0, 5, T - 1]], rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(s13, [r13[e][r, c] for e, r, c in at13], rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(s2, [r2[e][m, n] for e, m, n in at2], rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(stw, rtw.ravel(), rtol=1e-4, atol=1e-5)
