@@ -348,7 +348,9 @@ def moe_backward_workspace_bytes(T, d, f, E, k, B=0) -> int:
 def moe_backward(x, w13, w2, dy, topk_ids, topk_w, B: int = 0, workspace=None):
     """Gradients of the bf16 layer for the output gradient dy and the routing
     the forward used. Returns (dx bf16 [T, d], dw13 fp32 [E, 2f, d],
-    dw2 fp32 [E, d, f], dtopk_w fp32 [T, k])."""
+    dw2 fp32 [E, d, f], dtopk_w fp32 [T, k]). B: 16 or 32 (streaming
+    kernels), 64, 128 or 256 (tiled kernels; d and f multiples of 256), or
+    0 for the library's choice."""
     lib = load_library()
     dev = x.device
     _need(x, "x", (torch.bfloat16,), dev)
