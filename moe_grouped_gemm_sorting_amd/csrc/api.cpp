@@ -710,7 +710,11 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
         HIP_TRY(launch_bwd_swiglu(w.gu, w.v, w.sorted_ids, w.sorted_w, (int)max_padded(T, k, E, B), T, k, f,
                                   w.h, w.dgu, w.dgu_lo, dtopk_w, s),
                 "backward SwiGLU launch");
-        HIP_TRY(launch_tiled_gemm2(g2, 0, 0, 1, s), "backward GEMM launch");
+        // K = 2f split so that there are about four tiles per CU (fp32 atomics into acc)
+        const int64_t tiles = max_blocks(T, k, E, B) * (int64_t)(d / tiled_tile_cols(B, 0, false, 0, 0));
+        const int cu = cu_count_cached();
+        const int ks = (int)std::min<int64_t>(4, std::max<int64_t>(1, (4 * (int64_t)cu + tiles - 1) / tiles));
+        HIP_TRY(launch_tiled_gemm2(g2, 0, 0, ks, s), "backward GEMM launch");
     } else {
         HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
         // dg, du and the routing-weight gradients from v = Wd^T dy
