@@ -127,8 +127,8 @@ def backward_block(T, d, f, E, k):
     """The library's default sort block for the backward (streaming kernels
     for few rows per expert, tiled kernels from 64 rows per expert on)."""
     rows = T * k / E
-    if rows >= 64 and d % 256 == 0 and f % 256 == 0:
-        return 256 if rows >= 256 else (128 if rows >= 128 else 64)
+    if rows >= 2 and d % 256 == 0 and f % 256 == 0:
+        return 256 if rows >= 192 else (128 if rows >= 48 else 64)
     return 16 if rows <= 4 else 32
 
 

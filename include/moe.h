@@ -242,7 +242,7 @@ int moe_select_config(int T, int d, int f, int E, int k, int quant, int cu_count
  * sorted assignment list. bf16 only. B = 16 or 32 runs the GEMMs on the
  * streaming kernels; B = 64, 128 or 256 on the tiled kernels (d and f
  * multiples of 256, else MOE_ERR_UNSUPPORTED); B = 0 lets the library choose
- * (tiled from 64 assignments per expert on average).
+ * (tiled from 2 assignments per expert on average where d and f allow).
  * Layouts and ownership as in fused_moe; every output is overwritten. */
 size_t moe_backward_workspace_bytes(int T, int d, int f, int E, int k, int B);
 int moe_backward(int T, int d, int f, int E, int k, int B, const void *x,

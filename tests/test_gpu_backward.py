@@ -87,22 +87,23 @@ def test_backward_rejects_tiled_blocks_on_unsupported_shapes():
                          torch.from_numpy(w).to(DEV), B=64)
 
 
-@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill"])
-def test_backward_full_size_sampled(name):
+@pytest.mark.parametrize("name,B", [("mixtral_decode", 32), ("mixtral_decode", 0), ("mixtral_prefill", 0)])
+def test_backward_full_size_sampled(name, B):
     """The Mixtral-shaped layers at full size (the decode shape on the
-    streaming path, the prefill shape on the tiled path, each with the
-    library's block size) against the oracle's per-entry backward on sampled
-    entries: two dx rows, four routing-weight gradients, twelve entries each
-    of dW13 (gate and up rows) and dW2 in experts that tokens select."""
+    streaming path with 32-row blocks and on the library's choice, the tiled
+    path; the prefill shape on the tiled path) against the oracle's per-entry
+    backward on sampled entries: two dx rows, four routing-weight gradients,
+    twelve entries each of dW13 (gate and up rows) and dW2 in experts that
+    tokens select."""
     wl = workloads.get(name)
-    log(f"full-size backward: {name} (generating inputs)")
+    log(f"full-size backward: {name} B={B} (generating inputs)")
     x, logits = wl.activations(DEV)
     ws = wl.weights(DEV)
     ids, w = oracle.route(logits.cpu().numpy(), wl.k, wl.score)
     g = torch.Generator(device=DEV).manual_seed(wl.seed + 7)
     dy = torch.randn(wl.T, wl.d, generator=g, device=DEV).bfloat16()
     dx, dw13, dw2, dtw = moe.moe_backward(x, ws["w13"], ws["w2"], dy, torch.from_numpy(ids).to(DEV),
-                                          torch.from_numpy(w).to(DEV))
+                                          torch.from_numpy(w).to(DEV), B=B)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     used = np.unique(ids)
