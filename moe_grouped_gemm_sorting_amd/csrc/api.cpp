@@ -734,10 +734,17 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
                               static_cast<const uint16_t *>(dy), w.xs, w.dz_hi, w.dz_lo, s),
             "gather launch");
     const bool short_seg = (int64_t)T * k <= 256;
-    HIP_TRY(launch_wgrad(w.dz_hi, w.dz_lo, w.h, d, f, E, w.offsets, w.counts, short_seg, dw2, s),
-            "weight-gradient launch");
-    HIP_TRY(launch_wgrad(w.dgu, w.dgu_lo, w.xs, 2 * f, d, E, w.offsets, w.counts, short_seg, dw13, s),
-            "weight-gradient launch");
+    if (B >= 64 && !short_seg && d % 256 == 0 && f % 256 == 0) {
+        HIP_TRY(launch_wgrad_dma(w.dz_hi, w.dz_lo, w.h, d, f, E, w.offsets, dw2, s),
+                "weight-gradient launch");
+        HIP_TRY(launch_wgrad_dma(w.dgu, w.dgu_lo, w.xs, 2 * f, d, E, w.offsets, dw13, s),
+                "weight-gradient launch");
+    } else {
+        HIP_TRY(launch_wgrad(w.dz_hi, w.dz_lo, w.h, d, f, E, w.offsets, w.counts, short_seg, dw2, s),
+                "weight-gradient launch");
+        HIP_TRY(launch_wgrad(w.dgu, w.dgu_lo, w.xs, 2 * f, d, E, w.offsets, w.counts, short_seg, dw13, s),
+                "weight-gradient launch");
+    }
     return MOE_OK;
 }
 

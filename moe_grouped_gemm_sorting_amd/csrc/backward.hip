@@ -48,9 +48,20 @@ __global__ __launch_bounds__(256) void k_bwd_swiglu(const float *__restrict__ gu
     __shared__ float red[4];
     const int slot = blockIdx.x;
     const int a = sorted_ids[slot];
-    if (a >= T * k) return;
-    const float w = sorted_w[slot];
     const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+    if (a >= T * k) {   // padding slot: zero rows (the weight gradients read them)
+        if (c < f) {
+            const size_t o = (size_t)slot * 2 * f + c;
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(h + (size_t)slot * f + c) = z;
+            *reinterpret_cast<uint4 *>(dgu + o) = z;
+            *reinterpret_cast<uint4 *>(dgu + o + f) = z;
+            *reinterpret_cast<uint4 *>(dgu_lo + o) = z;
+            *reinterpret_cast<uint4 *>(dgu_lo + o + f) = z;
+        }
+        return;
+    }
+    const float w = sorted_w[slot];
     float part = 0.0f;
     if (c < f) {
         const size_t f2 = 2 * (size_t)f;
@@ -358,6 +369,176 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint16_t *__restrict__ p_hi
 hipError_t launch_transpose_bf16(const uint16_t *in, int E, int R, int C, uint16_t *out, hipStream_t s) {
     if (E == 0 || R % 64 || C % 64) return E == 0 ? hipSuccess : hipErrorInvalidValue;
     k_transpose_bf16<<<dim3(C / 64, R / 64, E), 256, 0, s>>>(in, R, C, out);
+    return hipGetLastError();
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void wg_dma16(const void *base, uint32_t off, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void wg_wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t wg_lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t *)p;
+}
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// The weight gradients for long segments of whole 32-row chunks whose
+// padding rows are zero (the tiled path's producers zero them): the same sum
+// as k_wgrad, with the slot rows moved into LDS by DMA as they lie in memory
+// (no VGPR round trip, no transposing stores) and the MFMA operands read
+// with the transposing LDS read ds_read_tr16_b64. Within a 16-lane group,
+// lane i of that read receives element i % 4 of the 8-byte chunks that lanes
+// 4j + i / 4 address (j = 0..3): with lane 4j + q pointing at row k0 + j and
+// columns c0 + 4q .. + 3, lane i gets rows k0 .. k0 + 3 of column c0 + i, and
+// two such reads give the 8 consecutive K values of a v_mfma_f32_16x16x32_bf16
+// operand. Tile 128 x 256, waves of 64 x 128 as 4 x 8 accumulators; three
+// 32 KB stages (P_hi, P_lo [32][128], Q [32][256] bf16), the 16-byte chunk c
+// of row r stored at position c ^ 2 (r % 4), so that a transposing read's
+// 16 lanes (4 rows x 2 chunks) meet 8 distinct chunk positions and no bank
+// twice. The DMA wait counts are written out as in the tiled GEMMs.
+constexpr int WD_NBUF = 3;
+constexpr int WD_PB = 32 * 256;           // bytes of one P plane per stage
+constexpr int WD_QB = 32 * 512;
+constexpr int WD_STAGE = 2 * WD_PB + WD_QB;   // 32 KB
+
+__global__ __launch_bounds__(256) void k_wgrad_dma(const uint16_t *__restrict__ p_hi,
+                                                   const uint16_t *__restrict__ p_lo,
+                                                   const uint16_t *__restrict__ q, int M, int N,
+                                                   const int32_t *__restrict__ offsets,
+                                                   float *__restrict__ C) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[WD_NBUF * WD_STAGE];
+    const int e = blockIdx.z;
+    const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 256;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int beg = offsets[e];
+    const int nch = (offsets[e + 1] - beg) / 32;   // segments are whole 64-row blocks
+    // DMA: instruction i of wave w fills 1 KB (64 chunks) of the stage:
+    // P planes 8 KB each (instructions 0..7 hi, 8..15 lo), Q 16 KB (16..31);
+    // wave w issues instructions w, w + 4, ..., (8 per wave)
+    uint32_t goff[8];
+    const uint16_t *gbase[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int ins = wave + 4 * t;
+        int plane, L;
+        if (ins < 16) { plane = ins < 8 ? 0 : 1; L = (ins % 8) * 64 + lane; }
+        else { plane = 2; L = (ins - 16) * 64 + lane; }
+        const int cpr = plane < 2 ? 16 : 32;
+        const int r = L / cpr, pos = L % cpr;
+        const int c = pos ^ ((r & 3) << 1);
+        if (plane < 2) {
+            gbase[t] = plane == 0 ? p_hi : p_lo;
+            goff[t] = (uint32_t)(r * M * 2 + m0 * 2 + c * 16);
+        } else {
+            gbase[t] = q;
+            goff[t] = (uint32_t)(r * N * 2 + n0 * 2 + c * 16);
+        }
+    }
+    const uint32_t lds0 = wg_lds_addr(lds);
+    auto issue = [&](int buf, int ch) {
+        ch = min(ch, nch - 1);
+        const size_t row0 = (size_t)beg + (size_t)ch * 32;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int ins = wave + 4 * t;
+            const size_t rowbytes = ins < 16 ? (size_t)M * 2 : (size_t)N * 2;
+            const uint8_t *b = reinterpret_cast<const uint8_t *>(gbase[t]) + row0 * rowbytes;
+            wg_dma16(b, goff[t], lds0 + (uint32_t)(buf * WD_STAGE + ins * 1024));
+        }
+    };
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // transposing read of 8 consecutive K rows (k = 8 g .. 8 g + 7, g = lane / 16) of column
+    // c0 + lane % 16 of a plane with rows of rb bytes
+    const int li = lane & 15, g = lane >> 4;
+    const int tj = li >> 2, tq = li & 3;
+    auto frag = [&](uint32_t plane_base, int rb, int c0) -> u32x4 {
+        u32x4 out;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int r = 8 * g + 4 * hh + tj;
+            const int col = c0 + 4 * tq;
+            const int chunk = (col >> 3) ^ ((r & 3) << 1);
+            const uint32_t addr = plane_base + (uint32_t)(r * rb + chunk * 16 + (col & 7) * 2);
+            const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)addr);
+            out[2 * hh] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+            out[2 * hh + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+        }
+        return out;
+    };
+    auto compute = [&](int buf) {
+        const uint32_t sb = lds0 + (uint32_t)(buf * WD_STAGE);
+        u32x4 bq[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) bq[b] = frag(sb + 2 * WD_PB, 512, 128 * wn + 16 * b);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const u32x4 ah = frag(sb, 256, 64 * wm + 16 * a);
+            const u32x4 al = frag(sb + WD_PB, 256, 64 * wm + 16 * a);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah),
+                                                                    __builtin_bit_cast(bf16x8, bq[b]),
+                                                                    acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al),
+                                                                    __builtin_bit_cast(bf16x8, bq[b]),
+                                                                    acc[a][b], 0, 0, 0);
+            }
+        }
+    };
+    if (nch > 0) {
+#pragma unroll
+        for (int b = 0; b < WD_NBUF - 1; ++b) issue(b, b);
+        wg_wait_vmem<8 * (WD_NBUF - 2)>();
+        __builtin_amdgcn_s_barrier();
+        for (int c0 = 0; c0 < nch; c0 += WD_NBUF) {
+            static_for<WD_NBUF>([&](auto ic) {
+                constexpr int r = decltype(ic)::value;
+                const int c = c0 + r;
+                if (c < nch) {
+                    issue((r + WD_NBUF - 1) % WD_NBUF, c + WD_NBUF - 1);
+                    compute(r);
+                    wg_wait_vmem<8 * (WD_NBUF - 2)>();
+                    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                }
+            });
+        }
+        wg_wait_vmem<0>();
+    }
+    // 16x16 accumulator: lane holds column lane % 16, rows 4 (lane / 16) + v
+    float *dst = C + (size_t)e * M * N;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int n = n0 + 128 * wn + 16 * b + li;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + 64 * wm + 16 * a + 4 * g + v;
+                if (m < M && n < N) dst[(size_t)m * N + n] = acc[a][b][v];
+            }
+        }
+}
+
+hipError_t launch_wgrad_dma(const uint16_t *p_hi, const uint16_t *p_lo, const uint16_t *q, int M, int N, int E,
+                            const int32_t *offsets, float *C, hipStream_t s) {
+    if (E == 0) return hipSuccess;
+    if (M % 128 || N % 256) return hipErrorInvalidValue;
+    k_wgrad_dma<<<dim3(N / 256, M / 128, E), 256, 0, s>>>(p_hi, p_lo, q, M, N, offsets, C);
     return hipGetLastError();
 }
 

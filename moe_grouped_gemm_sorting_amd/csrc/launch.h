@@ -99,6 +99,11 @@ hipError_t launch_bwd_swiglu(const float *gu, const float *v, const int32_t *sor
                              uint16_t *dgu_lo, float *dtw, hipStream_t s);
 // Backward: xs[slot] = x[t] and w[slot] dy[t] as two bf16 parts dz_hi + dz_lo
 // (zeros for padding slots; P slots).
+// The same for segments of whole 32-row chunks whose padding rows are zero
+// (the tiled path): operands by LDS DMA and transposing LDS reads. M a
+// multiple of 128, N of 256.
+hipError_t launch_wgrad_dma(const uint16_t *p_hi, const uint16_t *p_lo, const uint16_t *q, int M, int N, int E,
+                            const int32_t *offsets, float *C, hipStream_t s);
 hipError_t launch_gather_bwd(const int32_t *sorted_ids, const float *sorted_w, int P, int T, int k,
                              int d, const uint16_t *x, const uint16_t *dy, uint16_t *xs, uint16_t *dz_hi,
                              uint16_t *dz_lo, hipStream_t s);
