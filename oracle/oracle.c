@@ -405,6 +405,49 @@ static float weight2(const expert_view *v, int row, int col)
     return code * s;
 }
 
+/* Row `row` of an expert matrix with `cols` columns as fp32 operand values:
+ * the same value weight13 / weight2 give for each element (bf16 converted
+ * exactly; e4m3 code value times its fp32 scale; E2M1 code value times
+ * 2^(c - 127)), taken once per row so that a dot product reads a plain
+ * array. e4m3_tab / fp4_tab hold oracle_e4m3_decode / oracle_fp4_decode of
+ * every code. For an MXFP4
+ * block with c in [0, 254] the product of the code value and the fp32 2^e
+ * is exact (at most 3 significant bits, no underflow below 2^-149) or
+ * overflows to infinity, as the double-precision ldexp of mx_elem does once
+ * converted to fp32; the E8M0 NaN code 255 goes through mx_elem itself. */
+static void weight_row(const void *w, const void *s, int quant, int cols, int row,
+                       const float *e4m3_tab, const float *fp4_tab, float *out)
+{
+    const size_t base = (size_t)row * cols;
+    if (quant == 0) {
+        for (int c = 0; c < cols; ++c)
+            out[c] = bf16_bits_to_f32(((const uint16_t *)w)[base + c]);
+    } else if (quant == 3) {
+        const uint8_t *sc = (const uint8_t *)s + (size_t)row * (cols / 32);
+        for (int b = 0; b < cols / 32; ++b) {
+            const int e = (int)sc[b] - 127;
+            if (e > 127) {
+                for (int c = 32 * b; c < 32 * b + 32; ++c)
+                    out[c] = mx_elem(w, s, cols, row, c);
+                continue;
+            }
+            const float p2 = (float)ldexp(1.0, e);
+            for (int c = 32 * b; c < 32 * b + 32; ++c) {
+                uint8_t byte = ((const uint8_t *)w)[base / 2 + c / 2];
+                uint8_t q = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+                out[c] = fp4_tab[q] * p2;
+            }
+        }
+    } else {
+        const float *sc = (const float *)s;
+        const uint8_t *q = (const uint8_t *)w + base;
+        for (int c = 0; c < cols; ++c) {
+            const float scale = (quant == 1) ? sc[row] : sc[(size_t)(row / 128) * (cols / 128) + c / 128];
+            out[c] = e4m3_tab[q[c]] * scale;
+        }
+    }
+}
+
 /* Replace v[0..n) by its quantise-dequantise image: one group (quant 1),
  * groups of 128 (quant 2) or MXFP4 blocks of 32 (quant 3). */
 static void fake_quant(float *v, int n, int quant)
@@ -449,6 +492,11 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
                 return -1;
         }
     }
+    float e4m3_tab[256], fp4_tab[16];
+    for (int c = 0; c < 256; ++c)
+        e4m3_tab[c] = oracle_e4m3_decode((uint8_t)c);
+    for (int c = 0; c < 16; ++c)
+        fp4_tab[c] = oracle_fp4_decode((uint8_t)c);
     int bad = 0;
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -459,10 +507,13 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
         const int t = tokens[i];
         float *xt = (float *)malloc(sizeof(float) * (size_t)d);
         float *h = (float *)malloc(sizeof(float) * (size_t)f);
+        /* one weight row at a time: gate row, up row (d each), down row (f) */
+        float *wrow = (float *)malloc(sizeof(float) * (size_t)(2 * d + f));
         float *yt = y + (size_t)i * d;
-        if (!xt || !h) {
+        if (!xt || !h || !wrow) {
             free(xt);
             free(h);
+            free(wrow);
             bad |= 1;
             continue;
         }
@@ -475,13 +526,15 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
         for (int j = 0; j < k; ++j) {
             const int e = topk_ids[(size_t)t * k + j];
             const float w = topk_w[(size_t)t * k + j];
-            expert_view v = {d, f, quant, w13[e], w2[e],
-                             quant ? w13_scale[e] : NULL, quant ? w2_scale[e] : NULL};
+            const void *s13 = quant ? w13_scale[e] : NULL, *s2 = quant ? w2_scale[e] : NULL;
+            float *wg = wrow, *wu = wrow + d, *wd = wrow + 2 * d;
             for (int n = 0; n < f; ++n) {
+                weight_row(w13[e], s13, quant, d, n, e4m3_tab, fp4_tab, wg);
+                weight_row(w13[e], s13, quant, d, f + n, e4m3_tab, fp4_tab, wu);
                 float g = 0.0f, u = 0.0f;
                 for (int c = 0; c < d; ++c) {
-                    g += xt[c] * weight13(&v, n, c);
-                    u += xt[c] * weight13(&v, f + n, c);
+                    g += xt[c] * wg[c];
+                    u += xt[c] * wu[c];
                 }
                 float hn = silu(g) * u;
                 h[n] = h_exact ? hn : round_to_bf16(hn);
@@ -489,9 +542,10 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
             if (quant && !h_exact)
                 fake_quant(h, f, quant);
             for (int m = 0; m < d; ++m) {
+                weight_row(w2[e], s2, quant, f, m, e4m3_tab, fp4_tab, wd);
                 float z = 0.0f;
                 for (int n = 0; n < f; ++n)
-                    z += h[n] * weight2(&v, m, n);
+                    z += h[n] * wd[n];
                 yt[m] += w * z;
             }
         }
@@ -499,6 +553,7 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
             out[(size_t)i * d + m] = oracle_f32_to_bf16(yt[m]);
         free(xt);
         free(h);
+        free(wrow);
     }
     return bad ? -2 : 0;
 }
