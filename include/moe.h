@@ -31,7 +31,8 @@
  *  - Arguments are validated on the host before any HIP call. Device-side
  *    preconditions (not checked): expert ids in [0, E) where the caller
  *    supplies them, and finite inputs. Ids outside [0, E) are skipped by the
- *    sort and never reach an out-of-bounds address.
+ *    sort: they reach no out-of-bounds address, and the assignments that
+ *    carry them add nothing to the layer's output.
  *  - Return value: MOE_OK, or an error code. Nothing aborts and nothing is
  *    thrown. moe_last_error() gives this thread's last error text.
  *  - Calls on one stream are ordered. Calls that share output or workspace
@@ -54,8 +55,10 @@
  *    4, 6 and negatives), two codes per byte with the even element in the
  *    low nibble, and one E8M0 scale byte (2^(c - 127)) per 32 consecutive
  *    elements along the reduction dimension. Activations and h are
- *    quantised at run time as moe_quant_act_mx describes. Runs on the
- *    streaming kernels (B = 16 or 32); d and f must be multiples of 256.
+ *    quantised at run time as moe_quant_act_mx describes. d and f must be
+ *    multiples of 256; sort blocks of 16 or 32 rows run on the
+ *    weight-streaming kernels, blocks of 64, 128 or 256 rows on the
+ *    LDS-tiled kernels, which need d and f multiples of 512.
  *  - Weights are laid out with the reduction dimension contiguous:
  *      w13 [E, 2f, d]: rows 0..f-1 are the gate projection, rows f..2f-1
  *                      the up projection;

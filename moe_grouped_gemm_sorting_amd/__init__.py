@@ -12,6 +12,7 @@ import ctypes
 import os
 import warnings
 
+import numpy as np
 import torch
 
 __all__ = [
@@ -121,6 +122,46 @@ def _need(t, name, dtypes, device=None):
     return t
 
 
+def _shape(t, name, shape):
+    """Raise unless tensor t (if given) has exactly `shape`."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _weight_scale_shapes(quant, E, d, f):
+    """Expected shapes of (w13_scale, w2_scale) for a quant type (None for bf16)."""
+    if quant == "fp8_token":
+        return (E, 2 * f), (E, d)
+    if quant == "fp8_block":
+        return (E, 2 * f // 128, d // 128), (E, d // 128, f // 128)
+    if quant == "mxfp4":
+        return (E, 2 * f, d // 32), (E, d, f // 32)
+    return None, None
+
+
+def _h_shapes(quant, P, f):
+    """Shapes of (h, h_scale) in the format moe_gemm1_swiglu writes."""
+    if quant == "bf16":
+        return (P, f), None
+    if quant == "fp8_token":
+        return (P, f), (P,)
+    if quant == "fp8_block":
+        return (P, f), (P, f // 128)
+    return (P, f // 2), (P, f // 32)
+
+
+def _check_sort(sort, T, k, E, B):
+    """The sort buffers must have the sizes the library assumes for (T, k, E, B)."""
+    P, NB = moe_sort_max_padded(T, k, E, B), moe_sort_max_blocks(T, k, E, B)
+    if P < 0:
+        raise ValueError(f"bad sort shape T={T} k={k} E={E} B={B}")
+    _shape(sort["sorted_ids"], "sorted_ids", (P,))
+    _shape(sort["sorted_w"], "sorted_w", (P,))
+    _shape(sort["sorted_expert_ids"], "sorted_expert_ids", (NB,))
+    _shape(sort["num_valid"], "num_valid", (1,))
+    return P
+
+
 _W8 = (torch.uint8, torch.float8_e4m3fn)
 
 
@@ -161,6 +202,8 @@ def moe_topk(logits: torch.Tensor, k: int, score: str = "softmax", renorm: bool 
     """Top-k routing of fp32 logits [T, E]; returns (topk_ids int32, topk_w fp32), [T, k]."""
     lib = load_library()
     _need(logits, "logits", (torch.float32,))
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [T, E], got shape {tuple(logits.shape)}")
     T, E = logits.shape
     ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
     w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
@@ -175,6 +218,9 @@ def moe_sort(topk_ids: torch.Tensor, topk_w: torch.Tensor, E: int, B: int) -> di
     lib = load_library()
     _need(topk_ids, "topk_ids", (torch.int32,))
     _need(topk_w, "topk_w", (torch.float32,), topk_ids.device)
+    if topk_ids.dim() != 2:
+        raise ValueError(f"topk_ids must be [T, k], got shape {tuple(topk_ids.shape)}")
+    _shape(topk_w, "topk_w", topk_ids.shape)
     T, k = topk_ids.shape
     P, NB = moe_sort_max_padded(T, k, E, B), moe_sort_max_blocks(T, k, E, B)
     if P < 0:
@@ -197,6 +243,8 @@ def moe_quant_act(x: torch.Tensor, group: int):
     """Dynamic e4m3 quantisation of bf16 x [rows, cols]; returns (codes uint8, scales fp32)."""
     lib = load_library()
     _need(x, "x", (torch.bfloat16,))
+    if x.dim() != 2 or group < 1 or x.shape[1] % group:
+        raise ValueError(f"x must be [rows, cols] with cols a multiple of group={group}")
     rows, cols = x.shape
     codes = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
     scales = torch.empty(rows, cols // group, dtype=torch.float32, device=x.device)
@@ -209,6 +257,8 @@ def moe_quant_act_mx(x: torch.Tensor):
     [rows, cols/2], two per byte, E8M0 scales uint8 [rows, cols/32])."""
     lib = load_library()
     _need(x, "x", (torch.bfloat16,))
+    if x.dim() != 2 or x.shape[1] % 32:
+        raise ValueError(f"x must be [rows, cols] with cols a multiple of 32, got {tuple(x.shape)}")
     rows, cols = x.shape
     codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device)
     scales = torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device)
@@ -227,12 +277,15 @@ def moe_gemm1_swiglu(x, w13, sort: dict, k: int, B: int, quant: str = "bf16", w1
     codes [P, f/2] + E8M0 scales [P, f/32])."""
     lib = load_library()
     _need(x, "x", (torch.bfloat16,))
+    _need(w13, "w13", _wdtypes(quant), x.device)
+    if x.dim() != 2 or w13.dim() != 3:
+        raise ValueError("x must be [T, d] and w13 [E, 2f, d]")
     E, f2, dk = w13.shape
     f = f2 // 2
-    d = dk * _pk(quant)
-    _need(w13, "w13", _wdtypes(quant), x.device)
-    T = x.shape[0]
-    P = sort["sorted_ids"].numel()
+    T, d = x.shape
+    _shape(w13, "w13", (E, 2 * f, d // _pk(quant)))
+    P = _check_sort(sort, T, k, E, B)
+    _shape(w13_scale, "w13_scale", _weight_scale_shapes(quant, E, d, f)[0])
     dev = x.device
     q = QUANT[quant]
     if q == 0:
@@ -265,17 +318,28 @@ def moe_gemm2_combine(h, h_scale, w2, sort: dict, T: int, k: int, B: int, quant:
                       w2_scale=None, ksplit: int = 0, out=None, workspace=None):
     """Stage 2: grouped down GEMM + routing-weighted combine; returns out bf16 [T, d]."""
     lib = load_library()
+    _need(w2, "w2", _wdtypes(quant))
+    if w2.dim() != 3:
+        raise ValueError("w2 must be [E, d, f]")
     E, d, fk = w2.shape
     f = fk * _pk(quant)
     dev = w2.device
-    _need(w2, "w2", _wdtypes(quant))
     q = QUANT[quant]
     _need(h, "h", (torch.bfloat16,) if q == 0 else _wdtypes(quant), dev)
     if q:
         _need(w2_scale, "w2_scale", _sdtypes(quant), dev)
         _need(h_scale, "h_scale", _sdtypes(quant), dev)
+    P = _check_sort(sort, T, k, E, B)
+    hs, hss = _h_shapes(quant, P, f)
+    _shape(h, "h", hs)
+    if h_scale is not None and hss is not None and h_scale.numel() != int(np.prod(hss)):
+        raise ValueError(f"h_scale has {h_scale.numel()} elements, expected {int(np.prod(hss))}")
+    _shape(w2_scale, "w2_scale", _weight_scale_shapes(quant, E, d, f)[1])
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", (torch.bfloat16,), dev)
+        _shape(out, "out", (T, d))
     nbytes = moe_gemm2_workspace_bytes(T, d, f, E, k, B, quant)
     ws = _workspace(nbytes, dev, workspace)
     _check(lib.moe_gemm2_combine(T, d, f, E, k, B, q, ksplit, _ptr(h), _ptr(h_scale), _ptr(w2),
@@ -297,22 +361,36 @@ def fused_moe(x, w13, w2, k: int, logits=None, topk_ids=None, topk_w=None, quant
     lib = load_library()
     _need(x, "x", (torch.bfloat16,))
     dev = x.device
-    T, d = x.shape
-    E, f2, _ = w13.shape
-    f = f2 // 2
     q = QUANT[quant]
     _need(w13, "w13", _wdtypes(quant), dev)
     _need(w2, "w2", _wdtypes(quant), dev)
+    if x.dim() != 2 or w13.dim() != 3:
+        raise ValueError("x must be [T, d] and w13 [E, 2f, d]")
+    T, d = x.shape
+    E, f2, _ = w13.shape
+    f = f2 // 2
+    pk = _pk(quant)
+    _shape(w13, "w13", (E, 2 * f, d // pk))
+    _shape(w2, "w2", (E, d, f // pk))
     if logits is not None:
         _need(logits, "logits", (torch.float32,), dev)
+        _shape(logits, "logits", (T, E))
     else:
         _need(topk_ids, "topk_ids", (torch.int32,), dev)
         _need(topk_w, "topk_w", (torch.float32,), dev)
+        _shape(topk_ids, "topk_ids", (T, k))
+        _shape(topk_w, "topk_w", (T, k))
     if q:
         _need(w13_scale, "w13_scale", _sdtypes(quant), dev)
         _need(w2_scale, "w2_scale", _sdtypes(quant), dev)
+        s13, s2 = _weight_scale_shapes(quant, E, d, f)
+        _shape(w13_scale, "w13_scale", s13)
+        _shape(w2_scale, "w2_scale", s2)
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", (torch.bfloat16,), dev)
+        _shape(out, "out", (T, d))
     nbytes = fused_moe_workspace_bytes(T, d, f, E, k, quant, B, stage)
     if nbytes == 0:
         _check(lib.fused_moe(T, d, f, E, k, q, SCORE[score], int(renorm), *([None] * 8), B, stage,
@@ -359,10 +437,17 @@ def moe_backward(x, w13, w2, dy, topk_ids, topk_w, B: int = 0, workspace=None):
     _need(w2, "w2", (torch.bfloat16,), dev)
     _need(topk_ids, "topk_ids", (torch.int32,), dev)
     _need(topk_w, "topk_w", (torch.float32,), dev)
+    if x.dim() != 2 or w13.dim() != 3 or topk_ids.dim() != 2:
+        raise ValueError("x must be [T, d], w13 [E, 2f, d] and topk_ids [T, k]")
     T, d = x.shape
     E, f2, _ = w13.shape
     f = f2 // 2
     k = topk_ids.shape[1]
+    _shape(w13, "w13", (E, 2 * f, d))
+    _shape(w2, "w2", (E, d, f))
+    _shape(dy, "dy", (T, d))
+    _shape(topk_ids, "topk_ids", (T, k))
+    _shape(topk_w, "topk_w", (T, k))
     dx = torch.empty(T, d, device=dev, dtype=torch.bfloat16)
     dw13 = torch.empty(E, 2 * f, d, device=dev, dtype=torch.float32)
     dw2 = torch.empty(E, d, f, device=dev, dtype=torch.float32)

@@ -335,9 +335,18 @@ constexpr int STORED_SPLITS = 2;
 
 // GEMM2's fp32 buffer: the token accumulator [T, d], or, for the tiled
 // kernel, the weighted rows by K part and assignment [STORED_SPLITS][T*k, d]
-// (the larger of the two, so that one layout serves both).
-float *carve_gemm2(Carver &c, int T, int d, int k, int B) {
-    return c.take<float>((size_t)T * d * (use_tiled(B) ? (size_t)k * STORED_SPLITS : 1));
+// (the larger of the two, so that one layout serves both), then, for the
+// tiled kernel, the marks of the assignments the sort placed [T*k].
+struct Gemm2Ws {
+    float *acc = nullptr;
+    int32_t *written = nullptr;
+};
+
+Gemm2Ws carve_gemm2(Carver &c, int T, int d, int k, int B) {
+    Gemm2Ws w;
+    w.acc = c.take<float>((size_t)T * d * (use_tiled(B) ? (size_t)k * STORED_SPLITS : 1));
+    if (use_tiled(B)) w.written = c.take<int32_t>((size_t)T * k);
+    return w;
 }
 
 // The tiled down projection split into at most STORED_SPLITS parts of K
@@ -346,11 +355,15 @@ float *carve_gemm2(Carver &c, int T, int d, int k, int B) {
 // summation order.
 bool stored_rows(int B, int ksplit) { return use_tiled(B) && ksplit <= STORED_SPLITS; }
 
+// ids_valid: every assignment is in sorted_ids (routing ran inside the
+// library); otherwise the stored-row combine first marks the assignments the
+// sort placed, so that dropped ones (ids outside [0, E)) add nothing.
 int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, const void *h,
               const void *h_scale_v, const void *w2, const void *w2_scale_v,
               const int32_t *sorted_ids, const float *sorted_w, const int32_t *seid,
-              const int32_t *num_valid, void *out, float *acc, hipStream_t s,
+              const int32_t *num_valid, void *out, const Gemm2Ws &ws2, bool ids_valid, hipStream_t s,
               bool acc_zeroed = false) {
+    float *acc = ws2.acc;
     Gemm2Args g{};
     g.sh = GemmShape{T, d, f, E, k, B, quant};
     g.h = h;
@@ -375,9 +388,13 @@ int run_gemm2(int T, int d, int f, int E, int k, int B, int quant, int ksplit, c
     if (stored_rows(B, ksplit)) {
         g.acc = nullptr;
         g.yrows = acc;
+        if (!ids_valid)
+            HIP_TRY(launch_mark_written(sorted_ids, num_valid, (int)max_padded(T, k, E, B), T * k,
+                                        ws2.written, s),
+                    "mark launch");
         HIP_TRY(launch_tiled_gemm2(g, MOE_G2_BM, MOE_G2_TN, ksplit, s), "GEMM2 launch");
         HIP_TRY(launch_combine_rows(acc, T, k, tiled_gemm2_parts(f, quant, ksplit), d,
-                                    static_cast<uint16_t *>(out), s),
+                                    ids_valid ? nullptr : ws2.written, static_cast<uint16_t *>(out), s),
                 "combine launch");
         return MOE_OK;
     }
@@ -399,7 +416,7 @@ struct FusedWs {
     void *h = nullptr;
     void *h_scale = nullptr;   // fp32 (e4m3) or E8M0 bytes (MXFP4)
     Gemm1Ws g1;
-    float *acc = nullptr;
+    Gemm2Ws g2;
 };
 
 FusedWs carve_fused(Carver &c, int T, int d, int f, int E, int k, int quant, int B, bool route) {
@@ -420,7 +437,7 @@ FusedWs carve_fused(Carver &c, int T, int d, int f, int E, int k, int quant, int
     if (quant == 2) w.h_scale = c.take<float>(P * (f / 128));
     if (quant == MOE_QUANT_MXFP4) w.h_scale = c.take<uint8_t>(P * (f / 32));
     w.g1 = carve_gemm1(c, T, d, f, E, k, B, quant);
-    w.acc = carve_gemm2(c, T, d, k, B);
+    w.g2 = carve_gemm2(c, T, d, k, B);
     return w;
 }
 
@@ -561,9 +578,9 @@ int moe_gemm2_combine(int T, int d, int f, int E, int k, int B, int quant, int k
         return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, c.bytes());
     if (T == 0) return MOE_OK;
     Carver cw(ws);
-    float *acc = carve_gemm2(cw, T, d, k, B);
+    const Gemm2Ws w2s = carve_gemm2(cw, T, d, k, B);
     return run_gemm2(T, d, f, E, k, B, quant, ksplit, h, h_scale, w2, w2_scale, sorted_ids,
-                     sorted_w, sorted_expert_ids, num_valid, out, acc, (hipStream_t)stream);
+                     sorted_w, sorted_expert_ids, num_valid, out, w2s, false, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------- backward
@@ -880,6 +897,7 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     // the one-stage path needs a cleared accumulator before its kernel; the
     // routing+sort workgroup clears small ones on the way
     const size_t acc_n = (size_t)T * d;
+    float *const acc = w.g2.acc;
     // Routing runs inside the sort's single workgroup for small T * E (one
     // launch less); beyond that the one-wave-per-token routing kernel plus the
     // sort is faster (whole layer, MI355X: T=128, E=256 1692 -> 1595 us;
@@ -889,7 +907,7 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     if (logits && fuse_route) {
         HIP_TRY(launch_route_sort(logits, T, k, E, B, score, renorm, w.topk_ids, w.topk_w,
                                   w.sorted_ids, w.sorted_w, w.seid, w.counts, w.offsets,
-                                  w.num_valid, s, zero_in_sort ? w.acc : nullptr,
+                                  w.num_valid, s, zero_in_sort ? acc : nullptr,
                                   zero_in_sort ? (int)acc_n : 0),
                 "route+sort launch");
     } else if (logits) {
@@ -903,11 +921,11 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
                 "sort launch");
     }
     if (stage == 1) {
-        if (!zero_in_sort) HIP_TRY(launch_fill_f32(w.acc, acc_n, 0.0f, s), "fill launch");
+        if (!zero_in_sort) HIP_TRY(launch_fill_f32(acc, acc_n, 0.0f, s), "fill launch");
         HIP_TRY(launch_moe_1stage(GemmShape{T, d, f, E, k, B, quant}, x, w13, w2, w.sorted_ids,
-                                  w.sorted_w, w.seid, w.acc, s),
+                                  w.sorted_w, w.seid, acc, s),
                 "one-stage launch");
-        HIP_TRY(launch_finalize(w.acc, static_cast<uint16_t *>(out), acc_n, s), "finalize launch");
+        HIP_TRY(launch_finalize(acc, static_cast<uint16_t *>(out), acc_n, s), "finalize launch");
         return MOE_OK;
     }
     // GEMM1 also clears GEMM2's accumulator (same stream, so it is done first)
@@ -915,10 +933,10 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     if (ksplit <= 0) ksplit = pick_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
     const bool clear = !stored_rows(B, ksplit);
     rc = run_gemm1(T, d, f, E, k, B, quant, x, w13, w13_scale, w.sorted_ids, w.seid, w.num_valid,
-                   w.h, w.h_scale, w.g1, s, clear ? w.acc : nullptr, clear ? (size_t)T * d : 0);
+                   w.h, w.h_scale, w.g1, s, clear ? acc : nullptr, clear ? (size_t)T * d : 0);
     if (rc) return rc;
     return run_gemm2(T, d, f, E, k, B, quant, ksplit, w.h, w.h_scale, w2, w2_scale, w.sorted_ids,
-                     w.sorted_w, w.seid, w.num_valid, out, w.acc, s, true);
+                     w.sorted_w, w.seid, w.num_valid, out, w.g2, logits != nullptr, s, true);
 }
 
 }  // extern "C"

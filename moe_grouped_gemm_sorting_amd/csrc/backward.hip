@@ -38,8 +38,10 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t *__restri
 // dg = dh u silu'(g), du = dh silu(g), each stored as two bf16 parts
 // (dgu = bf16(x), dgu_lo = bf16(x - dgu), [P, 2f]), and the routing-weight
 // gradient dtw[a] += sum over the row of v h (one atomic per workgroup).
-// Workgroup: 2048 columns of one slot, 8 per thread; padding slots are
-// skipped (nothing reads their rows).
+// Workgroup: 2048 columns of one slot, 8 per thread. Padding slots get
+// zero rows of h, dgu and dgu_lo: the DMA weight-gradient kernel sums whole
+// 32-row chunks of each expert's segment, padding rows included, and
+// depends on those rows being zero.
 __global__ __launch_bounds__(256) void k_bwd_swiglu(const float *__restrict__ gu, const float *__restrict__ v,
                                                     const int32_t *__restrict__ sorted_ids,
                                                     const float *__restrict__ sorted_w, int T, int k, int f,

@@ -40,9 +40,15 @@ hipError_t launch_fill_f32(float *p, size_t n, float v, hipStream_t s);
 // acc fp32 [n] -> bf16 [n]
 hipError_t launch_finalize(const float *acc, uint16_t *out, size_t n, hipStream_t s);
 
-// out[t, :] = bf16(sum over j < k of rows[t*k + j, :]) (j ascending), rows fp32 [T*k, d]
-hipError_t launch_combine_rows(const float *rows, int T, int k, int parts, int d, uint16_t *out,
-                               hipStream_t s);
+// out[t, :] = bf16(sum over j < k of rows[t*k + j, :]) (j ascending), rows fp32
+// [parts][T*k, d]; written (optional, [T*k]) marks the rows GEMM2 stored: an
+// unmarked row counts as zero
+hipError_t launch_combine_rows(const float *rows, int T, int k, int parts, int d,
+                               const int32_t *written, uint16_t *out, hipStream_t s);
+// written[a] = 1 for the assignments in sorted_ids[0, num_valid), 0 for the
+// others (the ones the sort dropped); n_asg = T*k
+hipError_t launch_mark_written(const int32_t *sorted_ids, const int32_t *num_valid, int P, int n_asg,
+                               int32_t *written, hipStream_t s);
 
 struct GemmShape {
     int T, d, f, E, k, B, quant;
@@ -97,13 +103,16 @@ hipError_t launch_transpose_bf16(const uint16_t *in, int E, int R, int C, uint16
 hipError_t launch_bwd_swiglu(const float *gu, const float *v, const int32_t *sorted_ids,
                              const float *sorted_w, int P, int T, int k, int f, uint16_t *h, uint16_t *dgu,
                              uint16_t *dgu_lo, float *dtw, hipStream_t s);
-// Backward: xs[slot] = x[t] and w[slot] dy[t] as two bf16 parts dz_hi + dz_lo
-// (zeros for padding slots; P slots).
-// The same for segments of whole 32-row chunks whose padding rows are zero
-// (the tiled path): operands by LDS DMA and transposing LDS reads. M a
-// multiple of 128, N of 256.
+// Weight gradient per expert as launch_wgrad below, for segments of whole
+// 32-row chunks (the tiled path): operands by LDS DMA and transposing LDS
+// reads. M a multiple of 128, N of 256. Precondition: every padding row of
+// p_hi, p_lo and q inside an expert's padded segment [offsets[e],
+// offsets[e+1]) is zero (k_bwd_swiglu and k_gather_bwd write those zeros),
+// because whole chunks are summed, padding rows included.
 hipError_t launch_wgrad_dma(const uint16_t *p_hi, const uint16_t *p_lo, const uint16_t *q, int M, int N, int E,
                             const int32_t *offsets, float *C, hipStream_t s);
+// Backward: xs[slot] = x[t] and w[slot] dy[t] as two bf16 parts dz_hi + dz_lo
+// (zeros for padding slots; P slots).
 hipError_t launch_gather_bwd(const int32_t *sorted_ids, const float *sorted_w, int P, int T, int k,
                              int d, const uint16_t *x, const uint16_t *dy, uint16_t *xs, uint16_t *dz_hi,
                              uint16_t *dz_lo, hipStream_t s);

@@ -6,6 +6,8 @@
 // s = amax / 448 over the group (s = 1 when amax = 0), q = e4m3(v / s) with
 // round-to-nearest-even and saturation. Both divisions are IEEE
 // correctly rounded.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -206,9 +208,13 @@ hipError_t launch_finalize(const float *acc, uint16_t *out, size_t n, hipStream_
 // ascending j and rounded once to bf16. d is a multiple of 4.
 // rows: `parts` slabs of [T*k, d] (one per part of a split reduction); a
 // token's sum takes its rows in ascending j and, within a row, the parts in
-// ascending order.
+// ascending order. written (optional, [T*k]): nonzero for the assignments
+// the sort placed; rows of the others were never written and count as zero
+// (NULL: every assignment was placed).
 __global__ __launch_bounds__(256) void k_combine_rows(const float *__restrict__ rows, int T, int k,
-                                                      int parts, int d, uint16_t *__restrict__ out) {
+                                                      int parts, int d,
+                                                      const int32_t *__restrict__ written,
+                                                      uint16_t *__restrict__ out) {
     const int d4 = d / 4;
     const size_t n4 = (size_t)T * d4;
     const size_t slab4 = (size_t)T * k * d4;
@@ -218,11 +224,17 @@ __global__ __launch_bounds__(256) void k_combine_rows(const float *__restrict__ 
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
         const size_t t = i / d4, c = i - t * d4;
         const float4 *src = r4 + t * k * d4 + c;
-        float4 v = src[0];
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        bool first = true;
         for (int j = 0; j < k; ++j) {
+            if (written && !written[t * k + j]) continue;
             for (int q = 0; q < parts; ++q) {
-                if (j == 0 && q == 0) continue;
                 const float4 u = src[(size_t)q * slab4 + (size_t)j * d4];
+                if (first) {
+                    v = u;
+                    first = false;
+                    continue;
+                }
                 v.x += u.x;
                 v.y += u.y;
                 v.z += u.z;
@@ -234,13 +246,39 @@ __global__ __launch_bounds__(256) void k_combine_rows(const float *__restrict__ 
     }
 }
 
-hipError_t launch_combine_rows(const float *rows, int T, int k, int parts, int d, uint16_t *out,
-                               hipStream_t s) {
+hipError_t launch_combine_rows(const float *rows, int T, int k, int parts, int d,
+                               const int32_t *written, uint16_t *out, hipStream_t s) {
     const size_t n4 = (size_t)T * (d / 4);
     if (n4 == 0) return hipSuccess;
     size_t blocks = (n4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    k_combine_rows<<<(unsigned)blocks, 256, 0, s>>>(rows, T, k, parts, d, out);
+    k_combine_rows<<<(unsigned)blocks, 256, 0, s>>>(rows, T, k, parts, d, written, out);
+    return hipGetLastError();
+}
+
+// written[a] = 1 for every assignment a in sorted_ids[0, num_valid) (the
+// array is cleared first by the caller).
+__global__ __launch_bounds__(256) void k_mark_written(const int32_t *__restrict__ sorted_ids,
+                                                      const int32_t *__restrict__ num_valid, int n_asg,
+                                                      int32_t *__restrict__ written) {
+    const int nv = *num_valid;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < nv; i += gridDim.x * 256) {
+        const int a = sorted_ids[i];
+        if (a >= 0 && a < n_asg) written[a] = 1;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_clear_i32(int32_t *__restrict__ p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+hipError_t launch_mark_written(const int32_t *sorted_ids, const int32_t *num_valid, int P, int n_asg,
+                               int32_t *written, hipStream_t s) {
+    if (n_asg == 0) return hipSuccess;
+    const unsigned bc = (unsigned)std::min(1024, (n_asg + 255) / 256);
+    k_clear_i32<<<bc, 256, 0, s>>>(written, n_asg);
+    const unsigned bm = (unsigned)std::min(1024, (P + 255) / 256);
+    k_mark_written<<<bm, 256, 0, s>>>(sorted_ids, num_valid, n_asg, written);
     return hipGetLastError();
 }
 

@@ -21,7 +21,9 @@ passage it follows:
   per_Token and per_1x128 named in the AITER article, sections 1.1 and 3.2).
 * :func:`moe_backward` -- the gradients of the bf16 layer (the training
   step named as the next milestone: rocketrecap.com/entries/19116, 10:07),
-  from the chain rule of :func:`moe`.
+  from the chain rule of :func:`moe`; :func:`moe_backward_sampled` and
+  :func:`moe_backward_expert` give selected entries and blocks of the same
+  gradients in float64 for full-size layers.
 * :func:`fp4_encode` / :func:`fp4_decode` / :func:`mx_quant_rows` -- MXFP4,
   the quant type per_1x32 (same article, sections 1.1, 2.2 and 3.2;
   rocketrecap.com/entries/19188 glossary "MXFP4"), with the element format,
@@ -414,3 +416,86 @@ def moe_backward_sampled(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.nd
             _, _, _, _, dg, du = columns(a, [n])
             dw13[i] += (dg[0] if r < f else du[0]) * x[a // k, c]
     return dx, dw13, dw2, dtw
+
+
+def moe_backward_expert(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, e: int,
+                        w13_e, w2_e, dy_bf16: np.ndarray, rows13=(), cols13=(), rows2=(), cols2=(),
+                        full_asg=(), chunk: int = 2048):
+    """The gradients of :func:`moe_backward` that expert e contributes, in
+    float64 from the same chain rule, taken over all of e's assignments a
+    (ascending) at once with matrix products (for full-size layers):
+
+      g = x Wg^T, u = x Wu^T, h = bf16(silu(g) u), v = dy Wd, dh = w v,
+      dg = dh u silu'(g), du = dh silu(g)           (one row per assignment),
+      dW13[e][r, c] = sum_a (dg if r < f else du)[a, r mod f] x[t_a, c],
+      dW2[e][m, n] = sum_a w_a dy[t_a, m] h[a, n],
+
+    and, for the assignments listed in full_asg (all of expert e), the
+    routing-weight gradient <v, h> over all f and the assignment's share
+    Wg^T dg + Wu^T du of dx[t_a].
+
+    rows13 / cols13 (rows of [2f], columns of [d]) and rows2 / cols2 (rows
+    of [d], columns of [f]) select the weight-gradient blocks. w13_e / w2_e:
+    expert e's bf16 bits [2f, d] / [d, f]. Returns (dW13 block, dW2 block,
+    {a: dtopk_w[a]}, {a: dx share [d]})."""
+    x = bf16_bits_to_f32(np.asarray(x_bf16)).astype(np.float64)
+    dy = bf16_bits_to_f32(np.asarray(dy_bf16)).astype(np.float64)
+    ids = np.asarray(topk_ids)
+    wts = np.asarray(topk_w, dtype=np.float64)
+    k = ids.shape[1]
+    f = np.asarray(w13_e).shape[0] // 2
+    asg = np.flatnonzero(ids.ravel() == e)
+    tok = asg // k
+    wa = wts.ravel()[asg]
+
+    def f64(b):
+        return bf16_bits_to_f32(np.asarray(b)).astype(np.float64)
+
+    def silu(z):
+        return z / (1.0 + np.exp(-z))
+
+    def silu_grad(z):
+        s = 1.0 / (1.0 + np.exp(-z))
+        return s * (1.0 + z * (1.0 - s))
+
+    def bf16_round(v):
+        return f64(f32_to_bf16_bits(v.astype(np.float32))).reshape(v.shape)
+
+    def at_columns(sel, ns):
+        """g, u, h, v, dg, du of the assignments asg[sel] at the columns ns of f."""
+        ns = np.asarray(ns, dtype=np.int64)
+        xs = x[tok[sel]]
+        g = xs @ f64(np.asarray(w13_e)[ns]).T
+        u = xs @ f64(np.asarray(w13_e)[f + ns]).T
+        h = bf16_round(silu(g) * u)
+        v = dy[tok[sel]] @ f64(np.asarray(w2_e)[:, ns])
+        dh = wa[sel, None] * v
+        return g, u, h, v, dh * u * silu_grad(g), dh * silu(g)
+
+    every = np.arange(asg.size)
+    rows13, cols13 = np.asarray(rows13, np.int64), np.asarray(cols13, np.int64)
+    dw13 = np.zeros((rows13.size, cols13.size))
+    if rows13.size and cols13.size and asg.size:
+        _, _, _, _, dg, du = at_columns(every, rows13 % f)
+        lhs = np.where((rows13 < f)[None, :], dg, du)          # [assignments, rows13]
+        dw13 = lhs.T @ x[tok][:, cols13]
+    rows2, cols2 = np.asarray(rows2, np.int64), np.asarray(cols2, np.int64)
+    dw2 = np.zeros((rows2.size, cols2.size))
+    if rows2.size and cols2.size and asg.size:
+        _, _, h, _, _, _ = at_columns(every, cols2)
+        dw2 = (wa[:, None] * dy[tok][:, rows2]).T @ h
+    dtw, dx = {}, {}
+    sel = np.array([int(np.flatnonzero(asg == a)[0]) for a in full_asg], dtype=np.int64)
+    if sel.size:
+        d = x.shape[1]
+        vh = np.zeros(sel.size)
+        share = np.zeros((sel.size, d))
+        for s0 in range(0, f, chunk):
+            ns = np.arange(s0, min(f, s0 + chunk))
+            _, _, h, v, dg, du = at_columns(sel, ns)
+            vh += np.sum(v * h, axis=1)
+            share += dg @ f64(np.asarray(w13_e)[ns]) + du @ f64(np.asarray(w13_e)[f + ns])
+        for i, a in enumerate(full_asg):
+            dtw[int(a)] = float(vh[i])
+            dx[int(a)] = share[i]
+    return dw13, dw2, dtw, dx

@@ -41,15 +41,19 @@ TILED_SHAPES = [
 ]
 
 
-def _run_and_check(wl, B):
+def _run_and_check(wl, B, nan_workspace=False):
     x, logits = wl.activations(DEV)
     ws = wl.weights(DEV)
     ids, w = oracle.route(logits.cpu().numpy(), wl.k, wl.score)
     g = torch.Generator(device=DEV).manual_seed(wl.seed + 7)
     dy = torch.randn(wl.T, wl.d, generator=g, device=DEV).bfloat16()
-    log(f"backward {wl.name} B={B}")
+    log(f"backward {wl.name} B={B} nan_workspace={nan_workspace}")
+    work = None
+    if nan_workspace:
+        nbytes = moe.moe_backward_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, B)
+        work = torch.full((nbytes // 4 + 1,), float("nan"), device=DEV).view(torch.uint8)
     dx, dw13, dw2, dtw = moe.moe_backward(x, ws["w13"], ws["w2"], dy, torch.from_numpy(ids).to(DEV),
-                                          torch.from_numpy(w).to(DEV), B=B)
+                                          torch.from_numpy(w).to(DEV), B=B, workspace=work)
     torch.cuda.synchronize()
     w13 = [bits(ws["w13"][e]) for e in range(wl.E)]
     w2 = [bits(ws["w2"][e]) for e in range(wl.E)]
@@ -73,7 +77,12 @@ def test_backward_matches_the_oracle(wl, B):
 @pytest.mark.parametrize("wl", TILED_SHAPES, ids=lambda w: w.name)
 @pytest.mark.parametrize("B", [0, 64, 128, 256])
 def test_backward_tiled_matches_the_oracle(wl, B):
-    _run_and_check(wl, B)
+    """The tiled path with its workspace filled with NaN first: the
+    weight-gradient kernel sums whole 32-row chunks of each expert's segment,
+    padding rows included, so it relies on the producers writing zeros into
+    the padding rows of its operands; a padding row left unwritten would
+    carry NaN into dW."""
+    _run_and_check(wl, B, nan_workspace=True)
 
 
 def test_backward_rejects_tiled_blocks_on_unsupported_shapes():
@@ -88,13 +97,14 @@ def test_backward_rejects_tiled_blocks_on_unsupported_shapes():
 
 
 @pytest.mark.parametrize("name,B", [("mixtral_decode", 32), ("mixtral_decode", 0), ("mixtral_prefill", 0)])
-def test_backward_full_size_sampled(name, B):
+def test_backward_full_size(name, B):
     """The Mixtral-shaped layers at full size (the decode shape on the
     streaming path with 32-row blocks and on the library's choice, the tiled
-    path; the prefill shape on the tiled path) against the oracle's per-entry
-    backward on sampled entries: two dx rows, four routing-weight gradients,
-    twelve entries each of dW13 (gate and up rows) and dW2 in experts that
-    tokens select."""
+    path; the prefill shape on the tiled path) against the oracle's
+    per-expert float64 backward: 16 dx rows, the routing-weight gradient of
+    every assignment at decode (32 sampled ones at prefill), and in every
+    expert that tokens select one whole 128 x 256 tile of dW13 and one of
+    dW2 (the weight-gradient kernels' tile shape), at random tile positions."""
     wl = workloads.get(name)
     log(f"full-size backward: {name} B={B} (generating inputs)")
     x, logits = wl.activations(DEV)
@@ -106,17 +116,31 @@ def test_backward_full_size_sampled(name, B):
                                           torch.from_numpy(w).to(DEV), B=B)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
-    used = np.unique(ids)
-    tokens = [0, wl.T - 1]
-    asg = rng.choice(wl.T * wl.k, 4, replace=False).tolist()
-    at13 = [(int(rng.choice(used)), int(rng.integers(2 * wl.f)), int(rng.integers(wl.d))) for _ in range(12)]
-    at2 = [(int(rng.choice(used)), int(rng.integers(wl.d)), int(rng.integers(wl.f))) for _ in range(12)]
-    w13 = [bits(ws["w13"][e]) for e in range(wl.E)]
-    w2 = [bits(ws["w2"][e]) for e in range(wl.E)]
-    log("  oracle on the sampled entries")
-    s_dx, s13, s2, stw = oracle.moe_backward_sampled(bits(x), ids, w, w13, w2, bits(dy), dx_tokens=tokens,
-                                                     dw13_at=at13, dw2_at=at2, dtw_at=asg)
-    _check("dx", bf16_to_f64(bits(dx))[tokens], s_dx)
-    _check("dw13", np.array([dw13[e, r, c].item() for e, r, c in at13]), s13)
-    _check("dw2", np.array([dw2[e, m, n].item() for e, m, n in at2]), s2)
-    _check("dtopk_w", dtw.cpu().numpy().ravel()[asg], stw)
+    n_asg = wl.T * wl.k
+    tokens = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 14, replace=False)]))
+    dtw_asg = np.arange(n_asg) if n_asg <= 256 else np.sort(rng.choice(n_asg, 32, replace=False))
+    full = set((tokens[:, None] * wl.k + np.arange(wl.k)).ravel().tolist()) | set(dtw_asg.tolist())
+    xb, dyb = bits(x), bits(dy)
+    ref_dx = np.zeros((tokens.size, wl.d))
+    ref_tw = {}
+    for e in np.unique(ids):
+        e = int(e)
+        r13 = 128 * int(rng.integers(2 * wl.f // 128))
+        c13 = 256 * int(rng.integers(wl.d // 256))
+        r2 = 128 * int(rng.integers(wl.d // 128))
+        c2 = 256 * int(rng.integers(wl.f // 256))
+        asg = [a for a in np.flatnonzero(ids.ravel() == e).tolist() if a in full]
+        log(f"  oracle, expert {e}: dW13 tile ({r13}, {c13}), dW2 tile ({r2}, {c2}), {len(asg)} whole rows")
+        b13, b2, tw, share = oracle.moe_backward_expert(
+            xb, ids, w, e, bits(ws["w13"][e]), bits(ws["w2"][e]), dyb,
+            rows13=range(r13, r13 + 128), cols13=range(c13, c13 + 256),
+            rows2=range(r2, r2 + 128), cols2=range(c2, c2 + 256), full_asg=asg)
+        _check(f"dw13[{e}]", dw13[e, r13:r13 + 128, c13:c13 + 256].cpu().numpy(), b13)
+        _check(f"dw2[{e}]", dw2[e, r2:r2 + 128, c2:c2 + 256].cpu().numpy(), b2)
+        ref_tw.update(tw)
+        for a, row in share.items():
+            i = np.searchsorted(tokens, a // wl.k)
+            if i < tokens.size and tokens[i] == a // wl.k:
+                ref_dx[i] += row
+    _check("dx", bf16_to_f64(bits(dx))[tokens], ref_dx)
+    _check("dtopk_w", dtw.cpu().numpy().ravel()[dtw_asg], np.array([ref_tw[int(a)] for a in dtw_asg]))

@@ -166,3 +166,31 @@ def test_quant_act_mx_bit_exact(rows, cols):
     rc, rs = oracle.mx_quant_rows(bits(x))
     assert np.array_equal(scales.cpu().numpy(), rs)
     assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quant_act_mx_worked_blocks():
+    """The hand-worked MXFP4 blocks of tests/golden/mx_worked_blocks.json
+    (exact powers of two, values just below a binade, a subnormal amax, an
+    all-zero block): the GPU quantiser's E8M0 scales and E2M1 codes equal
+    the worked values."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "mx_worked_blocks.json")
+    blocks = json.load(open(path))["blocks"]
+    rows = []
+    for b in blocks:
+        if "bf16_bits" in b:
+            rows.append(np.array(b["bf16_bits"], np.uint16))
+        else:
+            v = np.array(b["values"], np.float32)
+            rows.append((v.view(np.uint32) >> 16).astype(np.uint16))   # exact: the values are bf16
+    x = torch.from_numpy(np.stack(rows).view(np.int16)).to(DEV).view(torch.bfloat16)
+    codes, scales = moe.moe_quant_act_mx(x)
+    torch.cuda.synchronize()
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    for r, b in enumerate(blocks):
+        assert scales[r, 0] == b["scale"], b["name"]
+        want = np.array(b["codes"], np.uint8)
+        got = np.empty(32, np.uint8)
+        got[0::2], got[1::2] = codes[r] & 15, codes[r] >> 4
+        assert np.array_equal(got, want), (b["name"], got, want)

@@ -194,3 +194,34 @@ def test_packaged_config_table_loads(lib):
     if not os.path.exists(moe.DEFAULT_CONFIG_TABLE):
         pytest.skip("no packaged table")
     assert moe.moe_load_config_table(moe.DEFAULT_CONFIG_TABLE) > 0
+
+
+def test_binding_shape_checks(lib):
+    """The binding's cross-checks of tensor shapes (host-side, CPU tensors):
+    a mismatched weight, scale, h or sort buffer raises before any library
+    call could read past it."""
+    import torch
+    E, d, f, T, k, B = 4, 256, 512, 10, 2, 32
+    assert moe._weight_scale_shapes("fp8_token", E, d, f) == ((E, 2 * f), (E, d))
+    assert moe._weight_scale_shapes("fp8_block", E, d, f) == ((E, 8, 2), (E, 2, 4))
+    assert moe._weight_scale_shapes("mxfp4", E, d, f) == ((E, 2 * f, 8), (E, d, 16))
+    assert moe._weight_scale_shapes("bf16", E, d, f) == (None, None)
+    P = moe.moe_sort_max_padded(T, k, E, B)
+    assert moe._h_shapes("bf16", P, f) == ((P, f), None)
+    assert moe._h_shapes("fp8_token", P, f) == ((P, f), (P,))
+    assert moe._h_shapes("mxfp4", P, f) == ((P, f // 2), (P, f // 32))
+    moe._shape(torch.empty(E, 2 * f, d), "w13", (E, 2 * f, d))
+    moe._shape(None, "unused", (1,))
+    with pytest.raises(ValueError, match="w13 has shape"):
+        moe._shape(torch.empty(E, 2 * f, d // 2), "w13", (E, 2 * f, d))
+    NB = moe.moe_sort_max_blocks(T, k, E, B)
+    good = dict(sorted_ids=torch.empty(P, dtype=torch.int32), sorted_w=torch.empty(P),
+                sorted_expert_ids=torch.empty(NB, dtype=torch.int32),
+                num_valid=torch.empty(1, dtype=torch.int32))
+    assert moe._check_sort(good, T, k, E, B) == P
+    with pytest.raises(ValueError, match="sorted_ids"):   # a sort made with another block size
+        moe._check_sort(good, T, k, E, 64)
+    with pytest.raises(ValueError, match="sorted_expert_ids"):
+        moe._check_sort(dict(good, sorted_expert_ids=torch.empty(NB - 1, dtype=torch.int32)), T, k, E, B)
+    with pytest.raises(ValueError, match="bad sort shape"):
+        moe._check_sort(good, T, 5, 4, B)

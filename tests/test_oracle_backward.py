@@ -119,3 +119,41 @@ def test_sampled_backward_matches_the_whole_backward():
     np.testing.assert_allclose(s13, [r13[e][r, c] for e, r, c in at13], rtol=1e-4, atol=1e-5)
     np.testing.assert_allclose(s2, [r2[e][m, n] for e, m, n in at2], rtol=1e-4, atol=1e-5)
     np.testing.assert_allclose(stw, rtw.ravel(), rtol=1e-4, atol=1e-5)
+
+
+def test_expert_blocks_match_the_whole_backward():
+    """moe_backward_expert (per expert, float64 matrix products over the
+    expert's assignments) against moe_backward (whole layer, fp32, token by
+    token): whole weight-gradient blocks of every expert, the routing-weight
+    gradient of every assignment and every dx row (summed over experts)."""
+    rng = np.random.default_rng(12)
+    T, d, f, E, k = 14, 64, 96, 4, 2
+    x = oracle.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32)).reshape(T, d)
+    dy = oracle.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32)).reshape(T, d)
+    w13 = [oracle.f32_to_bf16_bits((rng.standard_normal((2 * f, d)) * d ** -0.5).astype(np.float32))
+           .reshape(2 * f, d) for _ in range(E)]
+    w2 = [oracle.f32_to_bf16_bits((rng.standard_normal((d, f)) * f ** -0.5).astype(np.float32))
+          .reshape(d, f) for _ in range(E)]
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 3] = -1e9   # expert 3 unused: zero blocks, no assignments
+    ids, w = oracle.route(logits, k)
+    rdx, r13, r2, rtw = oracle.moe_backward(x, ids, w, w13, w2, dy)
+    dx = np.zeros((T, d))
+    for e in range(E):
+        asg = np.flatnonzero(ids.ravel() == e)
+        b13, b2, dtw, share = oracle.moe_backward_expert(
+            x, ids, w, e, w13[e], w2[e], dy, rows13=range(2 * f), cols13=range(d), rows2=range(d),
+            cols2=range(f), full_asg=asg, chunk=40)
+        np.testing.assert_allclose(b13, r13[e], rtol=1e-4, atol=1e-5)
+        np.testing.assert_allclose(b2, r2[e], rtol=1e-4, atol=1e-5)
+        for a in asg:
+            np.testing.assert_allclose(dtw[int(a)], rtw.ravel()[a], rtol=1e-4, atol=1e-5)
+            dx[a // k] += share[int(a)]
+        if e == 3:
+            assert asg.size == 0 and not b13.any() and not b2.any()
+    np.testing.assert_allclose(dx, rdx, rtol=1e-4, atol=1e-5)
+    # a sub-block picks the same entries
+    b13, b2, _, _ = oracle.moe_backward_expert(x, ids, w, 1, w13[1], w2[1], dy, rows13=[5, f + 7],
+                                               cols13=[0, 63], rows2=[2], cols2=[0, 95])
+    np.testing.assert_allclose(b13, r13[1][np.ix_([5, f + 7], [0, 63])], rtol=1e-4, atol=1e-5)
+    np.testing.assert_allclose(b2, r2[1][np.ix_([2], [0, 95])], rtol=1e-4, atol=1e-5)

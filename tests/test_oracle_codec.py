@@ -243,3 +243,40 @@ def test_mx_quant_rows_packs_blocks():
             assert scales[r, blk] == c
             packed = codes[r, blk * 16:(blk + 1) * 16]
             assert np.array_equal(packed & 15, q[0::2]) and np.array_equal(packed >> 4, q[1::2])
+
+
+def _golden_mx_blocks():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "mx_worked_blocks.json")
+    with open(path) as fh:
+        doc = json.load(fh)
+    out = []
+    for b in doc["blocks"]:
+        if "bf16_bits" in b:
+            bits = np.array(b["bf16_bits"], np.uint16)
+        else:
+            v = np.array(b["values"], np.float32)
+            bits = oracle.f32_to_bf16_bits(v).reshape(v.shape)
+            # every value is exact in bf16 (the blocks are meant for a bf16 quantiser too)
+            assert np.array_equal(oracle.bf16_bits_to_f32(bits).view(np.uint32), v.view(np.uint32))
+        out.append((b["name"], bits, b["scale"], np.array(b["codes"], np.uint8)))
+    return out
+
+
+def test_mx_worked_blocks_golden():
+    """Hand-worked MXFP4 blocks (tests/golden/mx_worked_blocks.json, each
+    step written out from the OCP MX definition): amax exactly 4 * 2^j and
+    6 * 2^j, just below 8 * 2^j and 4 * 2^j, a subnormal amax and an all-zero
+    block. The oracle's block rule and its row quantiser reproduce the
+    scale codes and every element code."""
+    blocks = _golden_mx_blocks()
+    for name, bits, scale, codes in blocks:
+        q, c, deq = oracle.mx_quant_group(oracle.bf16_bits_to_f32(bits))
+        assert c == scale, name
+        assert np.array_equal(q, codes), (name, q, codes)
+    rows = np.stack([b for _, b, _, _ in blocks])
+    packed, scales = oracle.mx_quant_rows(rows)
+    assert np.array_equal(scales[:, 0], [s for _, _, s, _ in blocks])
+    for r, (_, _, _, codes) in enumerate(blocks):
+        assert np.array_equal(packed[r] & 15, codes[0::2]) and np.array_equal(packed[r] >> 4, codes[1::2])
