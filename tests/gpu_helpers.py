@@ -53,12 +53,24 @@ def host_experts(wl, ws, experts):
     return w13, w2, s13, s2
 
 
-def oracle_layer(wl, x, logits, ws, tokens=None, ids=None, w=None):
-    """Oracle output rows (bf16 values as fp64) for `tokens` (default: all)."""
+def oracle_layer(wl, x, logits, ws, tokens=None, ids=None, w=None, chunk=256):
+    """Oracle output rows (bf16 values as fp64) for `tokens` (default: all),
+    computed `chunk` tokens at a time with a progress line per chunk."""
+    import time
     if ids is None:
         ids, w = oracle.route(logits.cpu().numpy(), wl.k, wl.score)
     tok = np.arange(wl.T, dtype=np.int32) if tokens is None else np.asarray(tokens, np.int32)
     need = sorted(set(ids[tok].ravel().tolist()))
     w13, w2, s13, s2 = host_experts(wl, ws, need)
-    _, out = oracle.moe(bits(x), ids, w, w13, w2, s13, s2, quant=wl.quant, tokens=tok)
+    xb = bits(x)
+    parts = []
+    t0 = time.perf_counter()
+    for i in range(0, tok.size, chunk):
+        _, out = oracle.moe(xb, ids, w, w13, w2, s13, s2, quant=wl.quant, tokens=tok[i:i + chunk])
+        parts.append(out)
+        if tok.size > chunk:
+            done = min(tok.size, i + chunk)
+            dt = time.perf_counter() - t0
+            log(f"    oracle {wl.name}: {done}/{tok.size} tokens, {dt:.1f} s ({done / dt:.1f} tokens/s)")
+    out = np.concatenate(parts) if parts else np.zeros((0, wl.d), np.uint16)
     return bf16_to_f64(out), ids, w
