@@ -432,10 +432,10 @@ static void weight_row(const void *w, const void *s, int quant, int cols, int ro
                 continue;
             }
             const float p2 = (float)ldexp(1.0, e);
-            for (int c = 32 * b; c < 32 * b + 32; ++c) {
-                uint8_t byte = ((const uint8_t *)w)[base / 2 + c / 2];
-                uint8_t q = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
-                out[c] = fp4_tab[q] * p2;
+            const uint8_t *bytes = (const uint8_t *)w + base / 2 + 16 * (size_t)b;
+            for (int i = 0; i < 16; ++i) {   /* even column in the low nibble */
+                out[32 * b + 2 * i] = fp4_tab[bytes[i] & 15] * p2;
+                out[32 * b + 2 * i + 1] = fp4_tab[bytes[i] >> 4] * p2;
             }
         }
     } else {

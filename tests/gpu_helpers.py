@@ -1,4 +1,6 @@
 """Shared helpers of the GPU parity tests (the HIP library against the CPU oracle)."""
+import os
+
 import numpy as np
 import torch
 
@@ -63,14 +65,21 @@ def oracle_layer(wl, x, logits, ws, tokens=None, ids=None, w=None, chunk=256):
     need = sorted(set(ids[tok].ravel().tolist()))
     w13, w2, s13, s2 = host_experts(wl, ws, need)
     xb = bits(x)
-    parts = []
+    # Tokens go to the oracle ordered by their experts (each token's row is
+    # computed on its own, so the order changes no value): threads working
+    # at the same time then read the same expert weights. The thread count
+    # is passed explicitly, as the process's OpenMP default can be lower.
+    order = np.lexsort(tuple(ids[tok, j] for j in reversed(range(wl.k))))
+    threads = int(os.environ.get("OMP_NUM_THREADS") or 0) or len(os.sched_getaffinity(0))
+    out = np.empty((tok.size, wl.d), np.uint16)
     t0 = time.perf_counter()
     for i in range(0, tok.size, chunk):
-        _, out = oracle.moe(xb, ids, w, w13, w2, s13, s2, quant=wl.quant, tokens=tok[i:i + chunk])
-        parts.append(out)
+        sel = order[i:i + chunk]
+        _, out[sel] = oracle.moe(xb, ids, w, w13, w2, s13, s2, quant=wl.quant, tokens=tok[sel],
+                                 threads=threads)
         if tok.size > chunk:
             done = min(tok.size, i + chunk)
             dt = time.perf_counter() - t0
-            log(f"    oracle {wl.name}: {done}/{tok.size} tokens, {dt:.1f} s ({done / dt:.1f} tokens/s)")
-    out = np.concatenate(parts) if parts else np.zeros((0, wl.d), np.uint16)
+            log(f"    oracle {wl.name}: {done}/{tok.size} tokens, {dt:.1f} s ({done / dt:.1f} tokens/s, "
+                f"{threads} threads)")
     return bf16_to_f64(out), ids, w
