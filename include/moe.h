@@ -222,6 +222,25 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
               const void *w2, const void *w2_scale,
               int B, int stage, int ksplit, void *out, void *ws, size_t ws_bytes, void *stream);
 
+/* fused_moe without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The workspace is a static array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library's device code, one per GPU,
+ * present from the library's first use on that GPU until the process ends;
+ * the call allocates nothing. Layers whose fused_moe workspace (the query
+ * fused_moe_workspace_bytes) exceeds that size are refused with
+ * MOE_ERR_UNSUPPORTED before any device work. Every call on one GPU uses the
+ * same array (the previous call's contents are overwritten; nothing in it
+ * needs to start at zero), so calls that overlap on one GPU, on different
+ * streams or host threads, race: order them on one stream. Arguments,
+ * results and errors are otherwise those of fused_moe. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int fused_moe_noalloc(int T, int d, int f, int E, int k, int quant, int score, int renorm,
+                      const float *logits, const int32_t *topk_ids, const float *topk_w,
+                      const void *x, const void *w13, const void *w13_scale,
+                      const void *w2, const void *w2_scale,
+                      int B, int stage, int ksplit, void *out, void *stream);
+
 /* The library's choice of block size B, stage and K-split for a shape
  * (AITER walk-through, sections 3.2 to 3.4 describe the choices; the rule
  * here is this library's own, from measurement on MI355X). cu_count <= 0

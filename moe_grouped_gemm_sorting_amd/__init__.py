@@ -22,7 +22,12 @@ __all__ = [
     "moe_gemm1_workspace_bytes", "moe_gemm1_swiglu", "moe_gemm2_workspace_bytes",
     "moe_gemm2_combine", "fused_moe_workspace_bytes", "fused_moe", "moe_select_config",
     "moe_load_config_table", "DEFAULT_CONFIG_TABLE", "moe_backward_workspace_bytes", "moe_backward",
+    "fused_moe_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
+
+# The size of fused_moe_noalloc's static workspace (MOE_NOALLOC_SCRATCH_BYTES
+# in include/moe.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmoe.so")
@@ -70,6 +75,7 @@ def load_library():
         "moe_gemm2_combine": (i32, [i32] * 8 + [P] * 9 + [P, sz, P]),
         "fused_moe_workspace_bytes": (sz, [i32] * 8),
         "fused_moe": (i32, [i32] * 8 + [P] * 8 + [i32, i32, i32, P, P, sz, P]),
+        "fused_moe_noalloc": (i32, [i32] * 8 + [P] * 8 + [i32, i32, i32, P, P]),
         "moe_select_config": (i32, [i32] * 7 + [P, P, P]),
         "moe_load_config_table": (i32, [ctypes.c_char_p, P]),
         "moe_backward_workspace_bytes": (sz, [i32] * 6),
@@ -399,6 +405,51 @@ def fused_moe(x, w13, w2, k: int, logits=None, topk_ids=None, topk_w=None, quant
     _check(lib.fused_moe(T, d, f, E, k, q, SCORE[score], int(renorm), _ptr(logits), _ptr(topk_ids),
                          _ptr(topk_w), _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2),
                          _ptr(w2_scale), B, stage, ksplit, _ptr(out), _ptr(ws), nbytes, _stream(x)))
+    return out
+
+
+def fused_moe_noalloc(x, w13, w2, k: int, logits=None, topk_ids=None, topk_w=None,
+                      quant: str = "bf16", w13_scale=None, w2_scale=None, score: str = "softmax",
+                      renorm: bool = True, B: int = 0, stage: int = 0, ksplit: int = 0, out=None):
+    """fused_moe on the library's static per-GPU workspace: no workspace
+    argument and no device allocation inside the call (pass `out` to avoid
+    the output allocation too). Returns out bf16 [T, d]."""
+    lib = load_library()
+    _need(x, "x", (torch.bfloat16,))
+    dev = x.device
+    q = QUANT[quant]
+    _need(w13, "w13", _wdtypes(quant), dev)
+    _need(w2, "w2", _wdtypes(quant), dev)
+    if x.dim() != 2 or w13.dim() != 3:
+        raise ValueError("x must be [T, d] and w13 [E, 2f, d]")
+    T, d = x.shape
+    E, f2, _ = w13.shape
+    f = f2 // 2
+    pk = _pk(quant)
+    _shape(w13, "w13", (E, 2 * f, d // pk))
+    _shape(w2, "w2", (E, d, f // pk))
+    if logits is not None:
+        _need(logits, "logits", (torch.float32,), dev)
+        _shape(logits, "logits", (T, E))
+    else:
+        _need(topk_ids, "topk_ids", (torch.int32,), dev)
+        _need(topk_w, "topk_w", (torch.float32,), dev)
+        _shape(topk_ids, "topk_ids", (T, k))
+        _shape(topk_w, "topk_w", (T, k))
+    if q:
+        _need(w13_scale, "w13_scale", _sdtypes(quant), dev)
+        _need(w2_scale, "w2_scale", _sdtypes(quant), dev)
+        s13, s2 = _weight_scale_shapes(quant, E, d, f)
+        _shape(w13_scale, "w13_scale", s13)
+        _shape(w2_scale, "w2_scale", s2)
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", (torch.bfloat16,), dev)
+        _shape(out, "out", (T, d))
+    _check(lib.fused_moe_noalloc(T, d, f, E, k, q, SCORE[score], int(renorm), _ptr(logits),
+                                 _ptr(topk_ids), _ptr(topk_w), _ptr(x), _ptr(w13), _ptr(w13_scale),
+                                 _ptr(w2), _ptr(w2_scale), B, stage, ksplit, _ptr(out), _stream(x)))
     return out
 
 

@@ -873,11 +873,15 @@ size_t fused_moe_workspace_bytes(int T, int d, int f, int E, int k, int quant, i
     return c.bytes();
 }
 
-int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renorm,
-              const float *logits, const int32_t *topk_ids, const float *topk_w, const void *x,
-              const void *w13, const void *w13_scale, const void *w2, const void *w2_scale,
-              int B, int stage, int ksplit, void *out, void *ws, size_t ws_bytes, void *stream) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+// The whole layer on a workspace of ws_bytes at ws (fused_moe and its
+// no-allocation variant).
+int fused_impl(int T, int d, int f, int E, int k, int quant, int score, int renorm,
+               const float *logits, const int32_t *topk_ids, const float *topk_w, const void *x,
+               const void *w13, const void *w13_scale, const void *w2, const void *w2_scale,
+               int B, int stage, int ksplit, void *out, void *ws, size_t ws_bytes, void *stream) {
     int rc = resolve(T, d, f, E, k, quant, &B, &stage);
     if (rc) return rc;
     if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
@@ -937,6 +941,71 @@ int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renor
     if (rc) return rc;
     return run_gemm2(T, d, f, E, k, B, quant, ksplit, w.h, w.h_scale, w2, w2_scale, w.sorted_ids,
                      w.sorted_w, w.seid, w.num_valid, out, w.g2, logits != nullptr, s, true);
+}
+
+// ------------------------------------------------- no-allocation variant
+// The workspace of fused_moe_noalloc: one array per GPU, loaded with the
+// library's code object and held until the process ends. Host code never
+// uses the name `scratch` as an address (on the host it is only a stand-in
+// for the device symbol): the device address is looked up per device with
+// hipGetSymbolAddress and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[MAX_DEVICES] = {};
+
+// The current device's scratch address (looked up on the device's first
+// call, with that device current).
+int scratch_address(void **out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                    MAX_DEVICES - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int fused_moe(int T, int d, int f, int E, int k, int quant, int score, int renorm,
+              const float *logits, const int32_t *topk_ids, const float *topk_w, const void *x,
+              const void *w13, const void *w13_scale, const void *w2, const void *w2_scale,
+              int B, int stage, int ksplit, void *out, void *ws, size_t ws_bytes, void *stream) {
+    g_err[0] = 0;
+    return fused_impl(T, d, f, E, k, quant, score, renorm, logits, topk_ids, topk_w, x, w13, w13_scale,
+                      w2, w2_scale, B, stage, ksplit, out, ws, ws_bytes, stream);
+}
+
+int fused_moe_noalloc(int T, int d, int f, int E, int k, int quant, int score, int renorm,
+                      const float *logits, const int32_t *topk_ids, const float *topk_w,
+                      const void *x, const void *w13, const void *w13_scale, const void *w2,
+                      const void *w2_scale, int B, int stage, int ksplit, void *out, void *stream) {
+    g_err[0] = 0;
+    int Br = B, stage_r = stage;
+    int rc = resolve(T, d, f, E, k, quant, &Br, &stage_r);
+    if (rc) return rc;
+    Carver c(nullptr);
+    carve_fused(c, T, d, f, E, k, quant, Br, true);
+    if (c.bytes() > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "this layer needs %zu bytes of workspace; the static scratch of fused_moe_noalloc "
+                    "holds %zu (use fused_moe with a caller-allocated workspace)",
+                    c.bytes(), (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    return fused_impl(T, d, f, E, k, quant, score, renorm, logits, topk_ids, topk_w, x, w13, w13_scale,
+                      w2, w2_scale, Br, stage_r, ksplit, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"
