@@ -246,17 +246,40 @@ int pick_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
 }
 
 // -------------------------------------------------------------- stage 1/2
+// Split of GEMM1's reduction (K = d) for few assignments (the AITER
+// walk-through, section 3.4, splits K when token * topk <= expert and the
+// tiles do not fill the CUs). bf16 on the streaming kernel: with
+// T * k <= E at most T * k sort blocks hold rows, which is too few
+// workgroups to keep enough weight bytes in flight; the parts' raw gate / up
+// sums are added in a fixed order by a second kernel that applies SwiGLU.
+// Aimed at about MOE_G1_WG_PER_CU workgroups per CU, at most 8 parts.
+#ifndef MOE_G1_WG_PER_CU
+#define MOE_G1_WG_PER_CU 8
+#endif
+int gemm1_ksplit(int T, int d, int f, int E, int k, int B, int quant, int cu) {
+    if (quant != 0 || use_tiled(B) || (int64_t)T * k > E) return 1;
+    const int64_t blocks = std::min<int64_t>(max_blocks(T, k, E, B), (int64_t)T * k);
+    const int64_t wgs = std::max<int64_t>(1, (int64_t)(f / (64 * MOE_G1_CT)) * blocks);
+    const int64_t want = ((int64_t)MOE_G1_WG_PER_CU * cu + wgs - 1) / wgs;
+    const int ks = (int)std::max<int64_t>(1, std::min<int64_t>(8, want));
+    return ks > 1 ? stream_gemm1_parts(d, ks) : 1;
+}
+
 struct Gemm1Ws {
     uint8_t *qx = nullptr;
     float *sx = nullptr;
     uint8_t *sxm = nullptr;   // MXFP4: E8M0 scales of x [T, d/32]
     uint16_t *hb = nullptr;
     float *amax = nullptr;
+    int ksplit = 1;           // GEMM1 parts (bf16 streaming kernel, few assignments)
+    float *gu_part = nullptr; // their raw sums [ksplit][T*k, 2f]
 };
 
 Gemm1Ws carve_gemm1(Carver &c, int T, int d, int f, int E, int k, int B, int quant) {
     Gemm1Ws w;
     const size_t P = (size_t)max_padded(T, k, E, B);
+    w.ksplit = gemm1_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
+    if (w.ksplit > 1) w.gu_part = c.take<float>((size_t)w.ksplit * T * k * 2 * f);
     if (quant == MOE_QUANT_MXFP4) {
         w.qx = c.take<uint8_t>((size_t)T * d / 2);
         w.sxm = c.take<uint8_t>((size_t)T * (d / 32));
@@ -321,7 +344,15 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     } else {
         if (!stream_gemm1_supported(g.sh))
             return fail(MOE_ERR_UNSUPPORTED, "no GEMM1 kernel for B=%d", B);
+        if (w.ksplit > 1) {
+            g.ksplit = w.ksplit;
+            g.gu_part = w.gu_part;
+        }
         HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");
+        if (w.ksplit > 1)
+            HIP_TRY(launch_swiglu_parts(w.gu_part, w.ksplit, T * k, f, sorted_ids, num_valid, (int)P,
+                                        static_cast<uint16_t *>(h), s),
+                    "SwiGLU launch");
     }
     if (quant == 1)
         HIP_TRY(launch_quant_h_rows(w.hb, w.amax, (int)P, f, num_valid, sorted_ids, T * k,

@@ -56,6 +56,11 @@ struct StreamParams {
     // weight) and adds <v, h> into the routing-weight gradient of the
     // assignment (fp32 atomics); bwd_f is the layer's f.
     float *gu_out;
+    // GEMM1 split over K (bf16): part blockIdx.y writes its raw gate / up sums
+    // of every real row to gu_part [parts][T*k][2f] fp32 by assignment
+    // (gate at column n, up at f + n) instead of h; a reduction kernel adds
+    // the parts in a fixed order and applies SwiGLU
+    float *gu_part;
     int bwd, bwd_f;
     const float *bwd_gu;
     const uint16_t *bwd_h;
@@ -508,6 +513,24 @@ __global__ __launch_bounds__(256) void k_gemm_stream(StreamParams p) {
 
     // ------------------------------------------------------------ epilogue
     if constexpr (GEMM1 && QUANT == 0) {
+        if (p.gu_part) {
+            const size_t f2 = 2 * (size_t)p.f;
+            float *part = p.gu_part + (size_t)blockIdx.y * sentinel * f2;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int a = __shfl(a_of_lane[rt], lg * 4 + i, 64);
+                    if (a >= sentinel) continue;   // padding rows are not stored
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        const int n = n0 + ct * 16 + lr;
+                        part[(size_t)a * f2 + n] = acc[rt][ct][i];
+                        part[(size_t)a * f2 + p.f + n] = acc[rt][CT + ct][i];
+                    }
+                }
+            return;
+        }
         if (p.bwd) {
             const int fb = p.bwd_f;
 #pragma unroll
@@ -755,8 +778,27 @@ hipError_t launch_stream_gemm1(const Gemm1Args &g, int CT, hipStream_t s) {
     const int RT = sh.B / 16;
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + sh.B - 1) / sh.B;
-    const dim3 grid(sh.f / (64 * CT), 1, NB);
+    // K split (bf16): parts of whole 128-byte steps, raw sums to gu_part
+    int parts = 1;
+    if (sh.quant == 0 && g.gu_part && g.ksplit > 1) {
+        const int steps = sh.d / Elem<0>::kstep;
+        const int steps_per = (steps + g.ksplit - 1) / g.ksplit;
+        p.kchunk = steps_per * Elem<0>::kstep;
+        p.gu_part = g.gu_part;
+        parts = (steps + steps_per - 1) / steps_per;
+    }
+    const dim3 grid(sh.f / (64 * CT), parts, NB);
     return dispatch<true>(p, sh.quant, RT, CT, grid, s);
+}
+
+// Parts of the bf16 GEMM1 K split actually launched for a requested split
+// (each part whole 128-byte steps).
+int stream_gemm1_parts(int d, int ksplit) {
+    const int steps = d / Elem<0>::kstep;
+    if (ksplit < 1) ksplit = 1;
+    if (ksplit > steps) ksplit = steps;
+    const int steps_per = (steps + ksplit - 1) / ksplit;
+    return (steps + steps_per - 1) / steps_per;
 }
 
 // Backward of the down projection and SwiGLU (bf16): v = Wd^T dy per slot,

@@ -71,7 +71,20 @@ struct Gemm1Args {
     uint8_t *h_mx;
     float *gu_out;          // optional (bf16): raw gate / up sums [P, 2f] fp32; the streaming
                             // kernel also writes h, the tiled kernel writes only these
+    // streaming kernel, bf16: split K = d into ksplit parts whose raw gate /
+    // up sums go to gu_part [parts][T*k, 2f] fp32 (by assignment); h is then
+    // written by launch_swiglu_parts
+    int ksplit;
+    float *gu_part;
 };
+
+// Parts the streaming bf16 GEMM1 launches for a requested K split.
+int stream_gemm1_parts(int d, int ksplit);
+// h[slot] = bf16(silu(sum_q g_q) * sum_q u_q) for the real slots (the parts
+// q ascending; g, u from gu_part [parts][n_asg, 2f] at the slot's
+// assignment); padding slots and slots past num_valid are left untouched.
+hipError_t launch_swiglu_parts(const float *gu_part, int parts, int n_asg, int f, const int32_t *sorted_ids,
+                               const int32_t *num_valid, int P, uint16_t *h, hipStream_t s);
 
 struct Gemm2Args {
     GemmShape sh;

@@ -282,4 +282,54 @@ hipError_t launch_mark_written(const int32_t *sorted_ids, const int32_t *num_val
     return hipGetLastError();
 }
 
+// The end of the bf16 GEMM1 split over K: for each real slot, the parts'
+// gate and up sums added in ascending part order (a fixed order, so the
+// result does not depend on scheduling), then h = bf16(silu(g) u), the same
+// epilogue as the unsplit kernel. One workgroup: 2048 columns of one slot.
+__global__ __launch_bounds__(256) void k_swiglu_parts(const float *__restrict__ gu_part, int parts, int n_asg,
+                                                      int f, const int32_t *__restrict__ sorted_ids,
+                                                      const int32_t *__restrict__ num_valid,
+                                                      uint16_t *__restrict__ h) {
+    const int slot = blockIdx.x;
+    if (slot >= *num_valid) return;
+    const int a = sorted_ids[slot];
+    if (a >= n_asg) return;
+    const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+    if (c >= f) return;
+    const size_t f2 = 2 * (size_t)f, slab = (size_t)n_asg * f2;
+    const float *src = gu_part + (size_t)a * f2 + c;
+    float g[8], u[8];
+#pragma unroll
+    for (int i = 0; i < 8; i += 4) {
+        const float4 gv = *reinterpret_cast<const float4 *>(src + i);
+        const float4 uv = *reinterpret_cast<const float4 *>(src + f + i);
+        g[i] = gv.x; g[i + 1] = gv.y; g[i + 2] = gv.z; g[i + 3] = gv.w;
+        u[i] = uv.x; u[i + 1] = uv.y; u[i + 2] = uv.z; u[i + 3] = uv.w;
+    }
+    for (int q = 1; q < parts; ++q) {
+        const float *sq = src + (size_t)q * slab;
+#pragma unroll
+        for (int i = 0; i < 8; i += 4) {
+            const float4 gv = *reinterpret_cast<const float4 *>(sq + i);
+            const float4 uv = *reinterpret_cast<const float4 *>(sq + f + i);
+            g[i] += gv.x; g[i + 1] += gv.y; g[i + 2] += gv.z; g[i + 3] += gv.w;
+            u[i] += uv.x; u[i + 1] += uv.y; u[i + 2] += uv.z; u[i + 3] += uv.w;
+        }
+    }
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = f32_to_bf16_bits(silu(g[2 * i]) * u[2 * i]) |
+               ((uint32_t)f32_to_bf16_bits(silu(g[2 * i + 1]) * u[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4 *>(h + (size_t)slot * f + c) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+hipError_t launch_swiglu_parts(const float *gu_part, int parts, int n_asg, int f, const int32_t *sorted_ids,
+                               const int32_t *num_valid, int P, uint16_t *h, hipStream_t s) {
+    if (P == 0 || n_asg == 0) return hipSuccess;
+    const dim3 grid((unsigned)P, (unsigned)((f / 8 + 255) / 256));
+    k_swiglu_parts<<<grid, 256, 0, s>>>(gu_part, parts, n_asg, f, sorted_ids, num_valid, h);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -109,6 +109,7 @@ def main(argv=None):
                          "DeepSeek-shaped fp8_block layers over T = 1..512")
     ap.add_argument("--out", required=True)
     ap.add_argument("--iters", type=int, default=10)
+    ap.add_argument("--all", action="store_true", help="print every candidate's time")
     args = ap.parse_args(argv)
 
     shapes = []
@@ -142,6 +143,9 @@ def main(argv=None):
             print(f"[tune] T={T} d={d} f={f} E={E} k={k} {quant}: no supported configuration",
                   file=sys.stderr, flush=True)
             continue
+        if args.all:
+            for r in rows:
+                print(f"[tune]   T={T} {quant}: B={r[0]} stage={r[1]} ksplit={r[2]} {r[3]:.1f} us", flush=True)
         B, stage, ks, us = rows[0]
         lines.append(f"{cu},{T},{d},{f},{E},{k},{quant},{B},{stage},{ks},{us:.1f},{base:.1f}")
         print(f"[tune] T={T} d={d} f={f} E={E} k={k} {quant}: B={B} stage={stage} ksplit={ks} "

@@ -234,3 +234,29 @@ def test_ids_outside_the_expert_range_add_nothing(B):
         err, _ = rel_err(bf16_to_f64(bits(o)), ref)
         assert err <= TOL["bf16"], (B, err)
     assert not out[7].float().any() and not out2[7].float().any()
+
+
+@pytest.mark.parametrize("T", (1, 2, 4))
+def test_gemm1_k_split_few_tokens(T):
+    """The single-token regime (T * k <= E) at the full Mixtral shape: with
+    sort blocks of 16 or 32 rows, bf16 GEMM1 splits its reduction over d and a
+    second kernel adds the parts in a fixed order before SwiGLU. Every token
+    against the oracle on the two-stage path, for both block sizes and the
+    library's choice; h is bit-identical over repeated calls."""
+    wl = workloads.get("mixtral_decode").replace(name=f"decode_t{T}", T=T, seed=60 + T)
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    ref, rid, rw = oracle_layer(wl, x, logits, ws)
+    for B in (16, 32, 0):
+        out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, B=B, stage=2 if B else 0)
+        torch.cuda.synchronize()
+        err, norm = rel_err(bf16_to_f64(bits(out)), ref)
+        log(f"split GEMM1 T={T} B={B}: err={err:.3e} norm={norm:.3e}")
+        assert err <= TOL["bf16"], (T, B, err)
+    ids, w = torch.from_numpy(rid).to(DEV), torch.from_numpy(rw).to(DEV)
+    srt = moe.moe_sort(ids, w, wl.E, 16)
+    h1, _ = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, 16)
+    h2, _ = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, 16)
+    torch.cuda.synchronize()
+    real = (srt["sorted_ids"] < wl.T * wl.k).cpu().numpy()
+    assert np.array_equal(bits(h1)[real], bits(h2)[real])

@@ -184,6 +184,8 @@ WORKLOADS = {
                               quant="mxfp4", seed=1006),
     "mixtral_prefill_mxfp4": Workload("mixtral_prefill_mxfp4", T=4096, d=4096, f=14336, E=8, k=2,
                                       quant="mxfp4", seed=1007),
+    # the single-token decode regime (T * k <= E) on the Mixtral shape
+    "mixtral_single": Workload("mixtral_single", T=1, d=4096, f=14336, E=8, k=2, seed=1008),
 }
 
 
