@@ -636,8 +636,10 @@ BwdWs carve_backward(Carver &c, int T, int d, int f, int E, int k, int B) {
     w.counts = c.take<int32_t>(E);
     w.offsets = c.take<int32_t>((size_t)E + 1);
     w.num_valid = c.take<int32_t>(1);
-    w.w13t = c.take<uint16_t>((size_t)E * 2 * f * d);
-    w.w2t = c.take<uint16_t>((size_t)E * f * d);
+    if (B < 64) {   // the streaming kernels read transposed copies of the weights
+        w.w13t = c.take<uint16_t>((size_t)E * 2 * f * d);
+        w.w2t = c.take<uint16_t>((size_t)E * f * d);
+    }
     w.gu = c.take<float>(P * 2 * f);
     w.h = c.take<uint16_t>(P * f);
     w.dgu = c.take<uint16_t>(P * 2 * f);
@@ -719,10 +721,12 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
     HIP_TRY(launch_sort(topk_ids, topk_w, T, k, E, B, w.sorted_ids, w.sorted_w, w.seid, w.counts,
                         w.offsets, w.num_valid, s),
             "sort launch");
-    HIP_TRY(launch_transpose_bf16(static_cast<const uint16_t *>(w13), E, 2 * f, d, w.w13t, s),
-            "transpose launch");
-    HIP_TRY(launch_transpose_bf16(static_cast<const uint16_t *>(w2), E, d, f, w.w2t, s),
-            "transpose launch");
+    if (B < 64) {
+        HIP_TRY(launch_transpose_bf16(static_cast<const uint16_t *>(w13), E, 2 * f, d, w.w13t, s),
+                "transpose launch");
+        HIP_TRY(launch_transpose_bf16(static_cast<const uint16_t *>(w2), E, d, f, w.w2t, s),
+                "transpose launch");
+    }
     HIP_TRY(launch_fill_f32(dtopk_w, (size_t)T * k, 0.0f, s), "fill launch");
     HIP_TRY(launch_fill_f32(w.acc, (size_t)T * d, 0.0f, s), "fill launch");
     // forward GEMM1 again, keeping the gate / up sums
@@ -739,7 +743,7 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
     Gemm2Args g2{};
     g2.sh = GemmShape{T, d, 2 * f, E, k, B, 0};
     g2.h = w.dgu;
-    g2.w2 = w.w13t;
+    g2.w2 = w.w13t;   // the tiled path reads w13 in place (below)
     g2.sorted_ids = w.sorted_ids;
     g2.sorted_w = nullptr;
     g2.sorted_expert_ids = w.seid;
@@ -747,11 +751,13 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
     g2.acc = w.acc;
     if (B >= 64) {
         HIP_TRY(launch_tiled_gemm1(g, 0, 0, s), "GEMM1 launch");
-        // v = Wd^T dy per slot: Wd^T [E, f, d] as GEMM1 weights of f/2 gate and f/2 up rows
+        // v = Wd^T dy per slot: Wd [E, d, f] read in place as [K][N] weights of f/2 gate
+        // and f/2 up columns
         Gemm1Args gv{};
         gv.sh = GemmShape{T, d, f / 2, E, k, B, 0};
         gv.a = dy;
-        gv.w13 = w.w2t;
+        gv.w13 = w2;
+        gv.w_kn = true;
         gv.sorted_ids = w.sorted_ids;
         gv.sorted_expert_ids = w.seid;
         gv.num_valid = w.num_valid;
@@ -764,6 +770,8 @@ int moe_backward(int T, int d, int f, int E, int k, int B, const void *x, const 
         const int64_t tiles = max_blocks(T, k, E, B) * (int64_t)(d / tiled_tile_cols(B, 0, false, 0, 0));
         const int cu = cu_count_cached();
         const int ks = (int)std::min<int64_t>(4, std::max<int64_t>(1, (4 * (int64_t)cu + tiles - 1) / tiles));
+        g2.w2 = w13;   // W13 [E, 2f, d] read in place as [K][N] weights
+        g2.w_kn = true;
         HIP_TRY(launch_tiled_gemm2(g2, 0, 0, ks, s), "backward GEMM launch");
     } else {
         HIP_TRY(launch_stream_gemm1(g, MOE_G1_CT, s), "GEMM1 launch");

@@ -60,6 +60,8 @@ namespace moe {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 #ifndef MOE_GROUP_M
 #define MOE_GROUP_M 8
@@ -70,6 +72,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #endif
 #ifndef MOE_TILED_STRIP2
 #define MOE_TILED_STRIP2 2
+#endif
+// 1: raise the wave's priority while it issues a sub-step's MFMAs (bf16)
+#ifndef MOE_TILED_PRIO
+#define MOE_TILED_PRIO 0
 #endif
 constexpr int GROUP_M = MOE_GROUP_M;  // sort blocks per tile group (block-group order)
 constexpr int ROWB = 128;       // bytes per row per K step
@@ -179,8 +185,18 @@ __device__ __forceinline__ f32x16 mma32_fp4(const u32x4 &a, const u32x4 &b, uint
 // rows). QUANT 0 (bf16) or 1 (e4m3, per-row activation scale and
 // per-channel weight scale applied in the epilogue). The 8 waves form a
 // WM x WN grid, each wave owning (BM / WM) rows x 64 weight rows.
-template <int QUANT, bool GEMM1, int BM, int TN, int WAVES>
+// BT (bf16 only): the weights are stored [K][N] (N contiguous) instead of
+// [N][K]: the backward's products with Wd^T and W13^T read the forward's
+// weights in place. A stage then holds the tile's 64 K rows of TN columns
+// (TN * 2 bytes each, 16-byte chunk c of K row r at position
+// c ^ 4 (r % 4)) and the MFMA B fragments come from two transposing reads
+// ds_read_tr16_b64 each: within a 16-lane group, lane 4j + q points at
+// K row k0 + j and columns c0 + 4q .. c0 + 4q + 3, and lane i receives K rows
+// k0 .. k0 + 3 of column c0 + i. The four K rows a half-wave reads then sit
+// in four different 64-byte bank groups.
+template <int QUANT, bool GEMM1, int BM, int TN, int WAVES, bool BT = false>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
+    static_assert(!BT || QUANT == 0, "weights stored [K][N] are bf16 only");
     constexpr int NTHR = 64 * WAVES;
     constexpr bool MX = QUANT == 3;             // MXFP4: E2M1 two per byte, E8M0 per 32
     auto eb = [](size_t n) -> size_t { return QUANT == 0 ? 2 * n : (MX ? n / 2 : n); };  // bytes of n elements
@@ -332,10 +348,22 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     uint32_t goff[NQ];
 #pragma unroll
     for (int i = NQA; i < NQ; ++i) {
-        const int row = 8 * (wave + WAVES * i) + (lane >> 3);
-        const int rb = row - BM;   // 0..TN-1
-        const int n = GEMM1 ? (rb < TN / 2 ? 0 : p.f - TN / 2) + nt * (TN / 2) + rb : nt * TN + rb;
-        goff[i] = (uint32_t)n * kbytes + swz(row, lane & 7) * 16;
+        if constexpr (BT) {
+            // instruction i fills K rows 2q and 2q + 1 of the B region
+            // (q = its kilobyte there); lane l: K row 2q + l / 32, chunk
+            // position l % 32, which holds the row's logical 8-column chunk
+            // (l % 32) ^ 4 (K row % 4)
+            const int q = wave + WAVES * (i - NQA);
+            const int kr = 2 * q + (lane >> 5);
+            const int lc = 8 * ((lane & 31) ^ ((kr & 3) << 2));   // column in the tile, 0..TN-1
+            const int n = GEMM1 ? (lc < TN / 2 ? 0 : p.f - TN / 2) + nt * (TN / 2) + lc : nt * TN + lc;
+            goff[i] = (uint32_t)kr * (uint32_t)(Ntot * 2) + (uint32_t)n * 2;
+        } else {
+            const int row = 8 * (wave + WAVES * i) + (lane >> 3);
+            const int rb = row - BM;   // 0..TN-1
+            const int n = GEMM1 ? (rb < TN / 2 ? 0 : p.f - TN / 2) + nt * (TN / 2) + rb : nt * TN + rb;
+            goff[i] = (uint32_t)n * kbytes + swz(row, lane & 7) * 16;
+        }
     }
     const uint32_t m0w = lds_addr(lds) + (uint32_t)wave * 1024u;
     // MXFP4 scale copies: pair q of K steps (steps 2q, 2q + 1 of this K
@@ -351,7 +379,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     };
     auto issue_part = [&](int buf, int kk, int i0, int i1) {
         const uint8_t *ab = p.a + eb(kk);
-        const uint8_t *bb = wexp + eb(kk);
+        // [N][K] weights advance along the row, [K][N] weights by kk rows
+        const uint8_t *bb = BT ? wexp + (size_t)kk * Ntot * 2 : wexp + eb(kk);
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             if (i < i0 || i >= i1) continue;
@@ -422,10 +451,31 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
             fa[rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB + swz(arow[rt], chunk) * 16);
+        if constexpr (BT) {
+            // K rows 8 chunk .. 8 chunk + 7 of column brow[ct]: two transposing
+            // reads of four K rows each (the lane's 16-lane group starts at
+            // column brow[ct] - lane % 16)
+            const uint32_t bbase = lds_addr(base) + (uint32_t)(BM * ROWB);
+            const int li = lane & 15, tj = li >> 2, tq = li & 3;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-            fb[ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
-                                                      swz(brow[ct], chunk) * 16);
+            for (int ct = 0; ct < CT; ++ct) {
+                const int col = brow[ct] - li + 4 * tq;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int kr = 8 * chunk + 4 * hh + tj;
+                    const int pos = (col >> 3) ^ ((kr & 3) << 2);
+                    const uint32_t addr = bbase + (uint32_t)(kr * (TN * 2) + pos * 16 + (col & 7) * 2);
+                    const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(uintptr_t)addr);
+                    fb[ct][2 * hh] = (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+                    fb[ct][2 * hh + 1] = (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                fb[ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
+                                                          swz(brow[ct], chunk) * 16);
+        }
     };
     // bf16: CH/2 sub-steps of K = 16 (lane half lh takes chunk 2s + lh); the
     // fragments of sub-step s+1 are read while the MFMAs of sub-step s run.
@@ -474,11 +524,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
             for (int sub = 0; sub < NSUB; ++sub) {
                 if (sub + 1 < NSUB) frags_at(base, 2 * (sub + 1) + lh, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
+                if constexpr (MOE_TILED_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         acc[rt][ct] = mma32_bf16(fa[sub & 1][rt], fb[sub & 1][ct], acc[rt][ct]);
+                if constexpr (MOE_TILED_PRIO) __builtin_amdgcn_s_setprio(0);
             }
         } else {
             constexpr int NSUB = CH / 4;
@@ -710,6 +762,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     clear_zero();
 }
 
+// bf16 with weights stored [K][N] (the backward): the 256-column tiles
+template <bool GEMM1>
+hipError_t dispatch_kn(const TiledParams &p, int BM, int TN, dim3 grid, hipStream_t s) {
+    if (TN != 256) return hipErrorInvalidValue;
+    if (BM == 64)
+        k_gemm_tiled<0, GEMM1, 64, 256, 8, true><<<grid, 512, 0, s>>>(p);
+    else if (BM == 128)
+        k_gemm_tiled<0, GEMM1, 128, 256, 8, true><<<grid, 512, 0, s>>>(p);
+    else if (BM == 256)
+        k_gemm_tiled<0, GEMM1, 256, 256, 8, true><<<grid, 512, 0, s>>>(p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 template <int QUANT, bool GEMM1>
 hipError_t dispatch_shape(const TiledParams &p, int BM, int TN, dim3 grid, hipStream_t s) {
     if (BM == 64 && TN == 256)
@@ -807,6 +874,10 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s)
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + ts.bm - 1) / ts.bm;
     const dim3 grid(grid_tiles(NB, sh.f / (ts.tn / 2)), 1);
+    if (g.w_kn) {
+        if (sh.quant != 0) return hipErrorInvalidValue;
+        return dispatch_kn<true>(p, ts.bm, ts.tn, grid, s);
+    }
     return dispatch<true>(p, sh.quant, ts.bm, ts.tn, grid, s);
 }
 
@@ -854,6 +925,10 @@ hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hi
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + ts.bm - 1) / ts.bm;
     const dim3 grid(grid_tiles(NB, sh.d / ts.tn), ksplit);
+    if (g.w_kn) {
+        if (sh.quant != 0) return hipErrorInvalidValue;
+        return dispatch_kn<false>(p, ts.bm, ts.tn, grid, s);
+    }
     return dispatch<false>(p, sh.quant, ts.bm, ts.tn, grid, s);
 }
 

@@ -76,6 +76,9 @@ struct Gemm1Args {
     // written by launch_swiglu_parts
     int ksplit;
     float *gu_part;
+    // tiled kernel, bf16: w13 is stored [K][N] = [d][2f] (N contiguous; the
+    // gate columns 0..f-1, the up columns f..2f-1) instead of [2f][d]
+    bool w_kn;
 };
 
 // Parts the streaming bf16 GEMM1 launches for a requested K split.
@@ -100,6 +103,7 @@ struct Gemm2Args {
     float *yrows;           // tiled kernel: rows [parts][T*k, d] by K part and assignment instead of acc
                             // (sorted_w NULL: unit weights, streaming kernel)
     const uint8_t *h_mx, *w2_mx;   // quant 3: E8M0 scales [P, f/32] and [E, d, f/32]
+    bool w_kn;              // tiled kernel, bf16: w2 stored [K][N] = [f][d] instead of [d][f]
 };
 
 // ---- backward of the bf16 layer (streaming kernel, B = 16 or 32)
