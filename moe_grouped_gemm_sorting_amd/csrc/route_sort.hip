@@ -7,10 +7,17 @@
 // order in which atomics land, so the result is bit-exact and repeatable.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
+
+// workgroups of the sort for large T*k (1 = the single-workgroup sort)
+#ifndef MOE_SORT_MAX_PARTS
+#define MOE_SORT_MAX_PARTS 64
+#endif
 
 // ---------------------------------------------------------------- routing
 // One wave per token; lane l holds the logits of experts l, l + 64, ...
@@ -146,40 +153,71 @@ hipError_t launch_topk(const float *logits, int T, int E, int k, int score, int 
 }
 
 // ------------------------------------------------------------------- sort
-// One workgroup of SORT_WAVES waves. The N = T*k assignments are cut into
-// SORT_WAVES contiguous segments, one per wave, so that "earlier wave" means
-// "smaller assignment index".
-//   1. count: cnt[w][e] = assignments of expert e in wave w's segment
-//      (LDS atomics; counts are order-free);
-//   2. scan: cnt[w][e] becomes the exclusive prefix over waves, the padded
-//      expert sizes are scanned into off[];
+// The N = T*k assignments are cut into `nparts` contiguous chunks, one per
+// workgroup of SORT_WAVES waves, and each chunk into SORT_WAVES contiguous
+// segments, one per wave, so that "earlier wave" (or "earlier workgroup")
+// means "smaller assignment index". No workgroup needs another's results:
+//   1. count: every workgroup counts all N assignments: cnt[w][e] for wave
+//      w's segment of its own chunk, below[e] / after[e] for the
+//      assignments before / after the chunk (LDS atomics; counts are
+//      order-free);
+//   2. scan: the totals give the padded expert sizes, scanned into off[]
+//      (the same in every workgroup), and cnt[w][e] becomes below[e] plus the
+//      exclusive prefix over the chunk's waves;
 //   3. scatter: each wave walks its segment 64 assignments at a time; the
 //      rank of an assignment among equal experts in the chunk comes from a
 //      peer mask built from log2(E) bit-plane ballots;
-//   4. padding slots, the tail and the per-block expert ids are filled.
+//   4. the padding slots of a share of the experts, a share of the tail and
+//      of the per-block expert ids are filled by each workgroup.
+// With one workgroup this is the whole sort in one launch (below = after = 0).
 constexpr int SORT_WAVES = 8;
 constexpr int SORT_THREADS = SORT_WAVES * 64;
 
-__device__ __forceinline__ void sort_block(
+__device__ __forceinline__ void sort_part(
     const int32_t *__restrict__ ids, const float *__restrict__ wts, int N, int E, int B, int P,
-    int NB, int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w,
+    int NB, int part, int nparts, int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w,
     int32_t *__restrict__ seid, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ num_valid) {
     extern __shared__ int lds[];
     int *cnt = lds;                     // [SORT_WAVES][E]
     int *tot = cnt + SORT_WAVES * E;    // [E]
     int *off = tot + E;                 // [E + 1]
+    int *below = off + E + 1;           // [E]
+    int *after = below + E;             // [E]
     __shared__ int wave_sum_lds[SORT_WAVES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < SORT_WAVES * E; i += SORT_THREADS) cnt[i] = 0;
+    for (int i = tid; i < E; i += SORT_THREADS) below[i] = after[i] = 0;
     __syncthreads();
 
-    const int seg = (((N + SORT_WAVES - 1) / SORT_WAVES) + 63) / 64 * 64;
-    const int beg = min(N, wave * seg), end = min(N, beg + seg);
+    // this workgroup's chunk [cbeg, cend) and this wave's segment of it
+    const int chunk = (((N + nparts - 1) / nparts) + 63) / 64 * 64;
+    const int cbeg = min(N, part * chunk), cend = min(N, cbeg + chunk);
+    const int seg = ((((cend - cbeg) + SORT_WAVES - 1) / SORT_WAVES) + 63) / 64 * 64;
+    const int beg = min(cend, cbeg + wave * seg), end = min(cend, beg + seg);
     for (int a = beg + lane; a < end; a += 64) {
         const int e = ids[a];
         if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave * E + e], 1);
+    }
+    if (nparts > 1) {
+        // the assignments outside the chunk, 8 independent loads per thread
+        // ahead of their atomics
+        auto count_range = [&](int lo, int hi, int *h) {
+            for (int a0 = lo + tid; a0 < hi; a0 += 8 * SORT_THREADS) {
+                int e[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int a = a0 + u * SORT_THREADS;
+                    e[u] = a < hi ? ids[a] : -1;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if ((unsigned)e[u] < (unsigned)E) atomicAdd(&h[e[u]], 1);
+            }
+        };
+        count_range(0, cbeg, below);
+        count_range(cend, N, after);
     }
     __syncthreads();
 
@@ -188,14 +226,15 @@ __device__ __forceinline__ void sort_block(
         const int e = base + tid;
         int pad = 0;
         if (e < E) {
-            int t = 0;
+            int t = below[e];
             for (int w = 0; w < SORT_WAVES; ++w) {
                 const int c = cnt[w * E + e];
                 cnt[w * E + e] = t;
                 t += c;
             }
+            t += after[e];
             tot[e] = t;
-            counts[e] = t;
+            if (part == 0) counts[e] = t;
             pad = (t + B - 1) / B * B;
         }
         int incl = pad;
@@ -219,8 +258,10 @@ __device__ __forceinline__ void sort_block(
     if (tid == 0) off[E] = carry;
     __syncthreads();
     const int nv = off[E];
-    for (int e = tid; e <= E; e += SORT_THREADS) offsets[e] = off[e];
-    if (tid == 0) *num_valid = nv;
+    if (part == 0) {
+        for (int e = tid; e <= E; e += SORT_THREADS) offsets[e] = off[e];
+        if (tid == 0) *num_valid = nv;
+    }
 
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const uint64_t lt = lanemask_lt();
@@ -245,16 +286,19 @@ __device__ __forceinline__ void sort_block(
         if (valid && rank == 0) cnt[wave * E + e] = basecnt + __popcll(peers);
     }
 
-    for (int e = tid; e < E; e += SORT_THREADS)
-        for (int i = off[e] + tot[e]; i < off[e + 1]; ++i) {
+    // padding slots of experts part, part + nparts, ...; this part's share
+    // of the tail and of the block expert ids
+    for (int e = part; e < E; e += nparts)
+        for (int i = off[e] + tot[e] + tid; i < off[e + 1]; i += SORT_THREADS) {
             sorted_ids[i] = N;
             sorted_w[i] = 0.0f;
         }
-    for (int i = nv + tid; i < P; i += SORT_THREADS) {
+    const int gtid = part * SORT_THREADS + tid, gstride = nparts * SORT_THREADS;
+    for (int i = nv + gtid; i < P; i += gstride) {
         sorted_ids[i] = N;
         sorted_w[i] = 0.0f;
     }
-    for (int b = tid; b < NB; b += SORT_THREADS) {
+    for (int b = gtid; b < NB; b += gstride) {
         const long slot = (long)b * B;
         int owner = -1;
         if (slot < nv) {
@@ -274,7 +318,8 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(
     int NB, int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w,
     int32_t *__restrict__ seid, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ num_valid) {
-    sort_block(ids, wts, N, E, B, P, NB, sorted_ids, sorted_w, seid, counts, offsets, num_valid);
+    sort_part(ids, wts, N, E, B, P, NB, blockIdx.x, gridDim.x, sorted_ids, sorted_w, seid, counts,
+              offsets, num_valid);
 }
 
 // Routing and sort in one launch (one workgroup): top-k of every token into
@@ -299,8 +344,8 @@ __global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
             topk_wave<PER_LANE == 0 ? 1 : PER_LANE>(logits, t, E, k, score, renorm, ids, wts);
     }
     __syncthreads();
-    sort_block(ids, wts, T * k, E, B, P, NB, sorted_ids, sorted_w, seid, counts, offsets,
-               num_valid);
+    sort_part(ids, wts, T * k, E, B, P, NB, 0, 1, sorted_ids, sorted_w, seid, counts, offsets,
+              num_valid);
 }
 
 hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, int score,
@@ -310,7 +355,7 @@ hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, in
                              int zero_n) {
     const int P = T * k + E * B - k;
     const int NB = (P + B - 1) / B;
-    const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + E + E + 1);
+    const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + 4 * (size_t)E + 1);
 #define MOE_ROUTE_SORT(PL)                                                                    \
     k_route_sort<PL><<<1, SORT_THREADS, lds, s>>>(logits, T, k, E, B, score, renorm, ids, w, P, \
                                                    NB, sorted_ids, sorted_w, sorted_expert_ids, \
@@ -330,9 +375,12 @@ hipError_t launch_sort(const int32_t *ids, const float *w, int T, int k, int E, 
     const int N = T * k;
     const int P = N + E * B - k;
     const int NB = (P + B - 1) / B;
-    const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + E + E + 1);
-    k_sort<<<1, SORT_THREADS, lds, s>>>(ids, w, N, E, B, P, NB, sorted_ids, sorted_w,
-                                        sorted_expert_ids, counts, offsets, num_valid);
+    const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + 4 * (size_t)E + 1);
+    // chunks of at least 512 assignments (one 64-assignment step per wave),
+    // at most 64 workgroups (each counts all N assignments)
+    const int parts = std::max(1, std::min(MOE_SORT_MAX_PARTS, N / 512));
+    k_sort<<<parts, SORT_THREADS, lds, s>>>(ids, w, N, E, B, P, NB, sorted_ids, sorted_w,
+                                            sorted_expert_ids, counts, offsets, num_valid);
     return hipGetLastError();
 }
 

@@ -194,3 +194,21 @@ def test_quant_act_mx_worked_blocks():
         got = np.empty(32, np.uint8)
         got[0::2], got[1::2] = codes[r] & 15, codes[r] >> 4
         assert np.array_equal(got, want), (b["name"], got, want)
+
+
+@pytest.mark.parametrize("N,E,k,B", [(511, 8, 1, 32), (512, 8, 2, 16), (1024, 8, 2, 128), (4095, 256, 5, 16),
+                                     (8192, 8, 2, 256), (32769, 64, 1, 64), (40000, 1024, 8, 32),
+                                     (131072, 8, 2, 256)])
+def test_multi_workgroup_sort_bit_exact(N, E, k, B):
+    """Sorts large enough to run on several workgroups (one per chunk of at
+    least 512 assignments, each counting all assignments to find its place):
+    every output bit-exact against the oracle, chunk sizes ragged and
+    round, skewed and uniform routing."""
+    rng = np.random.default_rng(N + E)
+    T = (N + k - 1) // k
+    p = rng.zipf(1.3, size=E * 4).astype(np.float64)
+    p = np.bincount(rng.integers(0, E, size=E * 4), weights=p, minlength=E)[:E]
+    p = p / p.sum()
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p if E > k else None) for _ in range(T)])
+    w = rng.random((T, k)).astype(np.float32)
+    _assert_sort_equal(ids.astype(np.int32), w, E, B)
