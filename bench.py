@@ -190,8 +190,9 @@ def record_kernel_avg(workload, run_dir):
 def record_mfma_counters(workload, run_dirs):
     """MFMA utilisation of `workload`'s GEMM kernels from rocprofv3 --pmc runs
     (one or more; each counter is averaged over the kernel's dispatches):
-      busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs), the fraction of
-             the kernel's GPU-busy cycles in which the CUs' matrix cores ran;
+      busy = MfmaUtil / 100, rocprofv3's derived metric: the MFMA-busy cycles
+             of all SIMDs (SQ_VALU_MFMA_BUSY_CYCLES) over GRBM_GUI_ACTIVE
+             times the SIMD count;
       counted FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_<type> (MFMA operations,
              padding rows included), per second of kernel time from the
              committed trace average, against the dtype's peak."""
@@ -216,8 +217,8 @@ def record_mfma_counters(workload, run_dirs):
             raise SystemExit(f"{label}: {len(hit)} kernels match")
         c = {n: float(np.mean(v)) for n, v in vals[hit[0]].items()}
         rec = {"kernel": hit[0], "counters_per_dispatch": {n: round(v) for n, v in c.items()}}
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c:
-            rec["mfma_busy_frac"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] * ncu), 4)
+        if "MfmaUtil" in c:   # rocprofv3's derived metric, in percent
+            rec["mfma_busy_frac"] = round(c["MfmaUtil"] / 100.0, 4)
         mops = [v for n, v in c.items() if n.startswith("SQ_INSTS_VALU_MFMA_MOPS")]
         if mops:
             rec["counted_flops"] = 512.0 * sum(mops)
