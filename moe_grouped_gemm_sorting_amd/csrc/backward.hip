@@ -402,41 +402,55 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 // 4j + i / 4 address (j = 0..3): with lane 4j + q pointing at row k0 + j and
 // columns c0 + 4q .. + 3, lane i gets rows k0 .. k0 + 3 of column c0 + i, and
 // two such reads give the 8 consecutive K values of a v_mfma_f32_16x16x32_bf16
-// operand. Tile 128 x 256, waves of 64 x 128 as 4 x 8 accumulators; three
-// 32 KB stages (P_hi, P_lo [32][128], Q [32][256] bf16), the 16-byte chunk c
-// of row r stored at position c ^ 2 (r % 4), so that a transposing read's
-// 16 lanes (4 rows x 2 chunks) meet 8 distinct chunk positions and no bank
-// twice. The DMA wait counts are written out as in the tiled GEMMs.
+// operand. Tile TM x 256 (TM = 128 or 256) with TM / 32 waves of 64 x 128 as
+// 4 x 8 accumulators; three stages of P_hi, P_lo [32][TM] and Q [32][256]
+// bf16 (32 KB for TM = 128, 48 KB for TM = 256), the 16-byte chunk c of row r
+// stored at position c ^ 2 (r % 4), so that a transposing read's 16 lanes
+// (4 rows x 2 chunks) meet 8 distinct chunk positions and no bank twice. The
+// DMA wait counts are written out as in the tiled GEMMs. The 256-row tile
+// moves a quarter fewer operand bytes per MFMA and puts two waves on each
+// SIMD, so one wave's fragment reads overlap the other's MFMAs.
 constexpr int WD_NBUF = 3;
-constexpr int WD_PB = 32 * 256;           // bytes of one P plane per stage
-constexpr int WD_QB = 32 * 512;
-constexpr int WD_STAGE = 2 * WD_PB + WD_QB;   // 32 KB
+constexpr int WD_QB = 32 * 512;           // bytes of the Q plane per stage
+template <int TM>
+struct WdShape {
+    static constexpr int WAVES = TM / 32;
+    static constexpr int PB = 32 * TM * 2;            // bytes of one P plane per stage
+    static constexpr int STAGE = 2 * PB + WD_QB;
+    static constexpr int NP = PB / 1024;              // DMA instructions per P plane
+    static constexpr int NI = STAGE / 1024 / WAVES;   // ... per wave per stage
+    static_assert(STAGE % (1024 * WAVES) == 0, "whole DMA instructions per wave");
+    static_assert(WD_NBUF * STAGE <= 160 * 1024, "LDS");
+};
 
-__global__ __launch_bounds__(256) void k_wgrad_dma(const uint16_t *__restrict__ p_hi,
-                                                   const uint16_t *__restrict__ p_lo,
-                                                   const uint16_t *__restrict__ q, int M, int N,
-                                                   const int32_t *__restrict__ offsets,
-                                                   float *__restrict__ C) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[WD_NBUF * WD_STAGE];
+template <int TM>
+__global__ __launch_bounds__(64 * (TM / 32)) void k_wgrad_dma(const uint16_t *__restrict__ p_hi,
+                                                              const uint16_t *__restrict__ p_lo,
+                                                              const uint16_t *__restrict__ q, int M, int N,
+                                                              const int32_t *__restrict__ offsets,
+                                                              float *__restrict__ C) {
+    using S = WdShape<TM>;
+    constexpr int NI = S::NI, NP = S::NP, PB = S::PB, STAGE = S::STAGE, WAVES = S::WAVES;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[WD_NBUF * STAGE];
     const int e = blockIdx.z;
-    const int m0 = blockIdx.y * 128, n0 = blockIdx.x * 256;
+    const int m0 = blockIdx.y * TM, n0 = blockIdx.x * 256;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int beg = offsets[e];
     const int nch = (offsets[e + 1] - beg) / 32;   // segments are whole 64-row blocks
-    // DMA: instruction i of wave w fills 1 KB (64 chunks) of the stage:
-    // P planes 8 KB each (instructions 0..7 hi, 8..15 lo), Q 16 KB (16..31);
-    // wave w issues instructions w, w + 4, ..., (8 per wave)
-    uint32_t goff[8];
-    const uint16_t *gbase[8];
+    // DMA: instruction i fills 1 KB (64 chunks) of the stage: the P planes
+    // NP KB each (instructions 0 .. NP - 1 hi, NP .. 2 NP - 1 lo), then Q
+    // 16 KB; wave w issues instructions w, w + WAVES, ... (NI per wave)
+    uint32_t goff[NI];
+    const uint16_t *gbase[NI];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int ins = wave + 4 * t;
+    for (int t = 0; t < NI; ++t) {
+        const int ins = wave + WAVES * t;
         int plane, L;
-        if (ins < 16) { plane = ins < 8 ? 0 : 1; L = (ins % 8) * 64 + lane; }
-        else { plane = 2; L = (ins - 16) * 64 + lane; }
-        const int cpr = plane < 2 ? 16 : 32;
+        if (ins < 2 * NP) { plane = ins < NP ? 0 : 1; L = (ins % NP) * 64 + lane; }
+        else { plane = 2; L = (ins - 2 * NP) * 64 + lane; }
+        const int cpr = plane < 2 ? TM / 8 : 32;   // 16-byte chunks per row
         const int r = L / cpr, pos = L % cpr;
         const int c = pos ^ ((r & 3) << 1);
         if (plane < 2) {
@@ -452,11 +466,11 @@ __global__ __launch_bounds__(256) void k_wgrad_dma(const uint16_t *__restrict__ 
         ch = min(ch, nch - 1);
         const size_t row0 = (size_t)beg + (size_t)ch * 32;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int ins = wave + 4 * t;
-            const size_t rowbytes = ins < 16 ? (size_t)M * 2 : (size_t)N * 2;
+        for (int t = 0; t < NI; ++t) {
+            const int ins = wave + WAVES * t;
+            const size_t rowbytes = ins < 2 * NP ? (size_t)M * 2 : (size_t)N * 2;
             const uint8_t *b = reinterpret_cast<const uint8_t *>(gbase[t]) + row0 * rowbytes;
-            wg_dma16(b, goff[t], lds0 + (uint32_t)(buf * WD_STAGE + ins * 1024));
+            wg_dma16(b, goff[t], lds0 + (uint32_t)(buf * STAGE + ins * 1024));
         }
     };
     f32x4 acc[4][8];
@@ -483,14 +497,14 @@ __global__ __launch_bounds__(256) void k_wgrad_dma(const uint16_t *__restrict__ 
         return out;
     };
     auto compute = [&](int buf) {
-        const uint32_t sb = lds0 + (uint32_t)(buf * WD_STAGE);
+        const uint32_t sb = lds0 + (uint32_t)(buf * STAGE);
         u32x4 bq[8];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) bq[b] = frag(sb + 2 * WD_PB, 512, 128 * wn + 16 * b);
+        for (int b = 0; b < 8; ++b) bq[b] = frag(sb + 2 * PB, 512, 128 * wn + 16 * b);
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const u32x4 ah = frag(sb, 256, 64 * wm + 16 * a);
-            const u32x4 al = frag(sb + WD_PB, 256, 64 * wm + 16 * a);
+            const u32x4 ah = frag(sb, 2 * TM, 64 * wm + 16 * a);
+            const u32x4 al = frag(sb + PB, 2 * TM, 64 * wm + 16 * a);
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ah),
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(256) void k_wgrad_dma(const uint16_t *__restrict__ 
     if (nch > 0) {
 #pragma unroll
         for (int b = 0; b < WD_NBUF - 1; ++b) issue(b, b);
-        wg_wait_vmem<8 * (WD_NBUF - 2)>();
+        wg_wait_vmem<NI * (WD_NBUF - 2)>();
         __builtin_amdgcn_s_barrier();
         for (int c0 = 0; c0 < nch; c0 += WD_NBUF) {
             static_for<WD_NBUF>([&](auto ic) {
@@ -514,7 +528,7 @@ __global__ __launch_bounds__(256) void k_wgrad_dma(const uint16_t *__restrict__ 
                 if (c < nch) {
                     issue((r + WD_NBUF - 1) % WD_NBUF, c + WD_NBUF - 1);
                     compute(r);
-                    wg_wait_vmem<8 * (WD_NBUF - 2)>();
+                    wg_wait_vmem<NI * (WD_NBUF - 2)>();
                     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                 }
             });
@@ -540,7 +554,15 @@ hipError_t launch_wgrad_dma(const uint16_t *p_hi, const uint16_t *p_lo, const ui
                             const int32_t *offsets, float *C, hipStream_t s) {
     if (E == 0) return hipSuccess;
     if (M % 128 || N % 256) return hipErrorInvalidValue;
-    k_wgrad_dma<<<dim3(N / 256, M / 128, E), 256, 0, s>>>(p_hi, p_lo, q, M, N, offsets, C);
+    // 256-row tiles where M allows; MOE_WGRAD_TM=128 keeps the 128-row tile
+    static const int tm_env = [] {
+        const char *v = getenv("MOE_WGRAD_TM");
+        return v ? atoi(v) : 0;
+    }();
+    if (M % 256 == 0 && tm_env != 128)
+        k_wgrad_dma<256><<<dim3(N / 256, M / 256, E), 512, 0, s>>>(p_hi, p_lo, q, M, N, offsets, C);
+    else
+        k_wgrad_dma<128><<<dim3(N / 256, M / 128, E), 256, 0, s>>>(p_hi, p_lo, q, M, N, offsets, C);
     return hipGetLastError();
 }
 
