@@ -61,6 +61,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 #ifndef MOE_GROUP_M
@@ -113,6 +114,9 @@ struct TiledParams {
     // written (the backward's recompute of the forward sums, and its
     // v = Wd^T dy with Wd^T split into two halves)
     float *raw_out;
+    // rows of the activation operand a (tokens for GEMM1, sort slots for
+    // GEMM2): the range its buffer descriptor allows
+    uint32_t a_rows;
 };
 
 // Chunk position of (row, chunk) inside the row's 128 bytes (an involution
@@ -143,7 +147,33 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t m
                  : "v"(off), "s"(base), "s"(m0)
                  : "memory", "m0");
 }
+// The same through a buffer descriptor (raw, stride 0): a lane whose offset
+// lies past the descriptor's num_records reads nothing from memory and
+// writes zeros to its 16 LDS bytes, which is how padding rows skip their
+// traffic while every lane still issues the instruction (the wait counts
+// stay fixed).
+__device__ __forceinline__ void dma16_buf(i32x4 rsrc, uint32_t off, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(rsrc), "s"(m0)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Buffer descriptor of n bytes from base: stride 0, no swizzle, the data
+// format the gfx9 family takes for untyped dword loads.
+__device__ __forceinline__ i32x4 buf_rsrc(const void *base, uint32_t n) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)n);
+    r[3] = 0x00020000;
+    return r;
+}
+// offset of a lane that must read nothing (past any num_records: operand
+// matrices are below 4 GiB and whole 128-byte rows)
+constexpr uint32_t DMA_SKIP = 0xFFFFFFF0u;
 
 // Wait until at most N of this wave's vector memory operations are pending
 // (they complete in issue order).
@@ -304,7 +334,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
     for (int i = 0; i < NQA; ++i) {
         const int row = 8 * (wave + WAVES * i) + (lane >> 3);
-        arow_src[i] = GEMM1 ? p.sorted_ids[slot0 + row] : slot0 + row;
+        arow_src[i] = p.sorted_ids[slot0 + row];   // the assignment, or padding (>= sentinel)
     }
     // MXFP4 scale rows: wave w copies tile rows 64 w .. 64 w + 63 (all
     // activation rows or all weight rows, BM being a multiple of 64), lane l
@@ -377,14 +407,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
                       lds_addr(lds) + (uint32_t)(NBUF * BUF + (q & 1) * SSLOT) + (uint32_t)wave * 1024u);
         }
     };
+    const uint32_t abytes = p.a_rows * kbytes;
     auto issue_part = [&](int buf, int kk, int i0, int i1) {
-        const uint8_t *ab = p.a + eb(kk);
+        // activation rows through a descriptor of the bytes from column kk on
+        const uint32_t ak = (uint32_t)eb(kk);
+        const i32x4 ar = buf_rsrc(p.a + ak, abytes - ak);
         // [N][K] weights advance along the row, [K][N] weights by kk rows
         const uint8_t *bb = BT ? wexp + (size_t)kk * Ntot * 2 : wexp + eb(kk);
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
             if (i < i0 || i >= i1) continue;
-            dma16(i < NQA ? ab : bb, goff[i], m0w + (uint32_t)(buf * BUF + i * WAVES * 1024));
+            const uint32_t m0 = m0w + (uint32_t)(buf * BUF + i * WAVES * 1024);
+            if (i < NQA)
+                dma16_buf(ar, goff[i], m0);
+            else
+                dma16(bb, goff[i], m0);
         }
     };
     static_assert(NBUF <= 3, "the first K step's wait count assumes at most 3 stages");
@@ -406,13 +443,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
         for (int b = 0; b < NBUF - 1; ++b) issue_part(b, kof(b), NQA, NQ);
     }
-    // activation rows (the compiler's wait for the sorted ids is here)
+    // activation rows (the compiler's wait for the sorted ids is here);
+    // padding rows read nothing and land as zeros
 #pragma unroll
     for (int i = 0; i < NQA; ++i) {
         const int row = 8 * (wave + WAVES * i) + (lane >> 3);
-        int src = arow_src[i];
-        if constexpr (GEMM1) src = src < sentinel ? src / p.k : 0;
-        goff[i] = (uint32_t)src * kbytes + swz(row, lane & 7) * 16;
+        const int src = GEMM1 ? arow_src[i] / p.k : slot0 + row;
+        goff[i] = arow_src[i] < sentinel ? (uint32_t)src * kbytes + swz(row, lane & 7) * 16 : DMA_SKIP;
     }
     if constexpr (MX) {
         int src = xsrc;
@@ -870,6 +907,7 @@ hipError_t launch_tiled_gemm1(const Gemm1Args &g, int bm, int tn, hipStream_t s)
     p.w_mx = g.w13_mx;
     p.out_mx = g.h_mx;
     p.raw_out = sh.quant == 0 ? g.gu_out : nullptr;
+    p.a_rows = (uint32_t)sh.T;
     const TileShape ts = tile_shape(sh.B, sh.quant, true, bm, tn);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + ts.bm - 1) / ts.bm;
@@ -924,6 +962,7 @@ hipError_t launch_tiled_gemm2(const Gemm2Args &g, int bm, int tn, int ksplit, hi
     const TileShape ts = tile_shape(sh.B, sh.quant, false, bm, tn);
     const int P = sh.T * sh.k + sh.E * sh.B - sh.k;
     const int NB = (P + ts.bm - 1) / ts.bm;
+    p.a_rows = (uint32_t)P;
     const dim3 grid(grid_tiles(NB, sh.d / ts.tn), ksplit);
     if (g.w_kn) {
         if (sh.quant != 0) return hipErrorInvalidValue;
