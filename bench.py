@@ -35,6 +35,7 @@ METRIC = "fused-MoE tokens/s + % HBM BW (decode) / % MFMA peak (prefill), Mixtra
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_AVG_FILE = os.path.join(ROOT, "profiles", "kernel_avg.json")
 MFMA_COUNTERS_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
+XCDS = 8   # accelerator dies of an MI355X, each with its own GRBM counters
 # the prefill layer measured beside a decode workload (same d, f, E, k, quant)
 PREFILL_OF = {"mixtral_decode": "mixtral_prefill", "mixtral_mxfp4": "mixtral_prefill_mxfp4"}
 KERNEL_SOURCES = ["moe_grouped_gemm_sorting_amd/csrc/gemm_stream.hip",
@@ -195,7 +196,12 @@ def record_mfma_counters(workload, run_dirs):
              times the SIMD count;
       counted FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_<type> (MFMA operations,
              padding rows included), per second of kernel time from the
-             committed trace average, against the dtype's peak."""
+             committed trace average, against the dtype's peak;
+      clock = GRBM_GUI_ACTIVE cycles per dispatch (rocprofv3 sums them over
+             the 8 XCDs; GRBM_COUNT reads the same) over 8 times the traced
+             kernel time (when a run collected it): the clock the kernel ran
+             at, and the counted rate against the peak scaled to that clock
+             (the quoted peaks assume 2.4 GHz)."""
     import workloads
     wl = workloads.get(workload)
     B, m1, m2 = _gemm_kernel_matchers(wl)
@@ -226,9 +232,15 @@ def record_mfma_counters(workload, run_dirs):
                 us = kav[label]["avg_us"]
                 rec["counted_TFLOPs"] = round(rec["counted_flops"] / (us * 1e-6) / 1e12, 1)
                 rec["counted_frac_of_peak"] = round(rec["counted_TFLOPs"] / peak, 4)
+        if "GRBM_GUI_ACTIVE" in c and kav.get(label):
+            ghz = c["GRBM_GUI_ACTIVE"] / XCDS / (kav[label]["avg_us"] * 1e3)
+            rec["gui_active_GHz"] = round(ghz, 3)
+            if "counted_TFLOPs" in rec:
+                rec["counted_frac_of_clock_peak"] = round(rec["counted_TFLOPs"] / (peak * ghz / 2.4), 4)
         out[label] = rec
     # the line's roofline object reports GEMM1
-    for k in ("mfma_busy_frac", "counted_flops", "counted_frac_of_peak", "kernel"):
+    for k in ("mfma_busy_frac", "counted_flops", "counted_frac_of_peak", "gui_active_GHz",
+              "counted_frac_of_clock_peak", "kernel"):
         if k in out["gemm1"]:
             out[k] = out["gemm1"][k]
     try:
@@ -417,7 +429,8 @@ def measure_forward(args, wl, x, logits, ws, dev, label):
     counters = committed_record(MFMA_COUNTERS_FILE, wl.name)
     if counters:
         roof["mfma_counters"] = {k: counters[k] for k in ("mfma_busy_frac", "counted_flops",
-                                                            "counted_frac_of_peak", "kernel")
+                                                            "counted_frac_of_peak", "gui_active_GHz",
+                                                            "counted_frac_of_clock_peak", "kernel")
                                  if k in counters}
     layer = {
         "bytes": layer_bytes, "flops": layer_flops,
