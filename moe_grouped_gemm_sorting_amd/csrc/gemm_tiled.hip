@@ -484,10 +484,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[rt][ct][v] = 0.0f;
 
+    // (weight fragments first: a sub-step's first MFMA takes fb[0] and fa[0],
+    // and the activation fragments follow in the order the MFMAs take them)
     auto frags_at = [&](const uint8_t *base, int chunk, u32x4 (&fa)[RT], u32x4 (&fb)[CT]) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            fa[rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB + swz(arow[rt], chunk) * 16);
         if constexpr (BT) {
             // K rows 8 chunk .. 8 chunk + 7 of column brow[ct]: two transposing
             // reads of four K rows each (the lane's 16-lane group starts at
@@ -513,6 +512,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
                 fb[ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
                                                           swz(brow[ct], chunk) * 16);
         }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            fa[rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB + swz(arow[rt], chunk) * 16);
     };
     // bf16: CH/2 sub-steps of K = 16 (lane half lh takes chunk 2s + lh); the
     // fragments of sub-step s+1 are read while the MFMAs of sub-step s run.
@@ -524,6 +526,25 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // 2 (j % 2) + lh of the row's 16 bytes in slot (j / 2) % 2. The even step
     // of a pair reads the rows' 16 bytes whole (a 16-lane group then covers
     // all 64 banks once) and the odd step reuses them.
+    // bf16 and MXFP4: the instruction order of a sub-step that also reads the next
+    // sub-step's fragments: one LDS read after each of the first MFMAs, so
+    // the reads' latency hides behind them. Left to itself the compiler
+    // reuses one set of fragment registers and waits for each read right
+    // before the MFMA that needs it. The pattern applies to the code since
+    // the last sched_barrier, which closes it: MFMAs do not move across
+    // sub-steps, where the same accumulators would form dependent chains.
+    constexpr int NRD = RT + (BT ? 2 : 1) * CT;   // LDS reads of one sub-step's fragments
+    auto interleave = [&]() {
+        constexpr int PAIRS = NRD < RT * CT ? NRD : RT * CT;
+#pragma unroll
+        for (int i = 0; i < PAIRS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, RT * CT - PAIRS, 0);
+        if constexpr (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     u32x4 xs[RT + CT];
     auto compute = [&](int buf, int j, int par) {
         if (!wave_live) return;
@@ -545,6 +566,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
             for (int ct = 0; ct < CT; ++ct) xb[ct] = lh ? xs[RT + ct][2 * par + 1] : xs[RT + ct][2 * par];
             u32x4 fa[2][RT], fb[2][CT];
             frags_at(base, 4 * lh, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
             static_for<4>([&](auto sc) {
                 constexpr int sub = decltype(sc)::value;
                 if constexpr (sub + 1 < 4) frags_at(base, 4 * lh + sub + 1, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
@@ -553,11 +575,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         acc[rt][ct] = mma32_fp4<sub>(fa[sub & 1][rt], fb[sub & 1][ct], xa[rt], xb[ct], acc[rt][ct]);
+                interleave();
             });
         } else if constexpr (QUANT == 0) {
             constexpr int NSUB = CH / 2;
             u32x4 fa[2][RT], fb[2][CT];
             frags_at(base, lh, fa[0], fb[0]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int sub = 0; sub < NSUB; ++sub) {
                 if (sub + 1 < NSUB) frags_at(base, 2 * (sub + 1) + lh, fa[(sub + 1) & 1], fb[(sub + 1) & 1]);
@@ -568,6 +592,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
                     for (int ct = 0; ct < CT; ++ct)
                         acc[rt][ct] = mma32_bf16(fa[sub & 1][rt], fb[sub & 1][ct], acc[rt][ct]);
                 if constexpr (MOE_TILED_PRIO) __builtin_amdgcn_s_setprio(0);
+                interleave();
             }
         } else {
             constexpr int NSUB = CH / 4;
