@@ -2,7 +2,9 @@
 workspace is the library's static per-GPU array) against fused_moe with a
 caller-allocated workspace, through the C ABI: two calls in a row, the
 second on a smaller input, both within the bf16 output tolerance of the
-first entry point's result; and a layer too large for the static array is
+first entry point's result; the same call captured in a HIP graph, whose
+every replay (with other calls on the same static array between replays)
+matches the eager result; and a layer too large for the static array is
 refused before any device work."""
 import os
 import re
@@ -51,6 +53,37 @@ def test_noalloc_matches_fused_moe_on_two_calls(name, B):
         log(f"noalloc {name} T={T} B={B}: err against fused_moe {err:.3e}")
         assert err <= TOL[wl.quant]
         assert torch.isfinite(got.float()).all()
+
+
+@pytest.mark.parametrize("name", ["mixtral_decode", "deepseek_fp8"])
+def test_noalloc_graph_replays_match_eager(name):
+    wl = workloads.get(name)
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    kw = dict(quant=wl.quant, w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"], score=wl.score)
+    ref = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, **kw)
+    # the captured call's inputs and output live in fixed buffers
+    xg, lg = x.clone(), logits.clone()
+    out = torch.empty_like(ref)
+    # an eager call first: it finds the scratch array's address
+    moe.fused_moe_noalloc(xg, ws["w13"], ws["w2"], wl.k, logits=lg, out=out, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.fused_moe_noalloc(xg, ws["w13"], ws["w2"], wl.k, logits=lg, out=out, **kw)
+    torch.cuda.synchronize()
+    other_x = torch.randn_like(x.float()).to(torch.bfloat16)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        err, _ = rel_err(bf16_to_f64(bits(out)), bf16_to_f64(bits(ref)))
+        log(f"graph replay {rep} of {name}: err against eager fused_moe {err:.3e}")
+        assert torch.isfinite(out.float()).all()
+        assert err <= TOL[wl.quant]
+        # eager work between replays, on the same static array
+        moe.fused_moe_noalloc(other_x, ws["w13"], ws["w2"], wl.k, logits=lg, **kw)
+        torch.cuda.synchronize()
 
 
 def test_noalloc_refuses_layers_beyond_its_scratch():
