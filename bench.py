@@ -264,9 +264,11 @@ def backward_block(T, d, f, E, k):
 
 def bench_backward(args, wl, x, logits, ws, dev):
     """K steps of moe_backward on resident inputs (the forward's routing, a
-    random output gradient). Roofline: HBM, counting each touched expert's
-    weights read once, every expert's fp32 weight gradients written once, and
-    x, dy, dx."""
+    random output gradient). Roofline: whichever bound takes longer at its
+    peak: HBM, counting each touched expert's weights read once, every
+    expert's fp32 weight gradients written once, and x, dy, dx; or the bf16
+    MFMAs, counting 16 d f FLOPs per assignment (the weight gradients' hi/lo
+    split not included)."""
     import torch
 
     import moe_grouped_gemm_sorting_amd as moe
@@ -311,6 +313,13 @@ def bench_backward(args, wl, x, logits, ws, dev):
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "the whole backward",
                      "algorithmic_bytes": wbytes, "flops": flops, "touched_experts": touched},
     }
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS["bf16"]
+    if flops / (peak * 1e12) > wbytes / (HBM_PEAK_GBS * 1e9):
+        hbm = {k: result["roofline"][k] for k in ("achieved", "peak", "unit", "frac")}
+        result["roofline"].update({"bound": "mfma", "achieved": round(tflops, 1), "peak": peak,
+                                   "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "hbm": hbm})
+        log(f"[bench] moe_backward: {tflops:.0f} TFLOP/s = {tflops / peak:.3f} of the bf16 MFMA peak")
     print(json.dumps(result), flush=True)
 
 
