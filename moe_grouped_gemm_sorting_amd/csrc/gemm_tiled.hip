@@ -17,10 +17,11 @@
 //
 // Operand staging: gfx950's global_load_lds_dwordx4 moves 16 bytes per lane
 // from global memory straight into LDS (lane l's bytes land at M0 + 16 l), so
-// no registers or LDS-store instructions carry the operands. Three LDS stages
-// (two for 256-row tiles) form a ring: while step j is multiplied out of one
-// stage, the loads of the next steps are in flight into the others, one
-// barrier per step.
+// no registers or LDS-store instructions carry the operands; activation rows
+// go through the buffer form, whose range check lets padding rows read
+// nothing. Three LDS stages (two for 256 x 256 tiles) form a ring: while step
+// j is multiplied out of one stage, the loads of the next steps are in
+// flight into the others, one barrier per step.
 // The loads are issued from inline assembly, with the vmcnt waits written out,
 // because the compiler, which cannot tell the stages apart, would otherwise
 // wait for every outstanding load at each barrier.
