@@ -48,10 +48,16 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the GEMM kernels' code: the sources with comments and
+    whitespace taken out, so that an edit of a comment keeps the records."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, p)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
