@@ -524,9 +524,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // MXFP4: 4 sub-steps of K = 64; lane half lh takes chunk 4 lh + s, i.e.
     // MX block 4 lh + s of the step, so the lane's four E8M0 scales of the
     // step are one dword of the scale row (byte s for sub-step s): dword
-    // 2 (j % 2) + lh of the row's 16 bytes in slot (j / 2) % 2. The even step
-    // of a pair reads the rows' 16 bytes whole (a 16-lane group then covers
-    // all 64 banks once) and the odd step reuses them.
+    // 2 (j % 2) + lh of the row's 16 bytes in slot (j / 2) % 2, read once per
+    // step right after the first sub-step's fragments.
     // bf16 and MXFP4: the instruction order of a sub-step that also reads the next
     // sub-step's fragments: one LDS read after each of the first MFMAs, so
     // the reads' latency hides behind them. Left to itself the compiler
@@ -546,27 +545,21 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
         if constexpr (NRD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PAIRS, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    u32x4 xs[RT + CT];
     auto compute = [&](int buf, int j, int par) {
         if (!wave_live) return;
         const uint8_t *base = lds + buf * BUF;
         if constexpr (MX) {
-            // par: the parity of j (a compile-time constant after unrolling)
-            if (par == 0) {
-                const uint8_t *sb = lds + NBUF * BUF + ((j >> 1) & 1) * SSLOT;
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) xs[rt] = *reinterpret_cast<const u32x4 *>(sb + arow[rt] * 16);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    xs[RT + ct] = *reinterpret_cast<const u32x4 *>(sb + (BM + brow[ct]) * 16);
-            }
-            uint32_t xa[RT], xb[CT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) xa[rt] = lh ? xs[rt][2 * par + 1] : xs[rt][2 * par];
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) xb[ct] = lh ? xs[RT + ct][2 * par + 1] : xs[RT + ct][2 * par];
+            // the first sub-step's fragments, then the step's scale dwords
+            // (dword 2 (j % 2) + lh of each row's 16 bytes in slot (j / 2) % 2),
+            // all in flight together
             u32x4 fa[2][RT], fb[2][CT];
             frags_at(base, 4 * lh, fa[0], fb[0]);
+            const uint8_t *sb = lds + NBUF * BUF + ((j >> 1) & 1) * SSLOT + (2 * (j & 1) + lh) * 4;
+            uint32_t xa[RT], xb[CT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const uint32_t *>(sb + arow[rt] * 16);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) xb[ct] = *reinterpret_cast<const uint32_t *>(sb + (BM + brow[ct]) * 16);
             __builtin_amdgcn_sched_barrier(0);
             static_for<4>([&](auto sc) {
                 constexpr int sub = decltype(sc)::value;
