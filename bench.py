@@ -152,8 +152,8 @@ def _gemm_kernel_matchers(wl):
     B, _, _ = moe.moe_select_config(wl.T, wl.d, wl.f, wl.E, wl.k, wl.quant, cu_count=256)
     q = moe.QUANT[wl.quant]
     if B >= 64:
-        return (B, lambda n: f"k_gemm_tiled<{q}, true," in n,
-                lambda n: f"k_gemm_tiled<{q}, false," in n)
+        return (B, lambda n: f"k_gemm_tiled<{q}, true, {B}," in n,
+                lambda n: f"k_gemm_tiled<{q}, false, {B}," in n)
     return (B, lambda n: f"k_gemm_stream<{q}," in n and "true>" in n,
             lambda n: f"k_gemm_stream<{q}," in n and "false>" in n)
 
