@@ -323,13 +323,14 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
         g.h = h;
         g.h_mx = static_cast<uint8_t *>(h_scale_v);
     } else {
+        // (per-token e4m3: the same launch clears the row amax of h, which
+        // GEMM1 takes with atomics)
         HIP_TRY(launch_quant_act(static_cast<const uint16_t *>(x), T, d, quant == 1 ? d : 128, w.qx,
-                                 w.sx, s),
+                                 w.sx, s, quant == 1 ? w.amax : nullptr, quant == 1 ? (int)P : 0),
                 "activation quantisation launch");
         g.a = w.qx;
         g.a_scale = w.sx;
         if (quant == 1) {
-            HIP_TRY(launch_fill_f32(w.amax, P, 0.0f, s), "fill launch");
             g.h = w.hb;
             g.h_scale = w.amax;
         } else {

@@ -26,9 +26,10 @@ hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, in
 hipError_t launch_quant_mx(const uint16_t *x, int rows, int cols, uint8_t *codes, uint8_t *scales,
                            hipStream_t s);
 
-// codes [rows, cols], scales [rows, cols / group]
+// codes [rows, cols], scales [rows, cols / group]; zero[0, zero_n), when
+// given, is cleared in the same launch
 hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, uint8_t *codes,
-                            float *scales, hipStream_t s);
+                            float *scales, hipStream_t s, float *zero = nullptr, int zero_n = 0);
 
 // h rows: bf16 [rows, cols] with row amax [rows] -> e4m3 codes + scale [rows]
 hipError_t launch_quant_h_rows(const uint16_t *h, const float *amax, int rows, int cols,

@@ -14,10 +14,12 @@
 namespace moe {
 
 // One workgroup of 256 threads per row. Thread t owns the 8-element chunks
-// t, t + 256, ... (16-byte loads). GROUP_ROW: one scale for the whole row;
-// otherwise one scale per 128 columns (16 consecutive chunks = 16 lanes).
-// With num_valid (rows of h by sort slot), rows at or past num_valid and
-// rows of padding slots (sorted_ids[r] == sentinel) are skipped.
+// t, t + 256, ... (16-byte loads, QU of them in flight). GROUP_ROW: one
+// scale for the whole row; otherwise one scale per 128 columns (16
+// consecutive chunks = 16 lanes). With num_valid (rows of h by sort slot),
+// rows at or past num_valid and rows of padding slots (sorted_ids[r] ==
+// sentinel) are skipped. zero[0, zero_n), when given, is cleared on the way
+// (the row amax that the e4m3 GEMM1 which follows takes with atomics).
 template <bool GROUP_ROW>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t *__restrict__ x,
                                                     const float *__restrict__ row_amax,
@@ -25,7 +27,9 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t *__restrict__
                                                     const int32_t *__restrict__ sorted_ids,
                                                     int sentinel, int cols,
                                                     uint8_t *__restrict__ codes,
-                                                    float *__restrict__ scales) {
+                                                    float *__restrict__ scales,
+                                                    float *__restrict__ zero, int zero_n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < zero_n; i += gridDim.x * 256) zero[i] = 0.0f;
     const int r = blockIdx.x;
     if (num_valid && r >= *num_valid) return;
     if (sorted_ids && sorted_ids[r] >= sentinel) return;
@@ -59,40 +63,45 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t *__restrict__
         s_row = amax == 0.0f ? 1.0f : amax / 448.0f;
         if (tid == 0) scales[r] = s_row;
     }
-    // chunk loop; for the 1x128 grouping all 16 lanes of a group are in the
-    // same iteration because 256 is a multiple of 16.
-    for (int c0 = 0; c0 < nchunk; c0 += 256) {
-        const int c = c0 + tid;
-        const bool live = c < nchunk;
-        float v[8];
-        if (live) {
-            const uint4 q = src[c];
-            const uint32_t wds[4] = {q.x, q.y, q.z, q.w};
+    // chunk loop, QU chunks per thread per pass with their loads issued
+    // first; for the 1x128 grouping all 16 lanes of a group are in the same
+    // pass because 256 is a multiple of 16.
+    constexpr int QU = 4;
+    for (int c0 = 0; c0 < nchunk; c0 += QU * 256) {
+        uint4 q[QU];
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+            const int c = c0 + u * 256 + tid;
+            q[u] = c < nchunk ? src[c] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+            const int c = c0 + u * 256 + tid;
+            const bool live = c < nchunk;
+            float v[8];
+            const uint32_t wds[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 v[2 * i] = bf16_bits_to_f32(wds[i] & 0xffffu);
                 v[2 * i + 1] = bf16_bits_to_f32(wds[i] >> 16);
             }
-        } else {
+            float s = s_row;
+            if (!GROUP_ROW) {
+                float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-        }
-        float s = s_row;
-        if (!GROUP_ROW) {
-            float m = 0.0f;
+                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
 #pragma unroll
-            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-#pragma unroll
-            for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-            s = m == 0.0f ? 1.0f : m / 448.0f;
-            if (live && (c & 15) == 0) scales[(size_t)r * (cols / 128) + c / 16] = s;
-        }
-        if (live) {
-            uint32_t lo = f32x2_to_e4m3x2(v[0] / s, v[1] / s) |
-                          (f32x2_to_e4m3x2(v[2] / s, v[3] / s) << 16);
-            uint32_t hi = f32x2_to_e4m3x2(v[4] / s, v[5] / s) |
-                          (f32x2_to_e4m3x2(v[6] / s, v[7] / s) << 16);
-            dst[c] = make_uint2(lo, hi);
+                for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                s = m == 0.0f ? 1.0f : m / 448.0f;
+                if (live && (c & 15) == 0) scales[(size_t)r * (cols / 128) + c / 16] = s;
+            }
+            if (live) {
+                uint32_t lo = f32x2_to_e4m3x2(v[0] / s, v[1] / s) |
+                              (f32x2_to_e4m3x2(v[2] / s, v[3] / s) << 16);
+                uint32_t hi = f32x2_to_e4m3x2(v[4] / s, v[5] / s) |
+                              (f32x2_to_e4m3x2(v[6] / s, v[7] / s) << 16);
+                dst[c] = make_uint2(lo, hi);
+            }
         }
     }
 }
@@ -143,12 +152,14 @@ hipError_t launch_quant_mx(const uint16_t *x, int rows, int cols, uint8_t *codes
 }
 
 hipError_t launch_quant_act(const uint16_t *x, int rows, int cols, int group, uint8_t *codes,
-                            float *scales, hipStream_t s) {
-    if (rows == 0) return hipSuccess;
+                            float *scales, hipStream_t s, float *zero, int zero_n) {
+    if (rows == 0) return zero_n > 0 ? launch_fill_f32(zero, (size_t)zero_n, 0.0f, s) : hipSuccess;
     if (group == cols)
-        k_quant_rows<true><<<rows, 256, 0, s>>>(x, nullptr, nullptr, nullptr, 0, cols, codes, scales);
+        k_quant_rows<true><<<rows, 256, 0, s>>>(x, nullptr, nullptr, nullptr, 0, cols, codes, scales,
+                                                zero, zero_n);
     else
-        k_quant_rows<false><<<rows, 256, 0, s>>>(x, nullptr, nullptr, nullptr, 0, cols, codes, scales);
+        k_quant_rows<false><<<rows, 256, 0, s>>>(x, nullptr, nullptr, nullptr, 0, cols, codes, scales,
+                                                 zero, zero_n);
     return hipGetLastError();
 }
 
@@ -157,7 +168,7 @@ hipError_t launch_quant_h_rows(const uint16_t *h, const float *amax, int rows, i
                                int sentinel, uint8_t *codes, float *scales, hipStream_t s) {
     if (rows == 0) return hipSuccess;
     k_quant_rows<true><<<rows, 256, 0, s>>>(h, amax, num_valid, sorted_ids, sentinel, cols, codes,
-                                            scales);
+                                            scales, nullptr, 0);
     return hipGetLastError();
 }
 

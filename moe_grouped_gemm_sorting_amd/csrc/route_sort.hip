@@ -286,30 +286,34 @@ __device__ __forceinline__ void sort_part(
         if (valid && rank == 0) cnt[wave * E + e] = basecnt + __popcll(peers);
     }
 
-    // padding slots of experts part, part + nparts, ...; this part's share
-    // of the tail and of the block expert ids
-    for (int e = part; e < E; e += nparts)
-        for (int i = off[e] + tot[e] + tid; i < off[e + 1]; i += SORT_THREADS) {
+    // this part's share of the slots: the padding at the end of each
+    // expert's segment, the tail after the last segment, and the per-block
+    // expert ids. A slot's expert is the last e with off[e] <= slot (a
+    // binary search over off[], so the work spreads over every thread
+    // whatever E is).
+    auto owner_of = [&](int slot) {
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= slot) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    };
+    const int gtid = part * SORT_THREADS + tid, gstride = nparts * SORT_THREADS;
+    for (int i = gtid; i < P; i += gstride) {
+        bool pad = i >= nv;
+        if (!pad) {
+            const int e = owner_of(i);
+            pad = i >= off[e] + tot[e];
+        }
+        if (pad) {
             sorted_ids[i] = N;
             sorted_w[i] = 0.0f;
         }
-    const int gtid = part * SORT_THREADS + tid, gstride = nparts * SORT_THREADS;
-    for (int i = nv + gtid; i < P; i += gstride) {
-        sorted_ids[i] = N;
-        sorted_w[i] = 0.0f;
     }
     for (int b = gtid; b < NB; b += gstride) {
-        const long slot = (long)b * B;
-        int owner = -1;
-        if (slot < nv) {
-            int lo = 0, hi = E - 1;  // last e with off[e] <= slot
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (off[mid] <= slot) lo = mid; else hi = mid - 1;
-            }
-            owner = lo;
-        }
-        seid[b] = owner;
+        const int slot = b * B;
+        seid[b] = slot < nv ? owner_of(slot) : -1;
     }
 }
 
