@@ -47,6 +47,20 @@ __device__ __forceinline__ uint32_t e2m1_code(float r) {
     return m | ((__float_as_uint(r) >> 28) & 8u);
 }
 
+// Eight E2M1 codes packed in a dword (v[i] in nibble i) by gfx950's
+// v_cvt_scalef32_pk_fp4_f32 at unit scale, two values per instruction. It
+// rounds exactly as e2m1_code (checked on the GPU against it for every
+// threshold and its neighbouring floats, denormals, signed zeros and values
+// past 6, in each byte position).
+__device__ __forceinline__ uint32_t e2m1_pack8(const float *v) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+    return w;
+}
+
 // Shared exponent of an MXFP4 block from its amax: floor(log2(amax)) - 2,
 // clamped to [-127, 127] (-127 for zero or subnormal amax), read off the
 // fp32 exponent field. Returns E; the E8M0 code is E + 127.

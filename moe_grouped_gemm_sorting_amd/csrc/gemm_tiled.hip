@@ -748,10 +748,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
                 uint32_t cw[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    uint32_t wv = 0;
+                    float sv[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) wv |= e2m1_code(v[8 * c + i] * inv) << (4 * i);
-                    cw[c] = wv;
+                    for (int i = 0; i < 8; ++i) sv[i] = v[8 * c + i] * inv;
+                    cw[c] = e2m1_pack8(sv);
                 }
                 const size_t slot = (size_t)slot0 + row;
                 const int col0 = nt * (TN / 2) + bk * 32;

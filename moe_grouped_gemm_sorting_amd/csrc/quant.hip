@@ -134,10 +134,10 @@ __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t *__restrict__ x
     uint32_t out[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        uint32_t word = 0;
+        float sv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) word |= e2m1_code(v[8 * j + i] * inv) << (4 * i);
-        out[j] = word;
+        for (int i = 0; i < 8; ++i) sv[i] = v[8 * j + i] * inv;
+        out[j] = e2m1_pack8(sv);
     }
     *reinterpret_cast<uint4 *>(codes + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
     scales[b] = (uint8_t)(E + 127);
