@@ -549,17 +549,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
         if (!wave_live) return;
         const uint8_t *base = lds + buf * BUF;
         if constexpr (MX) {
-            // the first sub-step's fragments, then the step's scale dwords
+            // the first sub-step's fragments and the step's scale dwords
             // (dword 2 (j % 2) + lh of each row's 16 bytes in slot (j / 2) % 2),
-            // all in flight together
+            // all in flight together, in the order the first MFMAs take them
+            // (weight column tile 0 and its scale, activation row tile 0 and
+            // its scale, then the others: the first MFMA waits for four reads)
             u32x4 fa[2][RT], fb[2][CT];
-            frags_at(base, 4 * lh, fa[0], fb[0]);
             const uint8_t *sb = lds + NBUF * BUF + ((j >> 1) & 1) * SSLOT + (2 * (j & 1) + lh) * 4;
             uint32_t xa[RT], xb[CT];
+            auto read_a = [&](int rt) {
+                fa[0][rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB + swz(arow[rt], 4 * lh) * 16);
+                xa[rt] = *reinterpret_cast<const uint32_t *>(sb + arow[rt] * 16);
+            };
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) xa[rt] = *reinterpret_cast<const uint32_t *>(sb + arow[rt] * 16);
+            for (int ct = 0; ct < CT; ++ct) {
+                fb[0][ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
+                                                             swz(brow[ct], 4 * lh) * 16);
+                xb[ct] = *reinterpret_cast<const uint32_t *>(sb + (BM + brow[ct]) * 16);
+                if (ct == 0) read_a(0);
+            }
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) xb[ct] = *reinterpret_cast<const uint32_t *>(sb + (BM + brow[ct]) * 16);
+            for (int rt = 1; rt < RT; ++rt) read_a(rt);
             __builtin_amdgcn_sched_barrier(0);
             static_for<4>([&](auto sc) {
                 constexpr int sub = decltype(sc)::value;
@@ -591,19 +601,50 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
         } else {
             constexpr int NSUB = CH / 4;
             u32x4 fa[NSUB][2][RT], fb[NSUB][2][CT];
+            // one sub-step's fragments (two chunks per row tile) in the order
+            // its MFMAs take them: weight column tile 0, activation row tile
+            // 0, then the others
+            auto read_sub = [&](int sub) {
+                const int c0 = 4 * sub + 2 * lh;
+                auto read_a = [&](int rt) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        fa[sub][h][rt] = *reinterpret_cast<const u32x4 *>(base + arow[rt] * ROWB +
+                                                                          swz(arow[rt], c0 + h) * 16);
+                };
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        fb[sub][h][ct] = *reinterpret_cast<const u32x4 *>(base + (BM + brow[ct]) * ROWB +
+                                                                          swz(brow[ct], c0 + h) * 16);
+                    if (ct == 0) read_a(0);
+                }
+#pragma unroll
+                for (int rt = 1; rt < RT; ++rt) read_a(rt);
+            };
+            // the next sub-step's reads go out between this one's MFMAs
+            read_sub(0);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int sub = 0; sub < NSUB; ++sub) {
-                frags_at(base, 4 * sub + 2 * lh, fa[sub][0], fb[sub][0]);
-                frags_at(base, 4 * sub + 2 * lh + 1, fa[sub][1], fb[sub][1]);
-            }
-#pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub)
+                if (sub + 1 < NSUB) read_sub(sub + 1);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         acc[rt][ct] = mma32_fp8(fa[sub][0][rt], fa[sub][1][rt], fb[sub][0][ct],
                                                 fb[sub][1][ct], acc[rt][ct]);
+                if (sub + 1 < NSUB) {
+                    constexpr int NR = 2 * (RT + CT), NM = RT * CT;
+#pragma unroll
+                    for (int i = 0; i < NM; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, NR / NM, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
