@@ -520,12 +520,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_tiled(TiledParams p) {
     // bf16: CH/2 sub-steps of K = 16 (lane half lh takes chunk 2s + lh); the
     // fragments of sub-step s+1 are read while the MFMAs of sub-step s run.
     // e4m3: CH/4 sub-steps of K = 64 (lane half lh takes chunks 4s + 2lh and
-    // 4s + 2lh + 1), all fragments read up front.
+    // 4s + 2lh + 1); the second sub-step's fragments are read between the
+    // first one's MFMAs (two reads after each).
     // MXFP4: 4 sub-steps of K = 64; lane half lh takes chunk 4 lh + s, i.e.
     // MX block 4 lh + s of the step, so the lane's four E8M0 scales of the
     // step are one dword of the scale row (byte s for sub-step s): dword
     // 2 (j % 2) + lh of the row's 16 bytes in slot (j / 2) % 2, read once per
-    // step right after the first sub-step's fragments.
+    // step together with the first sub-step's fragments.
     // bf16 and MXFP4: the instruction order of a sub-step that also reads the next
     // sub-step's fragments: one LDS read after each of the first MFMAs, so
     // the reads' latency hides behind them. Left to itself the compiler
