@@ -92,6 +92,23 @@ def test_sort_edge_cases():
     _assert_sort_equal(ids, rng.random((8192, 8)).astype(np.float32), 1024, 128)
 
 
+def test_sort_at_the_largest_accepted_size():
+    """T*k = 2^24 assignments, the most the library accepts (64 workgroups,
+    each counting all 16.8 M of them): every output bit-exact against the
+    oracle and repeatable; one assignment more is refused before any device
+    work."""
+    rng = np.random.default_rng(24)
+    T, k, E, B = 1 << 23, 2, 8, 256
+    first = rng.integers(0, E, size=T)
+    ids = np.stack([first, (first + 1 + rng.integers(0, E - 1, size=T)) % E], axis=1).astype(np.int32)
+    w = rng.random((T, k), dtype=np.float32)
+    log(f"sort of {T * k} assignments, E={E} B={B}")
+    _assert_sort_equal(ids, w, E, B)
+    over = torch.zeros(((1 << 24) + 1, 1), dtype=torch.int32, device=DEV)
+    with pytest.raises(moe.MoeError, match="2\\^24"):
+        moe.moe_sort(over, torch.ones(over.shape, dtype=torch.float32, device=DEV), E, B)
+
+
 @pytest.mark.parametrize("rows,cols,group", [(1, 128, 128), (3, 256, 256), (17, 4096, 4096),
                                              (128, 7168, 128), (5, 384, 128), (64, 2048, 2048)])
 def test_quant_act_bit_exact(rows, cols, group):
