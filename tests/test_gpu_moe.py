@@ -130,6 +130,32 @@ def test_fused_full_size_all_tokens(name):
     assert err <= TOL[wl.quant]
 
 
+def test_fused_at_the_largest_accepted_T():
+    """The Mixtral-shaped bf16 layer at T = 73728, close to the largest T
+    whose activation buffers stay below 2^31 elements with 256-row blocks
+    ((T k + E B) f < 2^31: T <= 73874), against the oracle on tokens spread
+    over the batch (the first and the last among them); T = 73875 is refused
+    before any device work."""
+    wl = workloads.get("mixtral_prefill").replace(T=73728, seed=77)
+    log(f"largest-T parity: T={wl.T} (generating inputs)")
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, score=wl.score, B=256)
+    torch.cuda.synchronize()
+    tokens = np.unique(np.concatenate([[0, wl.T - 1],
+                                       np.random.default_rng(5).integers(0, wl.T, size=30)]))
+    ref, _, _ = oracle_layer(wl, x, logits, ws, tokens=tokens)
+    got = bf16_to_f64(bits(out))[tokens]
+    err, norm = rel_err(got, ref)
+    log(f"  {len(tokens)} tokens: err={err:.3e} norm={norm:.3e}")
+    assert err <= TOL["bf16"]
+    del out
+    x_over = torch.zeros(wl.T + 147, wl.d, dtype=torch.bfloat16, device=DEV)
+    l_over = torch.zeros(wl.T + 147, wl.E, dtype=torch.float32, device=DEV)
+    with pytest.raises(moe.MoeError, match="2\\^31"):
+        moe.fused_moe(x_over, ws["w13"], ws["w2"], wl.k, logits=l_over, B=256)
+
+
 ONE_STAGE = [w for w in SMALL if w.quant == "bf16"] + [
     workloads.Workload("decode_t1", T=1, d=4096, f=14336, E=8, k=2, seed=31),
     workloads.Workload("decode_t4", T=4, d=4096, f=14336, E=8, k=2, seed=32),
