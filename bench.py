@@ -12,6 +12,8 @@ bf16). One JSON line goes to stdout. Besides the standard fields it reports:
                 algorithmic bytes (or FLOPs) per launch over its mean duration,
                 timed with HIP events on the stream it runs on;
   layer         the whole layer against the HBM and MFMA rooflines;
+  ms_per_call   median, minimum and maximum of K calls timed one by one
+                with HIP events (after the timed region);
   stages        mean per-stage times of the same path;
   cpu_baseline  the CPU oracle on the host cores, on a bounded token sample.
 """
@@ -363,8 +365,21 @@ def measure_forward(args, wl, x, logits, ws, dev, label):
     ms = wall * 1e3 / args.steps
     log(f"[bench] {label} fused_moe: {ms * 1e3:.1f} us/step, {wl.T / (ms / 1e3):,.0f} tokens/s")
 
-    # ---- per-stage timing with HIP events on the library's stream -----------
+    # ---- each call on its own, HIP events on the library's stream: median,
+    # minimum and maximum of K calls (outside the timed region) -------------
     stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    calls = np.array([a.elapsed_time(b) for a, b in evs])
+    per_call = {"median": round(float(np.median(calls)), 4), "min": round(float(calls.min()), 4),
+                "max": round(float(calls.max()), 4)}
+
+    # ---- per-stage timing with HIP events on the library's stream -----------
     ids, w = moe.moe_topk(logits, wl.k, wl.score)
     srt = moe.moe_sort(ids, w, wl.E, B)
     h, hs = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, B, wl.quant, ws["w13_scale"])
@@ -454,7 +469,8 @@ def measure_forward(args, wl, x, logits, ws, dev, label):
         "TFLOPs": round(layer_flops / (ms * 1e-3) / 1e12, 2),
         "mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[wl.quant], 4),
     }
-    return dict(ms=ms, B=B, stage=stage, ksplit=ksplit, stages=stages, roof=roof, layer=layer)
+    return dict(ms=ms, B=B, stage=stage, ksplit=ksplit, stages=stages, roof=roof, layer=layer,
+                per_call=per_call)
 
 
 def committed_record(path, workload):
@@ -594,7 +610,8 @@ def main():
         pm = measure_forward(args, pw, px, plog, ws, dev, pw.name)
         prefill = {"workload": pw.name, "T": pw.T, "weights": f"those of {wl.name}",
                    "value": round(pw.T / (pm["ms"] / 1e3), 1), "unit": "tokens/s",
-                   "ms_per_step": round(pm["ms"], 4), "B": pm["B"], "stage": pm["stage"],
+                   "ms_per_step": round(pm["ms"], 4), "ms_per_call": pm["per_call"],
+                   "B": pm["B"], "stage": pm["stage"],
                    "ksplit": pm["ksplit"], "roofline": pm["roof"], "layer": pm["layer"],
                    "stages_us": {k: round(v, 2) for k, v in pm["stages"].items()}}
         del px, plog
@@ -603,6 +620,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "ms_per_call": m["per_call"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "mxfp4": "mxfp4_e2m1"}.get(wl.quant, "fp8_e4m3"), "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "f": wl.f, "E": wl.E, "k": wl.k,
