@@ -11,6 +11,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "moe.h"
 
 namespace moe {
 
@@ -96,43 +97,59 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     topk_wave<PER_LANE>(logits, t, E, k, score, renorm, ids, w);
 }
 
-// One thread per token, for E <= 64: the same selection and scores, with
-// every sum taken in ascending expert / selection order.
+// One thread per token, for E <= EMAX <= 64: the same selection and scores,
+// with every sum taken in ascending expert / selection order. The row's
+// logits are loaded into registers up front (independent loads, one round
+// trip), and the selected logits and scores stay in registers.
+template <int EMAX>
 __device__ __forceinline__ void topk_thread(const float *__restrict__ logits, int t, int E, int k,
                                             int score, int renorm, int32_t *__restrict__ ids,
                                             float *__restrict__ w) {
     const float *row = logits + (size_t)t * E;
+    float v[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) v[e] = e < E ? row[e] : 0.0f;
     uint64_t taken = 0;
     float top = 0.0f;
-    for (int j = 0; j < k; ++j) {
+    float sel[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (j >= k) break;
         int best = -1;
         float bv = 0.0f;
-        for (int e = 0; e < E; ++e) {
-            const float v = row[e];
-            if (!((taken >> e) & 1ull) && (best < 0 || v > bv)) {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) {
+            if (e < E && !((taken >> e) & 1ull) && (best < 0 || v[e] > bv)) {
                 best = e;
-                bv = v;
+                bv = v[e];
             }
         }
         taken |= 1ull << best;
         if (j == 0) top = bv;
         ids[(size_t)t * k + j] = best;
-        w[(size_t)t * k + j] = bv;  // raw logit for now
+        sel[j] = bv;   // raw logit for now
     }
     float den = 1.0f;
     if (score == 0) {
         den = 0.0f;
-        for (int e = 0; e < E; ++e) den += expf(row[e] - top);
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+            if (e < E) den += expf(v[e] - top);
     }
     float sum = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const float l = w[(size_t)t * k + j];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (j >= k) break;
+        const float l = sel[j];
         const float p = score == 0 ? expf(l - top) / den : 1.0f / (1.0f + expf(-l));
-        w[(size_t)t * k + j] = p;
+        sel[j] = p;
         sum += p;
     }
-    if (renorm)
-        for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = w[(size_t)t * k + j] / sum;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (j >= k) break;
+        w[(size_t)t * k + j] = renorm ? sel[j] / sum : sel[j];
+    }
 }
 
 hipError_t launch_topk(const float *logits, int T, int E, int k, int score, int renorm,
@@ -340,12 +357,13 @@ __global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
     if (zero)
         for (int i = threadIdx.x; i < zero_n / 4; i += SORT_THREADS)
             reinterpret_cast<float4 *>(zero)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (PER_LANE == 0) {
+    if constexpr (PER_LANE <= 0) {
+        // one thread per token, E <= -PER_LANE
         for (int t = threadIdx.x; t < T; t += SORT_THREADS)
-            topk_thread(logits, t, E, k, score, renorm, ids, wts);
+            topk_thread<PER_LANE < 0 ? -PER_LANE : 1>(logits, t, E, k, score, renorm, ids, wts);
     } else {
         for (int t = threadIdx.x >> 6; t < T; t += SORT_WAVES)
-            topk_wave<PER_LANE == 0 ? 1 : PER_LANE>(logits, t, E, k, score, renorm, ids, wts);
+            topk_wave<PER_LANE <= 0 ? 1 : PER_LANE>(logits, t, E, k, score, renorm, ids, wts);
     }
     __syncthreads();
     sort_part(ids, wts, T * k, E, B, P, NB, 0, 1, sorted_ids, sorted_w, seid, counts, offsets,
@@ -364,7 +382,10 @@ hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, in
     k_route_sort<PL><<<1, SORT_THREADS, lds, s>>>(logits, T, k, E, B, score, renorm, ids, w, P, \
                                                    NB, sorted_ids, sorted_w, sorted_expert_ids, \
                                                    counts, offsets, num_valid, zero, zero_n)
-    if (E <= 64) MOE_ROUTE_SORT(0);
+    if (E <= 8) MOE_ROUTE_SORT(-8);
+    else if (E <= 16) MOE_ROUTE_SORT(-16);
+    else if (E <= 32) MOE_ROUTE_SORT(-32);
+    else if (E <= 64) MOE_ROUTE_SORT(-64);
     else if (E <= 128) MOE_ROUTE_SORT(2);
     else if (E <= 256) MOE_ROUTE_SORT(4);
     else if (E <= 512) MOE_ROUTE_SORT(8);
