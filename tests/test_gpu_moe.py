@@ -156,6 +156,38 @@ def test_fused_at_the_largest_accepted_T():
         moe.fused_moe(x_over, ws["w13"], ws["w2"], wl.k, logits=l_over, B=256)
 
 
+def test_streaming_gemm2_on_reused_and_dirty_workspaces():
+    """The streaming path with atomics into the fp32 accumulator: three fused
+    calls on one workspace filled with 0xFF bytes first, and the two-stage
+    entry point on such a workspace (the library clears what it adds into),
+    each against the oracle, at two token counts."""
+    for T in (32, 513):
+        wl = workloads.Workload(f"fin{T}", T=T, d=512, f=1024, E=8, k=2, seed=90 + T)
+        x, logits = wl.activations(DEV)
+        ws = wl.weights(DEV)
+        ref, ids, w = oracle_layer(wl, x, logits, ws)
+        B = 16
+        nbytes = moe.fused_moe_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, "bf16", B, 2)
+        work = torch.full((nbytes,), 255, dtype=torch.uint8, device=DEV)
+        for call in range(3):
+            out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, B=B, stage=2, ksplit=2,
+                                workspace=work)
+            torch.cuda.synchronize()
+            err, _ = rel_err(bf16_to_f64(bits(out)), ref)
+            log(f"streaming GEMM2 T={T} call {call}: err={err:.3e}")
+            assert err <= TOL["bf16"], (T, call, err)
+        tid, tw = moe.moe_topk(logits, wl.k)
+        srt = moe.moe_sort(tid, tw, wl.E, B)
+        h, hs = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, B)
+        n2 = moe.moe_gemm2_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, B, "bf16")
+        dirty = torch.full((n2,), 255, dtype=torch.uint8, device=DEV)
+        out2 = moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B, ksplit=2, workspace=dirty)
+        torch.cuda.synchronize()
+        err, _ = rel_err(bf16_to_f64(bits(out2)), ref)
+        log(f"two-stage GEMM2 T={T} on a dirty workspace: err={err:.3e}")
+        assert err <= TOL["bf16"], (T, err)
+
+
 ONE_STAGE = [w for w in SMALL if w.quant == "bf16"] + [
     workloads.Workload("decode_t1", T=1, d=4096, f=14336, E=8, k=2, seed=31),
     workloads.Workload("decode_t4", T=4, d=4096, f=14336, E=8, k=2, seed=32),
