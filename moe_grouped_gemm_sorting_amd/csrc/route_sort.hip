@@ -346,6 +346,7 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(
 // Routing and sort in one launch (one workgroup): top-k of every token into
 // ids / w, a workgroup barrier (which also orders the global writes for the
 // workgroup), then the sort.
+constexpr int ROUTE_SORT_MAX_N = 512;   // assignments T * k of the one-workgroup form
 template <int PER_LANE>
 __global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
     const float *__restrict__ logits, int T, int k, int E, int B, int score, int renorm,
@@ -357,16 +358,25 @@ __global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
     if (zero)
         for (int i = threadIdx.x; i < zero_n / 4; i += SORT_THREADS)
             reinterpret_cast<float4 *>(zero)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    // the selections go to LDS, where the sort reads them, and are copied
+    // out to ids / wts afterwards (T * k <= ROUTE_SORT_MAX_N, checked by the
+    // launcher)
+    __shared__ int32_t s_ids[ROUTE_SORT_MAX_N];
+    __shared__ float s_w[ROUTE_SORT_MAX_N];
     if constexpr (PER_LANE <= 0) {
         // one thread per token, E <= -PER_LANE
         for (int t = threadIdx.x; t < T; t += SORT_THREADS)
-            topk_thread<PER_LANE < 0 ? -PER_LANE : 1>(logits, t, E, k, score, renorm, ids, wts);
+            topk_thread<PER_LANE < 0 ? -PER_LANE : 1>(logits, t, E, k, score, renorm, s_ids, s_w);
     } else {
         for (int t = threadIdx.x >> 6; t < T; t += SORT_WAVES)
-            topk_wave<PER_LANE <= 0 ? 1 : PER_LANE>(logits, t, E, k, score, renorm, ids, wts);
+            topk_wave<PER_LANE <= 0 ? 1 : PER_LANE>(logits, t, E, k, score, renorm, s_ids, s_w);
     }
     __syncthreads();
-    sort_part(ids, wts, T * k, E, B, P, NB, 0, 1, sorted_ids, sorted_w, seid, counts, offsets,
+    for (int i = threadIdx.x; i < T * k; i += SORT_THREADS) {
+        ids[i] = s_ids[i];
+        wts[i] = s_w[i];
+    }
+    sort_part(s_ids, s_w, T * k, E, B, P, NB, 0, 1, sorted_ids, sorted_w, seid, counts, offsets,
               num_valid);
 }
 
@@ -375,6 +385,7 @@ hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, in
                              float *sorted_w, int32_t *sorted_expert_ids, int32_t *counts,
                              int32_t *offsets, int32_t *num_valid, hipStream_t s, float *zero,
                              int zero_n) {
+    if ((int64_t)T * k > ROUTE_SORT_MAX_N) return hipErrorInvalidValue;
     const int P = T * k + E * B - k;
     const int NB = (P + B - 1) / B;
     const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + 4 * (size_t)E + 1);
