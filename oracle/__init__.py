@@ -82,7 +82,7 @@ def _load():
         lib.oracle_sort.argtypes = [P, P, i32, i32, i32, i32, P, P, P, P, P, P]
         lib.oracle_sort.restype = i32
         lib.oracle_moe.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, P,
-                                   P, P, P, P, P, i32, P, P, i32]
+                                   P, P, P, P, P, i32, P, P, i32, P, i64, f32, P, i64, P]
         lib.oracle_moe.restype = i32
         lib.oracle_quant_rows.argtypes = [P, i32, i32, i32, P, P]
         lib.oracle_quant_rows.restype = i32
@@ -245,7 +245,7 @@ QUANT = {"bf16": 0, "fp8_token": 1, "fp8_block": 2, "mxfp4": 3}
 
 def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
         w13_scale=None, w2_scale=None, quant: str = "bf16", tokens=None,
-        h_exact: bool = False, threads: int = 0):
+        h_exact: bool = False, threads: int = 0, h_flip=None, tie_band: float = 0.0):
     """The MoE layer output for the rows listed in `tokens` (default: all).
 
     w13 / w2 (and the scales) are sequences indexed by expert holding numpy
@@ -253,7 +253,14 @@ def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
     w2[e] [d, f]; bf16 as uint16 bits, e4m3 codes as uint8 with fp32 scales,
     or (mxfp4) E2M1 codes packed two per byte [2f, d/2] / [d, f/2] with E8M0
     scales uint8 [2f, d/32] / [d, f/32].
-    Returns (y fp32 [n, d], out bf16 bits uint16 [n, d])."""
+    Element n of the h of assignment (tokens[i], j) has the flat index
+    (i * k + j) * f + n. `h_flip` lists such indices whose h is rounded to the
+    other of its two nearest bf16 values. With `tie_band` > 0 the call also
+    reports the elements whose fp32 h lies within tie_band * |h| of a bf16
+    rounding midpoint and whose other rounding would change the scale of
+    their quantisation group or, under the same scale, their own code.
+    Returns (y fp32 [n, d], out bf16 bits uint16 [n, d]), and with
+    tie_band > 0 also the reported elements as int64 rows (i, j, n)."""
     lib = _load()
     x = _c(x_bf16, np.uint16)
     ids = _c(topk_ids, np.int32)
@@ -286,11 +293,21 @@ def moe(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,
         s13 = s2 = None
     y = np.empty((tok.size, d), np.float32)
     out = np.empty((tok.size, d), np.uint16)
+    flip = np.unique(np.asarray([] if h_flip is None else h_flip, np.int64))
+    cap = tok.size * k * f if tie_band > 0 else 0
+    ties = np.empty(max(cap, 1), np.int64)
+    n_ties = np.zeros(1, np.int64)
     rc = lib.oracle_moe(T, d, f, E, k, q, int(h_exact), _ptr(x), _ptr(ids), _ptr(w), t13, s13,
-                        t2, s2, _ptr(tok), tok.size, _ptr(y), _ptr(out), int(threads))
+                        t2, s2, _ptr(tok), tok.size, _ptr(y), _ptr(out), int(threads),
+                        _ptr(flip), flip.size, float(tie_band), _ptr(ties), cap, _ptr(n_ties))
     if rc != 0:
         raise ValueError(f"oracle_moe failed ({rc})")
-    return y, out
+    if tie_band <= 0:
+        return y, out
+    if n_ties[0] > cap:
+        raise ValueError(f"oracle_moe reported {n_ties[0]} ties, more than the {cap} it can hold")
+    t = np.sort(ties[:n_ties[0]])
+    return y, out, np.stack([t // (k * f), (t // f) % k, t % f], axis=1)
 
 
 def moe_backward(x_bf16: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w13, w2,

@@ -24,6 +24,15 @@
  *    at 5:58). The intermediate h is rounded to bf16; fp8 layers then
  *    re-quantise that bf16 h (per row, or per 1x128 block) before the down
  *    projection, and quantise the input row the same way.
+ *    The sum order of an fp32 dot product is not fixed by the pages, so an
+ *    h whose fp32 value lies within rounding noise of the midpoint between
+ *    two bfloat16 values may round either way; where the other rounding
+ *    would change its quantisation group's scale (the largest magnitude, or
+ *    the MXFP4 shared exponent), every code of the group moves, and where it
+ *    would change the element's own code, that code moves. oracle_moe
+ *    reports such elements (tie_band > 0) and can round listed elements to
+ *    the other neighbour (h_flip), so that a test can bound what these
+ *    readings allow.
  *  - oracle_e4m3_encode / _decode / oracle_quant_group: the OCP FP8 E4M3FN
  *    format (bias 7, 3 mantissa bits, max 448, no infinities, S.1111.111 is
  *    NaN) and the scale rule s = amax / 448 (s = 1 when amax = 0),
@@ -86,6 +95,23 @@ uint16_t oracle_f32_to_bf16(float f)
 }
 
 static float round_to_bf16(float f) { return bf16_bits_to_f32(oracle_f32_to_bf16(f)); }
+
+/* The bfloat16 value adjacent to r (a finite bfloat16 value) on the side
+ * of v: one step of the 7-bit mantissa up or down. */
+static float bf16_neighbour(float r, float v)
+{
+    uint32_t u;
+    memcpy(&u, &r, sizeof u);
+    uint16_t b = (uint16_t)(u >> 16);
+    const int up = v > r;
+    if (r == 0.0f)
+        b = up ? 0x0001u : 0x8001u;
+    else if ((r > 0.0f) == up)
+        b = (uint16_t)(b + 1u); /* away from zero */
+    else
+        b = (uint16_t)(b - 1u); /* toward zero */
+    return bf16_bits_to_f32(b);
+}
 
 /* OCP E4M3FN decode: value = (-1)^s * 2^(e-7) * (1 + m/8) for e > 0,
  * (-1)^s * 2^-6 * (m/8) for e = 0, NaN for e = 15, m = 7. */
@@ -464,14 +490,113 @@ static void fake_quant(float *v, int n, int quant)
 
 static float silu(float z) { return z / (1.0f + expf(-z)); }
 
+/* What fixes a quantisation group's scale, from its largest magnitude a:
+ * a itself for the e4m3 formats (s = a / 448), the shared exponent of
+ * oracle_mx_quant_group for MXFP4. */
+static double group_scale_key(int quant, float a)
+{
+    if (quant != 3)
+        return a;
+    if (a == 0.0f)
+        return -127.0;
+    int ex;
+    frexp((double)a, &ex);
+    int E = (ex - 1) - 2;
+    return E < -127 ? -127.0 : (E > 127 ? 127.0 : (double)E);
+}
+
+/* Is key in the ascending list a[0..n)? */
+static int listed(const int64_t *a, int64_t n, int64_t key)
+{
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (a[mid] < key)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo < n && a[lo] == key;
+}
+
+/* Elements of one assignment's h (f values, bf16-rounded in h, fp32 before
+ * rounding in hpre) whose fp32 value lies within band * |value| of the
+ * midpoint between its bf16 rounding and the adjacent bf16 value, and whose
+ * rounding to that other value would change the scale of its group (f
+ * values for quant 1, 128 for quant 2, 32 for quant 3) or, under the same
+ * scale, its own code. Appends base + n for each; *n_ties counts them all,
+ * ties[] keeps the first max_ties. */
+static void find_ties(const float *h, const float *hpre, int f, int quant, float band, int64_t base,
+                      int64_t *ties, int64_t max_ties, int64_t *n_ties)
+{
+    const int g = (quant == 1) ? f : (quant == 2 ? 128 : 32);
+    for (int g0 = 0; g0 < f; g0 += g) {
+        float a1 = 0.0f, a2 = 0.0f; /* largest and second largest magnitude */
+        int i1 = -1;
+        for (int n = g0; n < g0 + g; ++n) {
+            const float a = fabsf(h[n]);
+            if (a > a1) {
+                a2 = a1;
+                a1 = a;
+                i1 = n;
+            } else if (a > a2) {
+                a2 = a;
+            }
+        }
+        const double key = group_scale_key(quant, a1);
+        /* the group's scale: a1 / 448 (e4m3), 2^key (MXFP4) */
+        const float s = (quant == 3) ? 1.0f : (a1 == 0.0f ? 1.0f : a1 / 448.0f);
+        for (int n = g0; n < g0 + g; ++n) {
+            const float r = h[n], v = hpre[n];
+            if (v == r)
+                continue;
+            const float o = bf16_neighbour(r, v);
+            const float mid = 0.5f * (r + o); /* exact: r and o are adjacent bf16 values */
+            if (fabsf(v - mid) > band * fabsf(v))
+                continue;
+            const float others = (n == i1) ? a2 : a1;
+            int moves = group_scale_key(quant, fmaxf(others, fabsf(o))) != key;
+            if (!moves && quant == 3)
+                moves = oracle_fp4_encode((float)ldexp((double)r, -(int)key)) !=
+                        oracle_fp4_encode((float)ldexp((double)o, -(int)key));
+            else if (!moves)
+                moves = oracle_e4m3_encode(r / s) != oracle_e4m3_encode(o / s);
+            if (!moves)
+                continue;
+            int64_t at;
+#ifdef _OPENMP
+#pragma omp atomic capture
+#endif
+            at = (*n_ties)++;
+            if (at < max_ties)
+                ties[at] = base + n;
+        }
+    }
+}
+
+/* The layer output for the rows tokens[0..n_tokens): y fp32 [n_tokens, d]
+ * and its bf16 rounding out. h_exact = 1 keeps h in fp32 and unquantised.
+ * Element n of the h of assignment (tokens[i], j) has the flat index
+ * (i * k + j) * f + n. h_flip (ascending, n_flip entries) lists elements
+ * rounded to the other of their two nearest bf16 values; tie_band > 0
+ * writes the elements find_ties reports to ties (at most max_ties) and
+ * their count to *n_ties. */
 int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
                const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                const void *const *w13, const void *const *w13_scale,
                const void *const *w2, const void *const *w2_scale,
-               const int32_t *tokens, int n_tokens, float *y, uint16_t *out, int nthreads)
+               const int32_t *tokens, int n_tokens, float *y, uint16_t *out, int nthreads,
+               const int64_t *h_flip, int64_t n_flip, float tie_band, int64_t *ties,
+               int64_t max_ties, int64_t *n_ties)
 {
     if (!x || !topk_ids || !topk_w || !w13 || !w2 || !tokens || !y || !out)
         return -1;
+    if (n_flip < 0 || (n_flip > 0 && !h_flip) || !(tie_band >= 0.0f))
+        return -1;
+    if (tie_band > 0.0f && (!ties || !n_ties || max_ties < 0))
+        return -1;
+    if (n_ties)
+        *n_ties = 0;
     if (T < 0 || d < 1 || f < 1 || E < 1 || k < 1 || k > E || n_tokens < 0)
         return -1;
     if (quant < 0 || quant > 3)
@@ -507,12 +632,14 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
         const int t = tokens[i];
         float *xt = (float *)malloc(sizeof(float) * (size_t)d);
         float *h = (float *)malloc(sizeof(float) * (size_t)f);
+        float *hpre = (float *)malloc(sizeof(float) * (size_t)f); /* h before its bf16 rounding */
         /* one weight row at a time: gate row, up row (d each), down row (f) */
         float *wrow = (float *)malloc(sizeof(float) * (size_t)(2 * d + f));
         float *yt = y + (size_t)i * d;
-        if (!xt || !h || !wrow) {
+        if (!xt || !h || !hpre || !wrow) {
             free(xt);
             free(h);
+            free(hpre);
             free(wrow);
             bad |= 1;
             continue;
@@ -536,9 +663,16 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
                     g += xt[c] * wg[c];
                     u += xt[c] * wu[c];
                 }
-                float hn = silu(g) * u;
-                h[n] = h_exact ? hn : round_to_bf16(hn);
+                const float hn = silu(g) * u;
+                float r = round_to_bf16(hn);
+                /* listed elements take the other of the two nearest bf16 values */
+                if (n_flip && r != hn && listed(h_flip, n_flip, ((int64_t)i * k + j) * f + n))
+                    r = bf16_neighbour(r, hn);
+                hpre[n] = hn;
+                h[n] = h_exact ? hn : r;
             }
+            if (quant && !h_exact && tie_band > 0.0f)
+                find_ties(h, hpre, f, quant, tie_band, ((int64_t)i * k + j) * f, ties, max_ties, n_ties);
             if (quant && !h_exact)
                 fake_quant(h, f, quant);
             for (int m = 0; m < d; ++m) {
@@ -553,6 +687,7 @@ int oracle_moe(int T, int d, int f, int E, int k, int quant, int h_exact,
             out[(size_t)i * d + m] = oracle_f32_to_bf16(yt[m]);
         free(xt);
         free(h);
+        free(hpre);
         free(wrow);
     }
     return bad ? -2 : 0;

@@ -1,11 +1,23 @@
-"""A seeded sweep of layer shapes and launch choices against the CPU oracle.
+"""Seeded sweeps of layer shapes and launch choices against the CPU oracle.
 
 Thirty-two configurations drawn once from a fixed-seed generator: token
 counts from 1 to 511 (ragged against every block size), 1 to 256 experts,
 top-1 to top-8, softmax and sigmoid scores over normal and Zipf logits,
 every weight format, and for each a block size the shape allows (the tiled
-kernels where the sizes permit them), a stage and a K-split. Each fused
-layer must meet the output bar of the other parity tests."""
+kernels where the sizes permit them), a stage and a K-split. A second draw
+of twenty-four takes many experts (128 to 1024), top-k up to 16, up to
+1024 tokens (the sort on several workgroups), and runs each layer through
+one of the three entry paths: the fused call, the two-stage calls (routing,
+sort, GEMM1, GEMM2 one by one) and the allocation-free call. Each layer
+must meet the output bar of the other parity tests.
+
+An h element whose fp32 value sits on a bf16 rounding midpoint may round
+either way under the two summation orders; where that decides its group's
+scale or its own code, one token's output can move by several per cent at
+these small widths (two to eight quantisation groups a row, one heavy
+expert weight). The oracle reports such elements and the output change of
+rounding each the other way, and a row's deviation counts beyond the sum
+of those changes."""
 import numpy as np
 import pytest
 import torch
@@ -58,12 +70,71 @@ def test_sweep_fused_against_the_oracle(case):
     wl, B, stage, ksplit = case
     x, logits = wl.activations(DEV)
     ws = wl.weights(DEV)
-    ref, _, _ = oracle_layer(wl, x, logits, ws)
+    slack = {}
+    ref, _, _ = oracle_layer(wl, x, logits, ws, slack=slack)
     out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, quant=wl.quant,
                         w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"], score=wl.score,
                         B=B, stage=stage, ksplit=ksplit)
     torch.cuda.synchronize()
-    err, norm = rel_err(bf16_to_f64(bits(out)), ref)
+    err, norm = rel_err(bf16_to_f64(bits(out)), ref, slack)
     log(f"sweep {wl.name}: err={err:.3e} norm={norm:.3e}")
     assert torch.isfinite(out.float()).all()
     assert err <= TOL[wl.quant], (wl, B, stage, ksplit, err)
+
+
+def _cases_wide(n=24, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        q = QUANTS[i % 4]
+        E = int(rng.choice([128, 256, 512, 1024]))
+        k = int(rng.integers(1, 17))
+        T = int(rng.choice([1, 7, 64, 300, 1024]))
+        unit = 512 if q == "mxfp4" else 128
+        d = unit * int(rng.integers(1, 3))
+        f = unit * int(rng.integers(1, 3))
+        score = "sigmoid" if rng.random() < 0.5 else "softmax"
+        logits = "zipf" if rng.random() < 0.5 else "normal"
+        Bs = [16, 32] + ([64, 128, 256] if _tiled_ok(q, d, f) else [])
+        B = int(rng.choice(Bs))
+        ksplit = int(rng.choice([0, 1, 2]))
+        path = ("fused", "two_stage", "noalloc")[i % 3]
+        wl = workloads.Workload(f"wide{i:02d}", T=T, d=d, f=f, E=E, k=k, quant=q, score=score,
+                                logits=logits, seed=5000 + i)
+        out.append((wl, B, ksplit, path))
+    return out
+
+
+WIDE = _cases_wide()
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[
+    f"{w.name}-{w.quant}-T{w.T}-E{w.E}k{w.k}-d{w.d}f{w.f}-B{B}ks{ks}-{path}" for w, B, ks, path in WIDE])
+def test_wide_sweep_every_entry_path_against_the_oracle(case):
+    wl, B, ksplit, path = case
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    slack = {}
+    ref, _, _ = oracle_layer(wl, x, logits, ws, slack=slack)
+    kw = dict(quant=wl.quant, w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"], score=wl.score)
+    if path == "noalloc":
+        need = moe.fused_moe_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, wl.quant, B, 2)
+        if need > moe.NOALLOC_SCRATCH_BYTES:
+            path = "fused"
+    if path == "fused":
+        out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, B=B, stage=2, ksplit=ksplit,
+                            **kw)
+    elif path == "noalloc":
+        out = moe.fused_moe_noalloc(x, ws["w13"], ws["w2"], wl.k, logits=logits, B=B, stage=2,
+                                    ksplit=ksplit, **kw)
+    else:
+        ids, w = moe.moe_topk(logits, wl.k, wl.score)
+        srt = moe.moe_sort(ids, w, wl.E, B)
+        h, hs = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, B, wl.quant, ws["w13_scale"])
+        out = moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B, wl.quant, ws["w2_scale"],
+                                    ksplit=ksplit)
+    torch.cuda.synchronize()
+    err, norm = rel_err(bf16_to_f64(bits(out)), ref, slack)
+    log(f"wide sweep {wl.name} ({path}): err={err:.3e} norm={norm:.3e}")
+    assert torch.isfinite(out.float()).all()
+    assert err <= TOL[wl.quant], (wl, B, ksplit, path, err)
