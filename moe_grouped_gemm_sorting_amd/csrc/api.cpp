@@ -294,10 +294,13 @@ Gemm1Ws carve_gemm1(Carver &c, int T, int d, int f, int E, int k, int B, int qua
     return w;
 }
 
+// x_ready: the activation codes are already in w (quantised by the routing
+// launch, which also cleared the per-token row amax of h), so no
+// quantisation launch here.
 int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x, const void *w13,
               const void *w13_scale_v, const int32_t *sorted_ids, const int32_t *seid,
               const int32_t *num_valid, void *h, void *h_scale_v, const Gemm1Ws &w, hipStream_t s,
-              float *zero = nullptr, size_t zero_n = 0) {
+              float *zero = nullptr, size_t zero_n = 0, bool x_ready = false) {
     // fp32 scales (e4m3) or E8M0 bytes (MXFP4)
     const float *w13_scale = quant == MOE_QUANT_MXFP4 ? nullptr : static_cast<const float *>(w13_scale_v);
     float *h_scale = quant == MOE_QUANT_MXFP4 ? nullptr : static_cast<float *>(h_scale_v);
@@ -315,8 +318,9 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
         g.a = x;
         g.h = h;
     } else if (quant == MOE_QUANT_MXFP4) {
-        HIP_TRY(launch_quant_mx(static_cast<const uint16_t *>(x), T, d, w.qx, w.sxm, s),
-                "activation quantisation launch");
+        if (!x_ready)
+            HIP_TRY(launch_quant_mx(static_cast<const uint16_t *>(x), T, d, w.qx, w.sxm, s),
+                    "activation quantisation launch");
         g.a = w.qx;
         g.a_mx = w.sxm;
         g.w13_mx = static_cast<const uint8_t *>(w13_scale_v);
@@ -325,9 +329,10 @@ int run_gemm1(int T, int d, int f, int E, int k, int B, int quant, const void *x
     } else {
         // (per-token e4m3: the same launch clears the row amax of h, which
         // GEMM1 takes with atomics)
-        HIP_TRY(launch_quant_act(static_cast<const uint16_t *>(x), T, d, quant == 1 ? d : 128, w.qx,
-                                 w.sx, s, quant == 1 ? w.amax : nullptr, quant == 1 ? (int)P : 0),
-                "activation quantisation launch");
+        if (!x_ready)
+            HIP_TRY(launch_quant_act(static_cast<const uint16_t *>(x), T, d, quant == 1 ? d : 128, w.qx,
+                                     w.sx, s, quant == 1 ? w.amax : nullptr, quant == 1 ? (int)P : 0),
+                    "activation quantisation launch");
         g.a = w.qx;
         g.a_scale = w.sx;
         if (quant == 1) {
@@ -948,14 +953,37 @@ int fused_impl(int T, int d, int f, int E, int k, int quant, int score, int reno
     // T=4096, E=8 2930 -> 2870 us; T=32, E=8 unchanged).
     const bool fuse_route = (int64_t)T * E <= MOE_FUSE_ROUTE_MAX;
     const bool zero_in_sort = stage == 1 && logits && fuse_route && acc_n <= (size_t(1) << 20);
+    // With logits, the routing launch also quantises the activations on
+    // workgroups of its own (they do not depend on the routing), which then
+    // run beside the one-workgroup route+sort or the top-k waves instead of
+    // in a launch of their own (per-token e4m3: and clears the row amax of h).
+    ActQuant aq{};
+    if (logits && quant != 0) {
+        aq.x = static_cast<const uint16_t *>(x);
+        aq.rows = T;
+        aq.cols = d;
+        aq.codes = w.g1.qx;
+        if (quant == MOE_QUANT_MXFP4) {
+            aq.kind = ACT_QUANT_MX;
+            aq.mx_scales = w.g1.sxm;
+        } else {
+            aq.kind = quant == 1 ? ACT_QUANT_ROW : ACT_QUANT_BLOCK;
+            aq.scales = w.g1.sx;
+            if (quant == 1) {
+                aq.zero = w.g1.amax;
+                aq.zero_n = (int)max_padded(T, k, E, B);
+            }
+        }
+    }
+    const bool x_ready = aq.kind != ACT_QUANT_NONE;
     if (logits && fuse_route) {
         HIP_TRY(launch_route_sort(logits, T, k, E, B, score, renorm, w.topk_ids, w.topk_w,
                                   w.sorted_ids, w.sorted_w, w.seid, w.counts, w.offsets,
                                   w.num_valid, s, zero_in_sort ? acc : nullptr,
-                                  zero_in_sort ? (int)acc_n : 0),
+                                  zero_in_sort ? (int)acc_n : 0, &aq),
                 "route+sort launch");
     } else if (logits) {
-        HIP_TRY(launch_topk(logits, T, E, k, score, renorm, w.topk_ids, w.topk_w, s), "topk launch");
+        HIP_TRY(launch_topk(logits, T, E, k, score, renorm, w.topk_ids, w.topk_w, s, &aq), "topk launch");
         HIP_TRY(launch_sort(w.topk_ids, w.topk_w, T, k, E, B, w.sorted_ids, w.sorted_w, w.seid,
                             w.counts, w.offsets, w.num_valid, s),
                 "sort launch");
@@ -977,7 +1005,7 @@ int fused_impl(int T, int d, int f, int E, int k, int quant, int score, int reno
     if (ksplit <= 0) ksplit = pick_ksplit(T, d, f, E, k, B, quant, cu_count_cached());
     const bool clear = !stored_rows(B, ksplit);
     rc = run_gemm1(T, d, f, E, k, B, quant, x, w13, w13_scale, w.sorted_ids, w.seid, w.num_valid,
-                   w.h, w.h_scale, w.g1, s, clear ? acc : nullptr, clear ? (size_t)T * d : 0);
+                   w.h, w.h_scale, w.g1, s, clear ? acc : nullptr, clear ? (size_t)T * d : 0, x_ready);
     if (rc) return rc;
     return run_gemm2(T, d, f, E, k, B, quant, ksplit, w.h, w.h_scale, w2, w2_scale, w.sorted_ids,
                      w.sorted_w, w.seid, w.num_valid, out, w.g2, logits != nullptr, s, true);

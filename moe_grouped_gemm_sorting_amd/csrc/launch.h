@@ -8,8 +8,25 @@
 
 namespace moe {
 
+// An activation quantisation that a routing launch carries on workgroups of
+// its own after the routing ones (the two are independent, so it runs while
+// the routing does). x bf16 [rows, cols]; ACT_QUANT_ROW: e4m3 codes
+// [rows, cols] with one fp32 scale per row; ACT_QUANT_BLOCK: one per 1x128;
+// ACT_QUANT_MX: E2M1 codes two per byte [rows, cols / 2] and E8M0 scales
+// [rows, cols / 32]. zero[0, zero_n), when given, is cleared on the way.
+enum { ACT_QUANT_NONE = 0, ACT_QUANT_ROW = 1, ACT_QUANT_BLOCK = 2, ACT_QUANT_MX = 3 };
+struct ActQuant {
+    const uint16_t *x;
+    int rows, cols, kind;
+    uint8_t *codes;
+    float *scales;        // e4m3 kinds
+    uint8_t *mx_scales;   // ACT_QUANT_MX
+    float *zero;
+    int zero_n;
+};
+
 hipError_t launch_topk(const float *logits, int T, int E, int k, int score, int renorm,
-                       int32_t *ids, float *w, hipStream_t s);
+                       int32_t *ids, float *w, hipStream_t s, const ActQuant *aq = nullptr);
 
 hipError_t launch_sort(const int32_t *ids, const float *w, int T, int k, int E, int B,
                        int32_t *sorted_ids, float *sorted_w, int32_t *sorted_expert_ids,
@@ -20,7 +37,7 @@ hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, in
                              int renorm, int32_t *ids, float *w, int32_t *sorted_ids,
                              float *sorted_w, int32_t *sorted_expert_ids, int32_t *counts,
                              int32_t *offsets, int32_t *num_valid, hipStream_t s,
-                             float *zero = nullptr, int zero_n = 0);
+                             float *zero = nullptr, int zero_n = 0, const ActQuant *aq = nullptr);
 
 // MXFP4: codes [rows, cols / 2] (two per byte), E8M0 scales [rows, cols / 32]
 hipError_t launch_quant_mx(const uint16_t *x, int rows, int cols, uint8_t *codes, uint8_t *scales,

@@ -1,28 +1,23 @@
 // quant.hip -- dynamic e4m3 quantisation of activations and of the
 // intermediate h, plus the accumulator fill and the final fp32 -> bf16 pass.
 //
-// Quantisation rule (the per_Token and per_1x128 quant types of the AITER
-// walk-through, itsolotime.com/th/archives/32381, sections 1.1 and 3.2):
-// s = amax / 448 over the group (s = 1 when amax = 0), q = e4m3(v / s) with
-// round-to-nearest-even and saturation. Both divisions are IEEE
-// correctly rounded.
+// The quantisation rules and the per-row and per-block bodies are in
+// quant_body.h (shared with the routing launches that carry the activation
+// quantisation).
 #include <algorithm>
 
-#include "common.h"
-#include "launch.h"
+#include "quant_body.h"
 
 namespace moe {
 
-// One workgroup of NT threads per row. Thread t owns the 8-element chunks
-// t, t + NT, ... (16-byte loads, QU of them in flight). GROUP_ROW: one
-// scale for the whole row; otherwise one scale per 128 columns (16
-// consecutive chunks = 16 lanes). With num_valid (rows of h by sort slot),
-// rows at or past num_valid and rows of padding slots (sorted_ids[r] ==
-// sentinel) are skipped. zero[0, zero_n), when given, is cleared on the way
-// (the row amax that the e4m3 GEMM1 which follows takes with atomics).
-// The rows of h (amax given, 14336 columns in the Mixtral shape) take 512
-// threads: 14.6 against 20.7 us for 1024 rows at 256 threads; the
-// activation rows, whose amax the workgroup finds itself, gain nothing.
+// One workgroup of NT threads per row (quant_row). With num_valid (rows of h
+// by sort slot), rows at or past num_valid and rows of padding slots
+// (sorted_ids[r] == sentinel) are skipped. zero[0, zero_n), when given, is
+// cleared on the way (the row amax that the e4m3 GEMM1 which follows takes
+// with atomics). The rows of h (amax given, 14336 columns in the Mixtral
+// shape) take 512 threads: 14.6 against 20.7 us for 1024 rows at 256
+// threads; the activation rows, whose amax the workgroup finds itself, gain
+// nothing.
 template <bool GROUP_ROW, int NT = 256>
 __global__ __launch_bounds__(NT) void k_quant_rows(const uint16_t *__restrict__ x,
                                                     const float *__restrict__ row_amax,
@@ -36,116 +31,16 @@ __global__ __launch_bounds__(NT) void k_quant_rows(const uint16_t *__restrict__ 
     const int r = blockIdx.x;
     if (num_valid && r >= *num_valid) return;
     if (sorted_ids && sorted_ids[r] >= sentinel) return;
-    const int tid = threadIdx.x;
-    const int nchunk = cols / 8;
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)r * cols);
-    uint2 *dst = reinterpret_cast<uint2 *>(codes + (size_t)r * cols);
-    __shared__ float red[NT / 64];
-
-    float s_row = 1.0f;
-    if (GROUP_ROW) {
-        float amax;
-        if (row_amax) {
-            amax = row_amax[r];
-        } else {
-            float m = 0.0f;
-            for (int c = tid; c < nchunk; c += NT) {
-                const uint4 q = src[c];
-                const uint32_t wds[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    m = fmaxf(m, fabsf(bf16_bits_to_f32(wds[i] & 0xffffu)));
-                    m = fmaxf(m, fabsf(bf16_bits_to_f32(wds[i] >> 16)));
-                }
-            }
-            m = wave_max(m);
-            if ((tid & 63) == 0) red[tid >> 6] = m;
-            __syncthreads();
-            amax = 0.0f;
-#pragma unroll
-            for (int w = 0; w < NT / 64; ++w) amax = fmaxf(amax, red[w]);
-        }
-        s_row = amax == 0.0f ? 1.0f : amax / 448.0f;
-        if (tid == 0) scales[r] = s_row;
-    }
-    // chunk loop, QU chunks per thread per pass with their loads issued
-    // first; for the 1x128 grouping all 16 lanes of a group are in the same
-    // pass because NT is a multiple of 16.
-    constexpr int QU = 4;
-    for (int c0 = 0; c0 < nchunk; c0 += QU * NT) {
-        uint4 q[QU];
-#pragma unroll
-        for (int u = 0; u < QU; ++u) {
-            const int c = c0 + u * NT + tid;
-            q[u] = c < nchunk ? src[c] : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int u = 0; u < QU; ++u) {
-            const int c = c0 + u * NT + tid;
-            const bool live = c < nchunk;
-            float v[8];
-            const uint32_t wds[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = bf16_bits_to_f32(wds[i] & 0xffffu);
-                v[2 * i + 1] = bf16_bits_to_f32(wds[i] >> 16);
-            }
-            float s = s_row;
-            if (!GROUP_ROW) {
-                float m = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-#pragma unroll
-                for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-                s = m == 0.0f ? 1.0f : m / 448.0f;
-                if (live && (c & 15) == 0) scales[(size_t)r * (cols / 128) + c / 16] = s;
-            }
-            if (live) {
-                uint32_t lo = f32x2_to_e4m3x2(v[0] / s, v[1] / s) |
-                              (f32x2_to_e4m3x2(v[2] / s, v[3] / s) << 16);
-                uint32_t hi = f32x2_to_e4m3x2(v[4] / s, v[5] / s) |
-                              (f32x2_to_e4m3x2(v[6] / s, v[7] / s) << 16);
-                dst[c] = make_uint2(lo, hi);
-            }
-        }
-    }
+    quant_row<GROUP_ROW, NT>(x, row_amax, r, cols, codes, scales);
 }
 
-// MXFP4 (per_1x32) quantisation: one thread per 32-element block of a row
-// (four 16-byte loads), codes packed two per byte (even column in the low
-// nibble), one E8M0 scale byte per block.
+// MXFP4 (per_1x32) quantisation: one thread per 32-element block of a row.
 __global__ __launch_bounds__(256) void k_quant_mx(const uint16_t *__restrict__ x, int rows, int cols,
                                                   uint8_t *__restrict__ codes,
                                                   uint8_t *__restrict__ scales) {
-    const int nb = cols / 32;
     const size_t b = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (b >= (size_t)rows * nb) return;
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + b * 32);
-    float v[32];
-    float amax = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint4 q = src[c];
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[8 * c + 2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-            v[8 * c + 2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-            amax = fmaxf(amax, fmaxf(fabsf(v[8 * c + 2 * i]), fabsf(v[8 * c + 2 * i + 1])));
-        }
-    }
-    const int E = mx_block_exp(amax);
-    const float inv = mx_inv_scale(E);
-    uint32_t out[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float sv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sv[i] = v[8 * j + i] * inv;
-        out[j] = e2m1_pack8(sv);
-    }
-    *reinterpret_cast<uint4 *>(codes + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
-    scales[b] = (uint8_t)(E + 127);
+    if (b >= (size_t)rows * (cols / 32)) return;
+    quant_mx_block(x, b, codes, scales);
 }
 
 hipError_t launch_quant_mx(const uint16_t *x, int rows, int cols, uint8_t *codes, uint8_t *scales,

@@ -12,6 +12,7 @@
 #include "common.h"
 #include "launch.h"
 #include "moe.h"
+#include "quant_body.h"
 
 namespace moe {
 
@@ -87,11 +88,17 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ logits, int 
     }
 }
 
+// Workgroups [0, route_wgs) route four tokens each; the ones after carry the
+// activation quantisation aq.
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, int T, int E,
                                               int k, int score, int renorm,
                                               int32_t *__restrict__ ids,
-                                              float *__restrict__ w) {
+                                              float *__restrict__ w, ActQuant aq, int route_wgs) {
+    if ((int)blockIdx.x >= route_wgs) {
+        act_quant_part<256>(aq, blockIdx.x - route_wgs, gridDim.x - route_wgs);
+        return;
+    }
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     topk_wave<PER_LANE>(logits, t, E, k, score, renorm, ids, w);
@@ -153,19 +160,21 @@ __device__ __forceinline__ void topk_thread(const float *__restrict__ logits, in
 }
 
 hipError_t launch_topk(const float *logits, int T, int E, int k, int score, int renorm,
-                       int32_t *ids, float *w, hipStream_t s) {
+                       int32_t *ids, float *w, hipStream_t s, const ActQuant *aq) {
     if (T == 0) return hipSuccess;
-    const dim3 grid((T + 3) / 4), block(256);
+    const ActQuant q = aq ? *aq : ActQuant{};
+    const int route_wgs = (T + 3) / 4;
+    const dim3 grid(route_wgs + act_quant_groups(q, 256)), block(256);
     if (E <= 64)
-        k_topk<1><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+        k_topk<1><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w, q, route_wgs);
     else if (E <= 128)
-        k_topk<2><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+        k_topk<2><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w, q, route_wgs);
     else if (E <= 256)
-        k_topk<4><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+        k_topk<4><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w, q, route_wgs);
     else if (E <= 512)
-        k_topk<8><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+        k_topk<8><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w, q, route_wgs);
     else
-        k_topk<16><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w);
+        k_topk<16><<<grid, block, 0, s>>>(logits, T, E, k, score, renorm, ids, w, q, route_wgs);
     return hipGetLastError();
 }
 
@@ -345,7 +354,8 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(
 
 // Routing and sort in one launch (one workgroup): top-k of every token into
 // ids / w, a workgroup barrier (which also orders the global writes for the
-// workgroup), then the sort.
+// workgroup), then the sort. Workgroups after the first carry the activation
+// quantisation aq.
 constexpr int ROUTE_SORT_MAX_N = 512;   // assignments T * k of the one-workgroup form
 template <int PER_LANE>
 __global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
@@ -353,7 +363,11 @@ __global__ __launch_bounds__(SORT_THREADS) void k_route_sort(
     int32_t *__restrict__ ids, float *__restrict__ wts, int P, int NB,
     int32_t *__restrict__ sorted_ids, float *__restrict__ sorted_w, int32_t *__restrict__ seid,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ num_valid,
-    float *__restrict__ zero, int zero_n) {
+    float *__restrict__ zero, int zero_n, ActQuant aq) {
+    if (blockIdx.x > 0) {
+        act_quant_part<SORT_THREADS>(aq, blockIdx.x - 1, gridDim.x - 1);
+        return;
+    }
     // optionally clear a (small) fp32 accumulator for the next stage
     if (zero)
         for (int i = threadIdx.x; i < zero_n / 4; i += SORT_THREADS)
@@ -384,15 +398,17 @@ hipError_t launch_route_sort(const float *logits, int T, int k, int E, int B, in
                              int renorm, int32_t *ids, float *w, int32_t *sorted_ids,
                              float *sorted_w, int32_t *sorted_expert_ids, int32_t *counts,
                              int32_t *offsets, int32_t *num_valid, hipStream_t s, float *zero,
-                             int zero_n) {
+                             int zero_n, const ActQuant *aq) {
     if ((int64_t)T * k > ROUTE_SORT_MAX_N) return hipErrorInvalidValue;
+    const ActQuant q = aq ? *aq : ActQuant{};
+    const unsigned wgs = 1 + (unsigned)act_quant_groups(q, SORT_THREADS);
     const int P = T * k + E * B - k;
     const int NB = (P + B - 1) / B;
     const size_t lds = sizeof(int) * ((size_t)SORT_WAVES * E + 4 * (size_t)E + 1);
 #define MOE_ROUTE_SORT(PL)                                                                    \
-    k_route_sort<PL><<<1, SORT_THREADS, lds, s>>>(logits, T, k, E, B, score, renorm, ids, w, P, \
-                                                   NB, sorted_ids, sorted_w, sorted_expert_ids, \
-                                                   counts, offsets, num_valid, zero, zero_n)
+    k_route_sort<PL><<<wgs, SORT_THREADS, lds, s>>>(logits, T, k, E, B, score, renorm, ids, w, P, \
+                                                     NB, sorted_ids, sorted_w, sorted_expert_ids, \
+                                                     counts, offsets, num_valid, zero, zero_n, q)
     if (E <= 8) MOE_ROUTE_SORT(-8);
     else if (E <= 16) MOE_ROUTE_SORT(-16);
     else if (E <= 32) MOE_ROUTE_SORT(-32);
