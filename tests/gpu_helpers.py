@@ -63,12 +63,13 @@ def host_experts(wl, ws, experts):
 
 
 # Relative distance from a bf16 rounding midpoint within which the fp32 value
-# of h may round either way: the fp32 sums of the gate and up products differ
-# between summation orders by a few units of 2^-24 times the square root of
-# the length (about 2^-18 at d = 4096), more where the sum cancels, and
-# silu's exponential by a few ulps; the largest gap seen between the GPU's
-# h and the fp64 value was 1.25e-5 (2^-16.3).
-TIE_BAND = 2.0 ** -16
+# of h may round either way. The oracle's fp32 sums stay within a few units
+# of 2^-24 times their terms' magnitudes, but the GPU's h has been seen up to
+# 2.13e-5 (2^-15.5) from the fp64 value on both GEMM1 kernels of the e4m3
+# layers (gate and up sums of e4m3 products, whose magnitudes were 4.5 to 5
+# times the sums'), which points at the accumulation inside the e4m3 matrix
+# instructions; the band is about three times that.
+TIE_BAND = 2.0 ** -14
 
 
 def oracle_layer(wl, x, logits, ws, tokens=None, ids=None, w=None, chunk=256, slack=None):
