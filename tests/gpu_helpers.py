@@ -64,11 +64,14 @@ def host_experts(wl, ws, experts):
 
 # Relative distance from a bf16 rounding midpoint within which the fp32 value
 # of h may round either way. The oracle's fp32 sums stay within a few units
-# of 2^-24 times their terms' magnitudes, but the GPU's h has been seen up to
-# 2.13e-5 (2^-15.5) from the fp64 value on both GEMM1 kernels of the e4m3
-# layers (gate and up sums of e4m3 products, whose magnitudes were 4.5 to 5
-# times the sums'), which points at the accumulation inside the e4m3 matrix
-# instructions; the band is about three times that.
+# of 2^-24 times their terms' magnitudes. The e4m3 matrix instruction
+# (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales) does not add its 64
+# products exactly: with every lane holding the same operand bytes, its
+# results missed the exact sums by up to 4.3e-5 (2^-14.5) of the sum of the
+# products' magnitudes, typically 2^-15 to 2^-17, and small products next to
+# a large one were partly dropped. The GPU's h has been seen 2.13e-5 from
+# its fp64 value (both GEMM1 kernels of a per-token e4m3 layer alike); the
+# band is about three times that.
 TIE_BAND = 2.0 ** -14
 
 
