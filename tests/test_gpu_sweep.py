@@ -8,8 +8,12 @@ kernels where the sizes permit them), a stage and a K-split. A second draw
 of twenty-four takes many experts (128 to 1024), top-k up to 16, up to
 1024 tokens (the sort on several workgroups), and runs each layer through
 one of the three entry paths: the fused call, the two-stage calls (routing,
-sort, GEMM1, GEMM2 one by one) and the allocation-free call. Each layer
-must meet the output bar of the other parity tests.
+sort, GEMM1, GEMM2 one by one) and the allocation-free call. A third draw
+of 48 mixes both ranges (1 to 512 experts, top-1 to top-16, 1 to 777
+tokens, router-style logits, the one-stage kernel) over the same paths; its
+sixth layer (per-token e4m3, T = 127, top-3 of 8) holds an h rounding tie
+that a narrower tie band missed. Each layer must meet the output bar of
+the other parity tests.
 
 An h element whose fp32 value sits on a bf16 rounding midpoint may round
 either way under the two summation orders; where that decides its group's
@@ -138,3 +142,62 @@ def test_wide_sweep_every_entry_path_against_the_oracle(case):
     log(f"wide sweep {wl.name} ({path}): err={err:.3e} norm={norm:.3e}")
     assert torch.isfinite(out.float()).all()
     assert err <= TOL[wl.quant], (wl, B, ksplit, path, err)
+
+
+def _cases_mixed(n=48, seed=99):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        q = QUANTS[i % 4]
+        E = int(rng.choice([1, 2, 3, 5, 8, 16, 64, 128, 256, 512]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.choice([1, 2, 9, 31, 64, 127, 200, 511, 777]))
+        unit = 512 if q == "mxfp4" else 128
+        d = unit * int(rng.integers(1, 3))
+        f = unit * int(rng.integers(1, 3))
+        score = "sigmoid" if rng.random() < 0.5 else "softmax"
+        logits = ("zipf", "normal", "router")[int(rng.integers(0, 3))]
+        Bs = [16, 32] + ([64, 128, 256] if _tiled_ok(q, d, f) else [])
+        B = int(rng.choice(Bs))
+        ksplit = int(rng.choice([0, 1, 2, 3]))
+        path = ("fused", "two_stage", "noalloc")[i % 3]
+        stage = 1 if (q == "bf16" and B <= 32 and path == "fused" and rng.random() < 0.3) else 2
+        wl = workloads.Workload(f"mixed{i:02d}", T=T, d=d, f=f, E=E, k=k, quant=q, score=score,
+                                logits=logits, seed=9000 + i)
+        out.append((wl, B, ksplit, path, stage))
+    return out
+
+
+MIXED = _cases_mixed()
+
+
+@pytest.mark.parametrize("case", MIXED, ids=[
+    f"{w.name}-{w.quant}-T{w.T}-E{w.E}k{w.k}-d{w.d}f{w.f}-B{B}ks{ks}-{path}-s{st}" for w, B, ks, path, st in MIXED])
+def test_mixed_sweep_against_the_oracle(case):
+    wl, B, ksplit, path, stage = case
+    x, logits = wl.activations(DEV)
+    ws = wl.weights(DEV)
+    slack = {}
+    ref, _, _ = oracle_layer(wl, x, logits, ws, slack=slack)
+    kw = dict(quant=wl.quant, w13_scale=ws["w13_scale"], w2_scale=ws["w2_scale"], score=wl.score)
+    if path == "noalloc":
+        need = moe.fused_moe_workspace_bytes(wl.T, wl.d, wl.f, wl.E, wl.k, wl.quant, B, 2)
+        if need > moe.NOALLOC_SCRATCH_BYTES:
+            path = "fused"
+    if path == "fused":
+        out = moe.fused_moe(x, ws["w13"], ws["w2"], wl.k, logits=logits, B=B, stage=stage, ksplit=ksplit,
+                            **kw)
+    elif path == "noalloc":
+        out = moe.fused_moe_noalloc(x, ws["w13"], ws["w2"], wl.k, logits=logits, B=B, stage=2,
+                                    ksplit=ksplit, **kw)
+    else:
+        ids, w = moe.moe_topk(logits, wl.k, wl.score)
+        srt = moe.moe_sort(ids, w, wl.E, B)
+        h, hs = moe.moe_gemm1_swiglu(x, ws["w13"], srt, wl.k, B, wl.quant, ws["w13_scale"])
+        out = moe.moe_gemm2_combine(h, hs, ws["w2"], srt, wl.T, wl.k, B, wl.quant, ws["w2_scale"],
+                                    ksplit=ksplit)
+    torch.cuda.synchronize()
+    err, norm = rel_err(bf16_to_f64(bits(out)), ref, slack)
+    log(f"mixed sweep {wl.name} ({path}): err={err:.3e} norm={norm:.3e}")
+    assert torch.isfinite(out.float()).all()
+    assert err <= TOL[wl.quant], (wl, B, ksplit, path, stage, err)
